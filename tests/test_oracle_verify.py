@@ -1,0 +1,297 @@
+"""Pins for the oracle's greedy and stochastic acceptance: hand-worked examples,
+plain greedy decoding of a toy model, the lossless guarantee as a statistical test,
+the closed-form single-draft accept rate, and special cases."""
+
+import zlib
+
+import numpy as np
+import pytest
+from scipy.stats import chisquare
+
+import oracle
+from oracle.tree import STATUS_BAD_TOKEN, STATUS_NONFINITE, STATUS_PATH_OVERFLOW
+from synth import make_workload, tree_chain, tree_random_attach
+
+
+def _ints(g, k):
+    return [int(x) for x in g[k]]
+
+
+# ---------------------------------------------------------------- greedy
+
+
+def test_greedy_hand_worked(golden):
+    g = golden("greedy_small.txt")
+    parent = np.array(_ints(g, "parent"), np.int32)
+    tokens = np.array(_ints(g, "tokens"), np.int32)
+    logits = np.array([[float(x) for x in r] for r in g["logits"]], np.float32)
+    res = oracle.verify_greedy(np.array([0, len(parent)]), parent, tokens, logits, 4, 4)
+    L = int(g["accept_len"][0])
+    assert res["status"] == 0
+    assert int(res["accept_len"][0]) == L
+    assert res["accept_nodes"][0, :L + 1].tolist() == _ints(g, "accept_nodes")
+    assert res["out_tokens"][0, :L + 1].tolist() == _ints(g, "out_tokens")
+    assert (res["accept_nodes"][0, L + 1:] == -1).all() and (res["out_tokens"][0, L + 1:] == -1).all()
+
+
+def _toy_logits(ctx, V, salt=0):
+    rng = np.random.default_rng(zlib.crc32(np.asarray(ctx, np.int64).tobytes()) + salt)
+    return (rng.standard_normal(V) * 2.0).astype(np.float32)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_greedy_reproduces_plain_greedy_decoding(seed):
+    """A deterministic toy target whose next-token logits depend on the whole token
+    path.  The accepted tokens plus the bonus token must equal what plain
+    token-by-token greedy decoding emits, and no child of the last accepted node may
+    continue that sequence."""
+    rng = np.random.default_rng(seed)
+    V = 12
+    root_ctx = (int(rng.integers(0, V)),)
+    parent, ctxs = [-1], [root_ctx]
+    frontier = [0]
+    for _depth in range(4):
+        nxt = []
+        for u in frontier:
+            for _ in range(int(rng.integers(0, 4))):
+                if rng.random() < 0.5:
+                    tok = int(np.argmax(_toy_logits(ctxs[u], V)))
+                else:
+                    tok = int(rng.integers(0, V))
+                parent.append(u)
+                ctxs.append(ctxs[u] + (tok,))
+                nxt.append(len(parent) - 1)
+        frontier = nxt
+    n = len(parent)
+    tokens = np.array([c[-1] for c in ctxs], np.int32)
+    logits = np.stack([_toy_logits(c, V) for c in ctxs])
+    res = oracle.verify_greedy(np.array([0, n]), np.array(parent, np.int32), tokens, logits, V, 8)
+    L = int(res["accept_len"][0])
+    ctx, seq = root_ctx, []
+    for _ in range(L + 1):
+        tok = int(np.argmax(_toy_logits(ctx, V)))
+        seq.append(tok)
+        ctx = ctx + (tok,)
+    assert res["out_tokens"][0, :L + 1].tolist() == seq
+    last = int(res["accept_nodes"][0, L])
+    kids = [c for c in range(n) if parent[c] == last]
+    assert all(int(tokens[c]) != seq[L] for c in kids)
+
+
+def test_greedy_tiny_fp32_workload_accepts_planted_path():
+    wl = make_workload("tiny_fp32", 0)
+    a3 = int(np.argmax(wl.logits[3]))
+    assert int(wl.tokens[7]) != a3 and int(wl.tokens[8]) != a3   # no chance hit below node 3
+    res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.V, wl.max_depth)
+    assert int(res["accept_len"][0]) == 2
+    assert res["accept_nodes"][0, :3].tolist() == [0, 1, 3]
+    assert int(res["out_tokens"][0, 2]) == a3
+
+
+def test_greedy_chain_all_or_none_accepted():
+    rng = np.random.default_rng(1)
+    V, n = 50, 6
+    parent, _ = tree_chain(n)
+    logits = rng.standard_normal((n, V)).astype(np.float32)
+    a = logits.argmax(1)
+    tokens = np.zeros(n, np.int32)
+    tokens[1:] = a[:-1]
+    res = oracle.verify_greedy(np.array([0, n]), parent, tokens, logits, V, 5)
+    assert int(res["accept_len"][0]) == 5
+    assert res["out_tokens"][0, :6].tolist() == list(a[:-1]) + [int(a[-1])]
+    tokens[1:] = (a[:-1] + 1) % V
+    res = oracle.verify_greedy(np.array([0, n]), parent, tokens, logits, V, 5)
+    assert int(res["accept_len"][0]) == 0
+    assert res["out_tokens"][0, 0] == a[0]
+
+
+def test_greedy_ties_lowest_vocab_index_and_lowest_sibling():
+    parent = np.array([-1, 0, 0, 0], np.int32)
+    logits = np.zeros((4, 6), np.float32)
+    logits[0, [2, 4]] = 3.0                       # tie between 2 and 4 -> 2
+    tokens = np.array([0, 4, 2, 2], np.int32)     # nodes 2 and 3 both match -> node 2
+    res = oracle.verify_greedy(np.array([0, 4]), parent, tokens, logits, 6, 3)
+    assert res["accept_nodes"][0, :2].tolist() == [0, 2]
+    assert int(res["out_tokens"][0, 1]) == 0      # row 2 all zero -> index 0
+
+
+def test_greedy_overflow_and_input_status():
+    n = 5
+    parent, _ = tree_chain(n)
+    logits = np.zeros((n, 3), np.float32)
+    tokens = np.zeros(n, np.int32)                # every node matches argmax 0
+    res = oracle.verify_greedy(np.array([0, n]), parent, tokens, logits, 3, 2)
+    assert res["status"] & STATUS_PATH_OVERFLOW
+    assert int(res["accept_len"][0]) == 2 and int(res["out_tokens"][0, 2]) == -1
+    bad = tokens.copy()
+    bad[3] = 3
+    assert oracle.verify_greedy(np.array([0, n]), parent, bad, logits, 3, 8)["status"] & STATUS_BAD_TOKEN
+    nf = logits.copy()
+    nf[2, 1] = np.inf
+    assert oracle.verify_greedy(np.array([0, n]), parent, tokens, nf, 3, 8)["status"] & STATUS_NONFINITE
+
+
+# ---------------------------------------------------------------- stochastic
+
+
+def _fixture_case(g, case):
+    p = np.array([[float(x) for x in r] for r in g["p"]])
+    q = np.array([[float(x) for x in r] for r in g["q"]])
+    parent = np.array(_ints(g, "parent"), np.int32)
+    tokens = np.array(_ints(g, f"{case}_tokens"), np.int32)
+    ua = [float(x) for x in g[f"{case}_u_acc"]]
+    us = [float(x) for x in g[f"{case}_u_smp"]]
+    return p, q, parent, tokens, ua, us
+
+
+@pytest.mark.parametrize("case", ["case1", "case2", "case3"])
+def test_stochastic_hand_worked(golden, case):
+    g = golden("stochastic_small.txt")
+    p, q, parent, tokens, ua, us = _fixture_case(g, case)
+    res = oracle.verify_stochastic(
+        np.array([0, len(parent)]), parent, tokens, np.log(p).astype(np.float32),
+        np.log(q).astype(np.float32), 3, 1.0, 0, 0, 4, uniforms=lambda b, i: (ua[i], us[i]))
+    L = int(res["accept_len"][0])
+    assert res["accept_nodes"][0, :L + 1].tolist() == _ints(g, f"{case}_accept_nodes")
+    assert res["out_tokens"][0, :L + 1].tolist() == _ints(g, f"{case}_out_tokens")
+    assert res["status"] == 0 and int(res["near_ties"][0]) == 0
+
+
+def _softmax(x):
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+class _ToyPair:
+    """Target and draft next-token logits as seeded functions of the token path."""
+
+    def __init__(self, V, salt, noise=1.5):
+        self.V, self.salt, self.noise = V, salt, noise
+
+    def logits(self, ctx):
+        rng = np.random.default_rng(zlib.crc32(np.asarray(ctx, np.int64).tobytes()) + self.salt)
+        t = rng.standard_normal(self.V) * 1.5
+        d = t + rng.standard_normal(self.V) * self.noise
+        return t.astype(np.float32), d.astype(np.float32)
+
+
+def _draft_tree(pair, T, root_ctx, widths, rng):
+    """Children of every node drawn i.i.d. from the draft at that node."""
+    parent, ctxs, frontier = [-1], [root_ctx], [0]
+    for w in widths:
+        nxt = []
+        for u in frontier:
+            _, d = pair.logits(ctxs[u])
+            qd = _softmax(d.astype(np.float64) / T)
+            for tok in rng.choice(pair.V, size=w, p=qd):
+                parent.append(u)
+                ctxs.append(ctxs[u] + (int(tok),))
+                nxt.append(len(parent) - 1)
+        frontier = nxt
+    tl = np.stack([pair.logits(c)[0] for c in ctxs])
+    dl = np.stack([pair.logits(c)[1] for c in ctxs])
+    tokens = np.array([c[-1] for c in ctxs], np.int32)
+    return np.array(parent, np.int32), tokens, tl, dl
+
+
+def test_stochastic_output_has_the_target_distribution():
+    """Lossless guarantee: over many independent steps, the first emitted token
+    follows the target's distribution, and so does the pair of the first two tokens
+    (when a step emits only one token, the second is drawn from the target itself, as
+    the next step would)."""
+    V, T, trials = 5, 0.7, 16000
+    pair = _ToyPair(V, salt=3)
+    root_ctx = (1,)
+    rng = np.random.default_rng(2024)
+    first = np.zeros(V, np.int64)
+    joint = np.zeros((V, V), np.int64)
+    for t in range(trials):
+        parent, tokens, tl, dl = _draft_tree(pair, T, root_ctx, (3, 2), rng)
+        res = oracle.verify_stochastic(np.array([0, len(parent)]), parent, tokens, tl, dl, V, T,
+                                       seed=99, offset=t, max_depth=4)
+        L = int(res["accept_len"][0])
+        t1 = int(res["out_tokens"][0, 0])
+        if L >= 1:
+            t2 = int(res["out_tokens"][0, 1])
+        else:
+            p2 = _softmax(pair.logits(root_ctx + (t1,))[0].astype(np.float64) / T)
+            t2 = int(rng.choice(V, p=p2))
+        first[t1] += 1
+        joint[t1, t2] += 1
+    p1 = _softmax(pair.logits(root_ctx)[0].astype(np.float64) / T)
+    assert chisquare(first, p1 * trials).pvalue > 1e-3
+    pj = np.array([[p1[a] * _softmax(pair.logits(root_ctx + (a,))[0].astype(np.float64) / T)[b]
+                    for b in range(V)] for a in range(V)])
+    assert chisquare(joint.ravel(), pj.ravel() * trials).pvalue > 1e-3
+
+
+def test_single_draft_accept_rate_is_one_minus_total_variation():
+    V, T, trials = 6, 1.0, 12000
+    pair = _ToyPair(V, salt=8, noise=1.0)
+    root_ctx = (2,)
+    rng = np.random.default_rng(5)
+    acc = 0
+    for t in range(trials):
+        parent, tokens, tl, dl = _draft_tree(pair, T, root_ctx, (1,), rng)
+        res = oracle.verify_stochastic(np.array([0, 2]), parent, tokens, tl, dl, V, T,
+                                       seed=1, offset=t, max_depth=2)
+        acc += int(res["accept_len"][0])
+    tl0, dl0 = pair.logits(root_ctx)
+    p, q = _softmax(tl0.astype(np.float64)), _softmax(dl0.astype(np.float64))
+    expect = np.minimum(p, q).sum()
+    std = np.sqrt(expect * (1 - expect) / trials)
+    assert abs(acc / trials - expect) < 4 * std
+
+
+def test_equal_target_and_draft_always_accepts_first_child():
+    rng = np.random.default_rng(12)
+    n, V = 20, 40
+    parent, _ = tree_random_attach(rng, n, 6)
+    lg = (rng.standard_normal((n, V)) * 3).astype(np.float32)
+    tokens = rng.integers(0, V, n).astype(np.int32)
+    res = oracle.verify_stochastic(np.array([0, n]), parent, tokens, lg, lg, V, 0.7, 3, 0, 8)
+    u, path = 0, [0]
+    while True:
+        kids = [c for c in range(n) if parent[c] == u]
+        if not kids:
+            break
+        u = kids[0]
+        path.append(u)
+    L = int(res["accept_len"][0])
+    assert res["accept_nodes"][0, :L + 1].tolist() == path
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_one_hot_target_reduces_to_greedy(seed):
+    rng = np.random.default_rng(seed)
+    n, V = 24, 30
+    parent, _ = tree_random_attach(rng, n, 5)
+    best = rng.integers(0, V, n)
+    tl = np.full((n, V), -1000.0, np.float32)
+    tl[np.arange(n), best] = 0.0
+    dl = (rng.standard_normal((n, V)) * 2).astype(np.float32)
+    tokens = rng.integers(0, V, n).astype(np.int32)
+    for i in range(1, n):                        # make about half the nodes match
+        if rng.random() < 0.5:
+            tokens[i] = best[parent[i]]
+    st = oracle.verify_stochastic(np.array([0, n]), parent, tokens, tl, dl, V, 1.0, 4, seed, 8)
+    gr = oracle.verify_greedy(np.array([0, n]), parent, tokens, tl, V, 8)
+    for k in ("accept_len", "accept_nodes", "out_tokens"):
+        assert np.array_equal(st[k], gr[k]), k
+
+
+def test_follow_mode_records_divergences():
+    wl = make_workload("stochastic_chain", 0)
+    sl = slice(0, int(wl.node_off[2]))
+    args = (wl.node_off[:3], wl.parent[sl], wl.tokens[sl], wl.logits[sl], wl.draft_logits[sl],
+            wl.V, wl.temperature, wl.rng_seed, wl.rng_offset, wl.max_depth)
+    own = oracle.verify_stochastic(*args)
+    same = oracle.verify_stochastic(*args, follow=[own["accept_nodes"][b][own["accept_nodes"][b] >= 0]
+                                                   for b in range(2)])
+    assert all(len(d) == 0 for d in same["divergences"])
+    assert np.array_equal(same["out_tokens"], own["out_tokens"])
+    other = [[0, 1, 2, 3, 4, 5], [0, 1, 2, 3, 4, 5]]
+    forced = oracle.verify_stochastic(*args, follow=other)
+    assert forced["accept_nodes"][:, :6].tolist() == other
+    changed = [b for b in range(2) if int(own["accept_len"][b]) != 5]
+    assert all(len(forced["divergences"][b]) >= 1 for b in changed)
