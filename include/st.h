@@ -1,0 +1,202 @@
+/*
+ * st.h -- C ABI of the token-tree verification library (libst.so, gfx950).
+ *
+ * The library runs the target model's side of tree-based speculative decoding
+ * for one attention layer: the ancestor mask of a speculated token tree,
+ * tree-masked attention of every tree node over the request's cached prefix
+ * plus its own root path, greedy or rejection-sampling acceptance down the
+ * tree, and compaction of the accepted path's KV rows.
+ *
+ * Sources (web pages, cited by title and section):
+ *   SpecInfer news article (sunluscious.com.cn), "Token 樹驗證器": the draft
+ *     outputs form one token tree; the verifier runs tree attention through a
+ *     constructed mask matrix with a depth-first KV-cache update.
+ *   "SpecInfer：基于树结构的LLM推测性推理加速技术" §2.1: tree nodes carry a
+ *     parent pointer; tree_attention(query, key, value, tree_mask); the longest
+ *     verified prefix is accepted.
+ *   Speculative-decoding explainer (intelliparadigm.com) §2.2: accept with
+ *     probability min(1, p_main/p_draft), left to right, replace at the first
+ *     rejection; §3.2: all candidates are verified in one forward pass.
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns all
+ *     memory; the library never allocates, frees or synchronises.  Every call
+ *     enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream) and returns at once.
+ *   - Request b owns tree nodes node_off[b] .. node_off[b+1]-1 (N_b >= 1
+ *     nodes).  Local node 0 is the root, the last token the target already
+ *     emitted; parent[] holds request-local indices with parent[root] = -1
+ *     and 0 <= parent[i] < i for the others.
+ *   - During verification node i of request b has its key/value at cache slot
+ *     prefix_len[b] + i.  Caches are head-major: [B][Hkv][S_max][D].
+ *   - Return value: ST_OK (0) or a negative ST_E_* code for a problem found on
+ *     the host before launching (nothing is enqueued then).
+ *   - Data-dependent problems found by the kernels are OR-ed into *status (a
+ *     device int32 that the caller zeroes; may be NULL) as ST_STATUS_* bits.
+ *     Outputs of a request with such a problem are unspecified but every
+ *     write stays inside the documented output ranges.
+ *   - Calls are stateless and thread-safe; concurrent calls on different
+ *     streams may not share output or workspace buffers.
+ */
+#ifndef ST_H
+#define ST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ST_OK 0
+#define ST_E_INVALID (-1)     /* null pointer or out-of-range scalar             */
+#define ST_E_UNSUPPORTED (-2) /* D not 64/128, Hq % Hkv != 0, max_nodes > 256... */
+#define ST_E_WORKSPACE (-3)   /* workspace smaller than the *_workspace() size   */
+#define ST_E_LAUNCH (-4)      /* the HIP runtime refused a launch                */
+
+#define ST_STATUS_BAD_PARENT 1    /* parent[] breaks the rules above            */
+#define ST_STATUS_BAD_TOKEN 2     /* a draft token outside [0, V)               */
+#define ST_STATUS_NONFINITE 4     /* a logit that is NaN or infinite            */
+#define ST_STATUS_PATH_OVERFLOW 8 /* accepted path longer than max_depth        */
+#define ST_STATUS_BAD_PREFIX 16   /* prefix_len outside [0, max_prefix], or the
+                                     request's slots run past S_max             */
+
+#define ST_MAX_NODES 256          /* per request                                */
+
+typedef enum { ST_F32 = 0, ST_BF16 = 1 } st_dtype;
+
+/* A batch of B token trees, nodes concatenated request after request. */
+typedef struct {
+  int32_t B;                /* [host] number of requests, >= 1                     */
+  int32_t total_nodes;      /* [host] T = node_off[B]                              */
+  int32_t max_nodes;        /* [host] >= every N_b, <= ST_MAX_NODES                */
+  int32_t max_depth;        /* [host] >= every node depth (root depth 0)           */
+  const int32_t* node_off;  /* [B+1], node_off[0] = 0, strictly increasing         */
+  const int32_t* parent;    /* [T] request-local parent index, root = -1           */
+} st_tree;
+
+/* Words per mask row: ceil(max_nodes / 64). */
+int st_mask_words(int max_nodes);
+
+/*
+ * st_tree_mask -- ancestor bitmask and depth of every tree node.
+ * Defines which tree keys each node may attend to (SpecInfer news article,
+ * "Token 樹驗證器"; the parent pointer of §2.1 of the SpecInfer developer
+ * article).  Bit (k % 64) of word (k / 64) of mask row i is set iff request-
+ * local node k lies on node i's root path (i itself included).
+ *   mask  [T][W] uint64, W = st_mask_words(max_nodes); unused bits are 0
+ *   depth [T] int32, edges between the node and its root
+ * A request with a bad parent array sets ST_STATUS_BAD_PARENT; its rows then
+ * hold the node's own bit plus whatever valid ancestors were reached.
+ */
+int st_tree_mask(const st_tree* tree, uint64_t* mask, int32_t* depth, int32_t* status,
+                 void* stream);
+
+/* Bytes of workspace st_tree_attention needs for these sizes (0 is possible). */
+size_t st_tree_attention_workspace(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype,
+                                   int max_prefix);
+
+/*
+ * st_tree_attention -- tree-masked attention of every tree node.
+ * For node i of request b and query head h (kv head g = h / (Hq/Hkv)):
+ *   out[i][h] = softmax_k(scale * q[i][h] . K[b][g][k]) . V[b][g][k]
+ * over the keys k < prefix_len[b] (the cached prefix, always visible) and the
+ * tree keys prefix_len[b] + j with bit j of mask row i set (SpecInfer
+ * developer article §2.1, tree_attention; masked entries excluded).
+ *   q        [T][Hq][D] of `dtype` (ST_F32 or ST_BF16)
+ *   k_cache, v_cache  [B][Hkv][S_max][D] of `dtype`; S_max >= every
+ *            prefix_len[b] + N_b; only slots below that are read
+ *   prefix_len [B] int32 in [0, max_prefix]
+ *   mask     [T][W] from st_tree_mask
+ *   out      [T][Hq][D] of `dtype` (bf16 stored round-to-nearest-even)
+ *   lse      [T][Hq] fp32 natural-log sum of exp of the scaled scores, or NULL
+ *   scale    the score scale; 1/sqrt(D) reproduces standard attention
+ * Accumulation and softmax are fp32.  D must be 64 or 128; Hq % Hkv == 0.
+ */
+int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype, float scale,
+                      const void* q, const void* k_cache, const void* v_cache, int S_max,
+                      const int32_t* prefix_len, int max_prefix, const uint64_t* mask,
+                      void* out, float* lse, void* workspace, size_t ws_bytes, int32_t* status,
+                      void* stream);
+
+/* Bytes of workspace st_verify_greedy needs. */
+size_t st_verify_greedy_workspace(const st_tree* tree, int V);
+
+/*
+ * st_verify_greedy -- accept the longest verified path (SpecInfer developer
+ * article §2.1).  Row i of `logits` [T][V] fp32 is the target's next-token
+ * distribution after node i; a[i] is its argmax (lowest index on ties).  From
+ * the root, the walk moves to the lowest-index child c with tokens[c] == a[u]
+ * and stops when there is none.
+ *   tokens       [T] int32 draft token of each node (the root's is unused)
+ *   accept_len   [B]   number L of accepted non-root nodes
+ *   accept_nodes [B][max_depth+1] local node ids of the path, root first, -1 padded
+ *   out_tokens   [B][max_depth+2] the L accepted tokens then the target's token
+ *                a[last] (so L+1 tokens are emitted), -1 padded
+ * If the path would pass max_depth nodes below the root it stops there, the
+ * last emitted token is -1 and ST_STATUS_PATH_OVERFLOW is set.
+ */
+int st_verify_greedy(const st_tree* tree, int V, const int32_t* tokens, const float* logits,
+                     int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                     void* workspace, size_t ws_bytes, int32_t* status, void* stream);
+
+/* Bytes of workspace st_verify_stochastic needs. */
+size_t st_verify_stochastic_workspace(const st_tree* tree, int V);
+
+/*
+ * st_verify_stochastic -- rejection sampling down the tree (speculative-
+ * decoding explainer §2.2: accept with probability min(1, p/q), check left to
+ * right, replace at the first rejection so the output keeps the target's
+ * distribution).  p_i = softmax(target_logits[i] / temperature) and q_i =
+ * softmax(draft_logits[i] / temperature) are the target's and the draft's
+ * distributions for the children of node i.  At node u with residual r
+ * (initially p_u) the children are tested in ascending index: child c with
+ * token x is accepted iff u_acc(c) * q_u[x] < r[x]; after a rejection
+ * r <- normalise(max(0, r - q_u)) (unchanged if that has no mass).  On an
+ * acceptance the walk moves to c with r = p_c.  When no child is accepted the
+ * replacement token is the smallest v whose running sum of r (ascending v)
+ * exceeds u_smp(u) * sum(r).  Uniforms come from Philox4x64-10 with key
+ * (seed, 0) and counter (local node, request, offset, 0): u_acc = top 24 bits
+ * of word 0, u_smp = top 24 bits of word 1, times 2^-24.
+ *   target_logits, draft_logits [T][V] fp32; temperature > 0
+ *   outputs as for st_verify_greedy;
+ *   near_ties [B] int32 or NULL: comparisons on the taken path with
+ *   |r[x] - u*q[x]| < 1e-6, plus 1 if the replacement draw's threshold lies
+ *   within 1e-6 * sum(r) of its bin's edges.
+ * Decisions use fp32 exponentials with fp64 sums.
+ */
+int st_verify_stochastic(const st_tree* tree, int V, const int32_t* tokens,
+                         const float* target_logits, const float* draft_logits, float temperature,
+                         uint64_t seed, uint64_t offset, int32_t* accept_len,
+                         int32_t* accept_nodes, int32_t* out_tokens, int32_t* near_ties,
+                         void* workspace, size_t ws_bytes, int32_t* status, void* stream);
+
+/*
+ * st_kv_compact -- move the accepted path's keys and values into contiguous
+ * slots (the depth-first KV-cache update of the SpecInfer news article,
+ * "Token 樹驗證器").  For request b with P = prefix_len[b], L = accept_len[b]
+ * and path = accept_nodes[b][0..L], slot P + j of every kv head takes what
+ * slot P + path[j] held before the call, for j = 0..L, in k_cache and
+ * v_cache ([B][Hkv][S_max][D] of `dtype`, updated in place).  Other slots are
+ * not touched.
+ *   accept_nodes [B][max_path] as written by the verify calls (max_path =
+ *                max_depth + 1)
+ *   src_slot [B][max_path] int32: P + path[j] for j <= L, -1 after
+ *   new_len  [B] int32: P + L + 1
+ * A request whose L + 1 exceeds max_path, or whose path leaves [0, S_max - P),
+ * sets ST_STATUS_PATH_OVERFLOW or ST_STATUS_BAD_PARENT and is left unmoved
+ * (new_len = P).  Call once per layer.
+ */
+int st_kv_compact(int B, int Hkv, int D, st_dtype dtype, void* k_cache, void* v_cache, int S_max,
+                  const int32_t* prefix_len, const int32_t* accept_len,
+                  const int32_t* accept_nodes, int max_path, int32_t* src_slot, int32_t* new_len,
+                  int32_t* status, void* stream);
+
+/* Text for a return code or for a status bit (host memory, static). */
+const char* st_status_str(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ST_H */

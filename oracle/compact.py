@@ -9,6 +9,8 @@ path[0..L] (path[0] = 0, the root) is gathered so that slot P_b + j holds what
 slot P_b + path[j] held before; the committed length becomes P_b + L + 1.  A
 node's slot after the move is P_b + depth, its position in the sequence, so
 position-encoded keys stay valid.  Every copy reads the state before the call.
+A root path strictly increases (parents precede children); a path that does not,
+or that leaves the cache, is rejected (status bit 1) and nothing moves.
 """
 
 from __future__ import annotations
@@ -35,7 +37,8 @@ def kv_compact(k_cache, v_cache, prefix_len, accept_len, accept_nodes, max_path:
             new_len[b] = P
             continue
         path = [int(x) for x in accept_nodes[b, :L + 1]]
-        if any(not (0 <= n and P + n < S_max) for n in path):
+        increasing = all(path[j] > path[j - 1] for j in range(1, len(path)))
+        if not increasing or any(not (0 <= n and P + n < S_max) for n in path):
             status |= STATUS_BAD_PARENT
             new_len[b] = P
             continue

@@ -41,9 +41,10 @@ NEAR_TIE_EPS = 1e-6
 
 def _input_status(node_off, parent, tokens, V, rows):
     status = check_tree(node_off, parent)
+    roots = set(int(x) for x in node_off[:-1])
     T = int(node_off[-1])
     for t in range(T):
-        if not (0 <= int(tokens[t]) < V):
+        if t not in roots and not (0 <= int(tokens[t]) < V):   # a root's token is not checked
             status |= STATUS_BAD_TOKEN
     for r in rows:
         if r is not None and not np.all(np.isfinite(r)):

@@ -1,0 +1,53 @@
+"""The C-ABI library loads without a GPU and exports every function include/st.h
+declares; the Python binding carries the same names.  No compute calls."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_tree_verification_st_amd as st
+from token_tree_verification_st_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", h), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \*]*?\b(st_\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("st_tree_mask", "st_tree_attention", "st_verify_greedy", "st_verify_stochastic",
+              "st_kv_compact", "st_status_str"):
+        assert n in names
+
+
+@pytest.mark.skipif(not os.path.exists(binding.LIB_PATH), reason="libst.so not built")
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+        assert hasattr(st, n) or hasattr(binding, n), f"binding lacks {n}"
+
+
+@pytest.mark.skipif(not os.path.exists(binding.LIB_PATH), reason="libst.so not built")
+def test_host_only_calls():
+    assert st.st_mask_words(1) == 1 and st.st_mask_words(64) == 1 and st.st_mask_words(65) == 2
+    assert st.st_mask_words(256) == 4
+    assert "workspace" in st.st_status_str(-3)
+    assert "parent" in st.st_status_str(1)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,172 @@
+"""GPU parity: ancestor mask (bit-exact) and tree attention (max-abs error) of the
+HIP path against the oracle, through the C ABI."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import (build_workload, make_workload, tree_beam_plus_leaves, tree_chain,
+                   tree_complete_binary, tree_random_attach)
+from token_tree_verification_st_amd import to_device
+from tests.gpu_util import BF16_TOL, F32_TOL, attention_errors, gpu_mask, require_gpu, \
+    sample_rows, say, status_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# ---------------------------------------------------------------- mask
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama7b", "ragged_batch", "stochastic_tree",
+                                  "stochastic_chain"])
+def test_mask_named_workloads(name):
+    wl = make_workload(name, 0)
+    dw = to_device(wl)
+    mask, depth = gpu_mask(dw)
+    ref, ref_depth = oracle.tree_mask(wl.node_off, wl.parent, dw.tree.W)
+    assert np.array_equal(mask, ref)
+    assert np.array_equal(depth, ref_depth)
+    assert status_of(dw) == 0
+
+
+def test_mask_random_trees_all_word_counts():
+    rng = np.random.default_rng(1)
+    trees, sizes = [], [1, 2, 63, 64, 65, 127, 128, 129, 200, 256]
+    for n in sizes:
+        trees.append(tree_random_attach(rng, n, int(rng.integers(1, 40))))
+    trees.append(tree_chain(256))
+    trees.append(tree_complete_binary(255))
+    wl = build_workload("masks", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=0,
+                        prefix_lens=[0] * len(trees), trees=trees, max_depth=255)
+    dw = to_device(wl)
+    mask, depth = gpu_mask(dw)
+    ref, ref_depth = oracle.tree_mask(wl.node_off, wl.parent, 4)
+    assert dw.tree.W == 4
+    assert np.array_equal(mask, ref) and np.array_equal(depth, ref_depth)
+
+
+def test_mask_bad_parent_sets_status():
+    rng = np.random.default_rng(2)
+    wl = build_workload("bad", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=0, prefix_lens=[0, 0],
+                        trees=[tree_chain(5), tree_chain(4)], max_depth=4)
+    wl.parent[3] = 3          # request 0, node 3 points at itself
+    dw = to_device(wl)
+    gpu_mask(dw)
+    assert status_of(dw) & 1
+
+
+# ---------------------------------------------------------------- attention
+
+
+def test_attention_tiny_fp32_full():
+    wl = make_workload("tiny_fp32", 0)
+    err, lerr = attention_errors(wl, to_device(wl))
+    say(f"tiny_fp32 max-abs {err:.2e} lse {lerr:.2e}")
+    assert err <= F32_TOL and lerr <= F32_TOL
+
+
+def _small_case(seed, dtype="bf16", D=128, Hq=4, Hkv=4, B=3, pmax=700, nmax=90, q_sigma=1.0,
+                poison=False):
+    rng = np.random.default_rng(seed)
+    prefix = [int(rng.integers(0, pmax)) for _ in range(B)]
+    trees = [tree_random_attach(rng, int(rng.integers(1, nmax + 1)), 7) for _ in range(B)]
+    return build_workload(f"small{seed}", rng, dtype=dtype, Hq=Hq, Hkv=Hkv, D=D, V=0,
+                          prefix_lens=prefix, trees=trees, max_depth=7, q_sigma=q_sigma,
+                          poison_unused=poison)
+
+
+@pytest.mark.parametrize("seed,D,Hq,Hkv", [(1, 128, 4, 4), (2, 64, 4, 4), (3, 128, 8, 2),
+                                           (4, 64, 6, 3), (5, 128, 16, 1)])
+def test_attention_bf16_small_full(seed, D, Hq, Hkv):
+    wl = _small_case(seed, D=D, Hq=Hq, Hkv=Hkv)
+    err, lerr = attention_errors(wl, to_device(wl))
+    say(f"seed {seed} D {D} Hq {Hq} Hkv {Hkv}: max-abs {err:.2e} lse {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= 1e-3
+
+
+@pytest.mark.parametrize("split_keys", [64, 128, 320])
+def test_attention_forced_splits_and_combine(split_keys, monkeypatch):
+    monkeypatch.setenv("ST_ATTN_SPLIT_KEYS", str(split_keys))
+    for dtype in ("bf16", "f32"):
+        wl = _small_case(10 + split_keys, dtype=dtype, D=64 if dtype == "f32" else 128)
+        err, lerr = attention_errors(wl, to_device(wl))
+        say(f"split {split_keys} {dtype}: max-abs {err:.2e} lse {lerr:.2e}")
+        tol = F32_TOL if dtype == "f32" else BF16_TOL
+        assert err <= tol and lerr <= (F32_TOL if dtype == "f32" else 1e-3)
+
+
+def test_attention_peaked_softmax_exercises_rescaling():
+    wl = _small_case(21, q_sigma=8.0, pmax=1500)
+    err, lerr = attention_errors(wl, to_device(wl))
+    say(f"peaked: max-abs {err:.2e} lse {lerr:.2e}")
+    assert err <= BF16_TOL
+
+
+def test_attention_never_reads_unused_slots():
+    for dtype in ("bf16", "f32"):
+        wl = _small_case(31, dtype=dtype, D=128 if dtype == "bf16" else 64, poison=True)
+        err, _ = attention_errors(wl, to_device(wl))
+        assert err <= (BF16_TOL if dtype == "bf16" else F32_TOL)
+
+
+def test_attention_edge_sizes():
+    rng = np.random.default_rng(41)
+    # single node and empty prefix; prefix that ends exactly on a tile; 256-node tree
+    trees = [tree_chain(1), tree_random_attach(rng, 17, 5), tree_random_attach(rng, 256, 30),
+             tree_chain(64)]
+    wl = build_workload("edges", rng, dtype="bf16", Hq=4, Hkv=2, D=128, V=0,
+                        prefix_lens=[0, 128, 63, 1], trees=trees, max_depth=255)
+    err, lerr = attention_errors(wl, to_device(wl))
+    say(f"edges: max-abs {err:.2e} lse {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= 1e-3
+
+
+def test_attention_bad_prefix_sets_status():
+    wl = _small_case(51)
+    dw = to_device(wl, max_prefix=int(wl.prefix_len.max()) - 1)
+    from token_tree_verification_st_amd import step
+    step.run_mask(dw)
+    step.run_attention(dw)
+    torch.cuda.synchronize()
+    assert status_of(dw) & 16
+
+
+@pytest.mark.parametrize("name", ["llama7b", "ragged_batch", "llama70b_gqa", "stochastic_tree",
+                                  "stochastic_chain"])
+def test_attention_full_size_sampled_rows(name):
+    wl = make_workload(name, 0)
+    nodes, heads = sample_rows(wl)
+    err, lerr = attention_errors(wl, to_device(wl), nodes=nodes, heads=heads)
+    say(f"{name}: {len(nodes)} nodes x {len(heads)} heads, max-abs {err:.2e} lse {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= 1e-3
+
+
+def test_attention_host_errors():
+    from token_tree_verification_st_amd import binding
+    wl = _small_case(61)
+    dw = to_device(wl)
+    lib = binding.load_library()
+    # unsupported head size
+    assert lib.st_tree_attention_workspace(dw.tree.ref, 4, 4, 96, 1, 100) == 0
+    q96 = torch.zeros(dw.T, 4, 96, dtype=torch.bfloat16, device="cuda")
+    rc = lib.st_tree_attention(dw.tree.ref, 4, 4, 96, 1, 0.1, q96.data_ptr(),
+                               dw.k_cache.data_ptr(), dw.v_cache.data_ptr(), dw.S_max,
+                               dw.prefix_len.data_ptr(), dw.max_prefix, dw.buf["mask"].data_ptr(),
+                               q96.data_ptr(), None, None, 0, None, None)
+    assert rc == -2
+    need = lib.st_tree_attention_workspace(dw.tree.ref, 4, 4, 128, 1, dw.max_prefix)
+    if need:
+        rc = lib.st_tree_attention(dw.tree.ref, 4, 4, 128, 1, 0.1, dw.q.data_ptr(),
+                                   dw.k_cache.data_ptr(), dw.v_cache.data_ptr(), dw.S_max,
+                                   dw.prefix_len.data_ptr(), dw.max_prefix,
+                                   dw.buf["mask"].data_ptr(), dw.buf["out"].data_ptr(), None,
+                                   dw.buf["attn_ws"].data_ptr(), need - 1, None, None)
+        assert rc == -3

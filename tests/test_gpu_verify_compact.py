@@ -1,0 +1,235 @@
+"""GPU parity: greedy and stochastic acceptance, KV compaction and the whole step,
+HIP path against the oracle through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import build_workload, make_workload, tree_chain, tree_random_attach
+from token_tree_verification_st_amd import to_device
+from token_tree_verification_st_amd import step as stp
+from tests.gpu_util import device_paths, require_gpu, say, status_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _greedy_gpu(wl, dw=None):
+    dw = dw or to_device(wl)
+    stp.run_verify(dw, stochastic=False)
+    torch.cuda.synchronize()
+    return dw, device_paths(dw)
+
+
+def _assert_paths_equal(res, gpu):
+    al, an, ot = gpu
+    assert np.array_equal(al, res["accept_len"])
+    assert np.array_equal(an, res["accept_nodes"])
+    assert np.array_equal(ot, res["out_tokens"])
+
+
+# ---------------------------------------------------------------- greedy
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama7b", "ragged_batch"])
+def test_greedy_named_workloads(name):
+    wl = make_workload(name, 0)
+    dw, gpu = _greedy_gpu(wl)
+    res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.V, wl.max_depth)
+    _assert_paths_equal(res, gpu)
+    assert status_of(dw) == 0 == res["status"]
+    say(f"{name}: accept_len {gpu[0].tolist()}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_greedy_random_planted_trees(seed):
+    rng = np.random.default_rng(seed)
+    B = 6
+    trees = [tree_random_attach(rng, int(rng.integers(1, 200)), 12) for _ in range(B)]
+    wl = build_workload("g", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=int(rng.integers(3, 5000)),
+                        prefix_lens=[1] * B, trees=trees, max_depth=12, token_rule="plant_leaf_path",
+                        logit_sigma=1.0)
+    # small vocab with few distinct values makes exact ties likely
+    wl.logits[:] = np.round(wl.logits)
+    dw, gpu = _greedy_gpu(wl)
+    res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.V, wl.max_depth)
+    _assert_paths_equal(res, gpu)
+
+
+def test_greedy_status_bits():
+    rng = np.random.default_rng(7)
+    wl = build_workload("s", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=50, prefix_lens=[1, 1],
+                        trees=[tree_chain(6), tree_chain(3)], max_depth=2)
+    wl.tokens[1:6] = wl.logits[0:5].argmax(1)       # request 0 accepts everything
+    dw, gpu = _greedy_gpu(wl)
+    res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.V, wl.max_depth)
+    _assert_paths_equal(res, gpu)
+    assert status_of(dw) & 8 and res["status"] & 8
+    wl.tokens[7] = 50
+    wl.logits[2, 3] = np.nan
+    dw, _ = _greedy_gpu(wl)
+    assert status_of(dw) & 2 and status_of(dw) & 4
+
+
+# ---------------------------------------------------------------- stochastic
+
+
+def _stochastic_check(wl, dw=None):
+    dw = dw or to_device(wl)
+    stp.run_verify(dw, stochastic=True)
+    torch.cuda.synchronize()
+    al, an, ot = device_paths(dw)
+    ties_gpu = dw.buf["near_ties"].cpu().numpy()
+    follow = [an[b][:al[b] + 1] for b in range(wl.B)]
+    res = oracle.verify_stochastic(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.draft_logits,
+                                   wl.V, wl.temperature, wl.rng_seed, wl.rng_offset, wl.max_depth,
+                                   follow=follow)
+    for b in range(wl.B):
+        for (u, c, tie) in res["divergences"][b]:
+            assert tie, f"request {b}: decision at node {u} child {c} differs without a near tie"
+        L = int(al[b])
+        assert np.array_equal(ot[b, :L], res["out_tokens"][b, :L])
+        if ot[b, L] != res["out_tokens"][b, L]:
+            assert res["bonus_tie"][b], f"request {b}: replacement token differs"
+    assert status_of(dw) == 0
+    return dw, (al, an, ot), res, ties_gpu
+
+
+@pytest.mark.parametrize("name", ["stochastic_tree", "stochastic_chain"])
+def test_stochastic_named_workloads(name):
+    wl = make_workload(name, 0)
+    dw, gpu, res, ties_gpu = _stochastic_check(wl)
+    say(f"{name}: accept_len {gpu[0].tolist()} near ties gpu {int(ties_gpu.sum())} "
+        f"oracle {int(res['near_ties'].sum())}")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_stochastic_many_offsets_small_vocab(seed):
+    rng = np.random.default_rng(100 + seed)
+    B = 8
+    trees = [tree_random_attach(rng, int(rng.integers(1, 40)), 6) for _ in range(B)]
+    wl = build_workload("st", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=int(rng.integers(2, 40)),
+                        prefix_lens=[1] * B, trees=trees, max_depth=6, token_rule="draft_sample",
+                        logit_sigma=2.0, draft_noise_sigma=1.0, temperature=0.7 + 0.3 * seed)
+    dw = to_device(wl)
+    for off in range(20):
+        wl.rng_offset = off
+        dw.rng_offset = off
+        _stochastic_check(wl, dw)
+
+
+def test_stochastic_equal_distributions_accept_first_children():
+    rng = np.random.default_rng(5)
+    trees = [tree_random_attach(rng, 30, 6) for _ in range(4)]
+    wl = build_workload("eq", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=1000, prefix_lens=[1] * 4,
+                        trees=trees, max_depth=6, token_rule="uniform", logit_sigma=3.0,
+                        draft_noise_sigma=0.0, temperature=0.7)
+    dw, (al, an, ot), res, _ = _stochastic_check(wl)
+    for b in range(4):
+        lo, hi = int(wl.node_off[b]), int(wl.node_off[b + 1])
+        par = wl.parent[lo:hi]
+        u, path = 0, [0]
+        while True:
+            kids = [c for c in range(hi - lo) if par[c] == u]
+            if not kids:
+                break
+            u = kids[0]
+            path.append(u)
+        assert an[b, :al[b] + 1].tolist() == path
+
+
+# ---------------------------------------------------------------- compaction and whole step
+
+
+def _compact_expect(wl, dw_before_k, dw_before_v, al, an):
+    kn, vn, src, new_len, st = oracle.kv_compact(dw_before_k, dw_before_v, wl.prefix_len, al, an,
+                                                 an.shape[1])
+    return kn, vn, src, new_len, st
+
+
+def test_compaction_random_paths_bit_exact():
+    rng = np.random.default_rng(9)
+    B, Hkv, D = 5, 3, 128
+    trees = [tree_random_attach(rng, int(rng.integers(1, 60)), 9) for _ in range(B)]
+    wl = build_workload("c", rng, dtype="bf16", Hq=Hkv, Hkv=Hkv, D=D, V=0,
+                        prefix_lens=[int(x) for x in rng.integers(0, 300, B)], trees=trees,
+                        max_depth=9)
+    dw = to_device(wl)
+    mp = wl.max_depth + 1
+    an = np.full((B, mp), -1, np.int32)
+    al = np.zeros(B, np.int32)
+    for b in range(B):
+        lo, hi = int(wl.node_off[b]), int(wl.node_off[b + 1])
+        leaf = int(rng.integers(0, hi - lo))
+        path = oracle.root_path(wl.parent[lo:hi], leaf)[::-1]
+        an[b, :len(path)] = path
+        al[b] = len(path) - 1
+    dw.buf["accept_len"].copy_(torch.from_numpy(al))
+    dw.buf["accept_nodes"].copy_(torch.from_numpy(an))
+    stp.run_compact(dw)
+    torch.cuda.synchronize()
+    kn, vn, src, new_len, st = _compact_expect(wl, wl.k_cache, wl.v_cache, al, an)
+    assert np.array_equal(dw.k_cache.cpu().view(torch.int16).numpy().view(np.uint16), kn)
+    assert np.array_equal(dw.v_cache.cpu().view(torch.int16).numpy().view(np.uint16), vn)
+    assert np.array_equal(dw.buf["src_slot"].cpu().numpy(), src)
+    assert np.array_equal(dw.buf["new_len"].cpu().numpy(), new_len)
+    assert status_of(dw) == 0 == st
+
+
+def test_compaction_rejects_bad_paths():
+    rng = np.random.default_rng(10)
+    wl = build_workload("cb", rng, dtype="f32", Hq=2, Hkv=2, D=64, V=0, prefix_lens=[4, 4],
+                        trees=[tree_chain(5), tree_chain(5)], max_depth=4)
+    dw = to_device(wl)
+    an = np.array([[0, 2, 1, -1, -1], [0, 1, 2, 3, 4]], np.int32)
+    al = np.array([2, 7], np.int32)
+    dw.buf["accept_len"].copy_(torch.from_numpy(al))
+    dw.buf["accept_nodes"].copy_(torch.from_numpy(an))
+    stp.run_compact(dw)
+    torch.cuda.synchronize()
+    kn, vn, src, new_len, st = _compact_expect(wl, wl.k_cache, wl.v_cache, al, an)
+    assert status_of(dw) == st == (1 | 8)
+    assert np.array_equal(dw.k_cache.cpu().numpy(), kn)
+    assert np.array_equal(dw.buf["new_len"].cpu().numpy(), new_len)
+
+
+@pytest.mark.parametrize("name,stochastic", [("tiny_fp32", False), ("ragged_batch", False),
+                                             ("stochastic_tree", True)])
+def test_whole_step_matches_oracle(name, stochastic):
+    """mask -> attention -> acceptance -> compaction, as the benchmark runs it."""
+    wl = make_workload(name, 0)
+    dw = to_device(wl)
+    k0, v0 = dw.k_cache.clone(), dw.v_cache.clone()
+    stp.verification_step(dw, stochastic=stochastic)
+    torch.cuda.synchronize()
+    al, an, ot = device_paths(dw)
+    if stochastic:
+        follow = [an[b][:al[b] + 1] for b in range(wl.B)]
+        res = oracle.verify_stochastic(wl.node_off, wl.parent, wl.tokens, wl.logits,
+                                       wl.draft_logits, wl.V, wl.temperature, wl.rng_seed,
+                                       wl.rng_offset, wl.max_depth, follow=follow)
+        assert all(t for d in res["divergences"] for (_, _, t) in d)
+    else:
+        res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.V,
+                                   wl.max_depth)
+        _assert_paths_equal(res, (al, an, ot))
+    # compaction: rows outside [P, P+N) untouched, rows inside as the oracle moves them
+    for b in range(wl.B):
+        P, n = int(wl.prefix_len[b]), int(wl.node_off[b + 1] - wl.node_off[b])
+        for cache, before in ((dw.k_cache, k0), (dw.v_cache, v0)):
+            assert torch.equal(cache[b, :, :P], before[b, :, :P])
+            assert torch.equal(cache[b, :, P + n:], before[b, :, P + n:])
+            L = int(al[b])
+            path = an[b, :L + 1]
+            moved = before[b][:, P + torch.from_numpy(path.astype(np.int64)).cuda()]
+            assert torch.equal(cache[b, :, P:P + L + 1], moved)
+            assert torch.equal(cache[b, :, P + L + 1:P + n], before[b, :, P + L + 1:P + n])
+    assert np.array_equal(dw.buf["new_len"].cpu().numpy(),
+                          wl.prefix_len + al + 1)
+    assert status_of(dw) == 0
+    say(f"{name}: step ok, accept_len {al.tolist()}")

@@ -1,0 +1,29 @@
+"""Token-tree verification on MI355X (gfx950).
+
+The target model's side of tree-based speculative decoding for one attention
+layer, as hand-written HIP kernels behind a C ABI (include/st.h, libst.so):
+ancestor mask, tree-masked split-KV attention, greedy and rejection-sampling
+acceptance, KV compaction.  This package is the thin Python binding; torch
+provides device memory and streams.
+"""
+
+from .binding import (  # noqa: F401
+    LIB_PATH,
+    ST_BF16,
+    ST_F32,
+    ST_MAX_NODES,
+    Tree,
+    decode_status,
+    load_library,
+    st_kv_compact,
+    st_mask_words,
+    st_status_str,
+    st_tree_attention,
+    st_tree_attention_workspace,
+    st_tree_mask,
+    st_verify_greedy,
+    st_verify_greedy_workspace,
+    st_verify_stochastic,
+    st_verify_stochastic_workspace,
+)
+from .device_io import DeviceWorkload, to_device  # noqa: F401

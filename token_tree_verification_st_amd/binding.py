@@ -1,0 +1,254 @@
+"""Thin ctypes binding of libst.so.
+
+Each ``st_*`` function has the name of the C entry point it calls and only
+marshals arguments: torch tensors become device pointers, the stream is
+torch's current stream, and a negative return code raises.  Every step of the
+verification path runs in the library's HIP kernels; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libst.so")
+
+ST_F32, ST_BF16 = 0, 1
+ST_MAX_NODES = 256
+STATUS_BITS = {1: "bad parent", 2: "bad token", 4: "non-finite logit", 8: "path overflow",
+               16: "bad prefix length"}
+
+
+class StTree(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("total_nodes", ctypes.c_int32),
+        ("max_nodes", ctypes.c_int32),
+        ("max_depth", ctypes.c_int32),
+        ("node_off", ctypes.c_void_p),
+        ("parent", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_c = ctypes
+
+
+def _declare(lib):
+    P = _c.c_void_p
+    I = _c.c_int
+    S = _c.c_size_t
+    TP = _c.POINTER(StTree)
+    sig = {
+        "st_mask_words": (I, [I]),
+        "st_tree_mask": (I, [TP, P, P, P, P]),
+        "st_tree_attention_workspace": (S, [TP, I, I, I, I, I]),
+        "st_tree_attention": (I, [TP, I, I, I, I, _c.c_float, P, P, P, I, P, I, P, P, P, P, S, P,
+                                  P]),
+        "st_verify_greedy_workspace": (S, [TP, I]),
+        "st_verify_greedy": (I, [TP, I, P, P, P, P, P, P, S, P, P]),
+        "st_verify_stochastic_workspace": (S, [TP, I]),
+        "st_verify_stochastic": (I, [TP, I, P, P, P, _c.c_float, _c.c_uint64, _c.c_uint64, P, P,
+                                     P, P, P, S, P, P]),
+        "st_kv_compact": (I, [I, I, I, I, P, P, I, P, P, P, I, P, P, P, P]),
+        "st_status_str": (_c.c_char_p, [I]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libst.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m token_tree_verification_st_amd.build`")
+        _lib = _declare(ctypes.CDLL(path))
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load_library().st_status_str(rc).decode()
+        raise RuntimeError(f"{what} failed: {msg} ({rc})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, numel=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return t
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def decode_status(word: int) -> list:
+    return [txt for bit, txt in STATUS_BITS.items() if word & bit]
+
+
+@dataclass
+class Tree:
+    """A batch of token trees on the device (request-local parent indices)."""
+
+    node_off: torch.Tensor    # int32 [B+1]
+    parent: torch.Tensor      # int32 [T]
+    max_nodes: int
+    max_depth: int
+
+    def __post_init__(self):
+        _dev(self.node_off, "node_off", torch.int32)
+        _dev(self.parent, "parent", torch.int32)
+        if not (1 <= self.max_nodes <= ST_MAX_NODES):
+            raise ValueError(f"max_nodes must be in [1, {ST_MAX_NODES}]")
+        self.B = self.node_off.numel() - 1
+        self.T = self.parent.numel()
+        self.c = StTree(self.B, self.T, self.max_nodes, self.max_depth,
+                        self.node_off.data_ptr(), self.parent.data_ptr())
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+    @property
+    def W(self) -> int:
+        return (self.max_nodes + 63) // 64
+
+
+def st_mask_words(max_nodes: int) -> int:
+    return load_library().st_mask_words(max_nodes)
+
+
+def st_tree_mask(tree: Tree, mask: torch.Tensor, depth: torch.Tensor, status=None):
+    _dev(mask, "mask", torch.int64, tree.T * tree.W)
+    _dev(depth, "depth", torch.int32, tree.T)
+    _check(load_library().st_tree_mask(tree.ref, _ptr(mask), _ptr(depth), _ptr(status),
+                                       _stream()), "st_tree_mask")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ST_F32
+    if t.dtype == torch.bfloat16:
+        return ST_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def st_tree_attention_workspace(tree: Tree, Hq: int, Hkv: int, D: int, dtype: torch.dtype,
+                                max_prefix: int) -> int:
+    code = ST_F32 if dtype == torch.float32 else ST_BF16
+    return load_library().st_tree_attention_workspace(tree.ref, Hq, Hkv, D, code, max_prefix)
+
+
+def st_tree_attention(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix: int, mask, out,
+                      lse=None, workspace=None, scale: Optional[float] = None, status=None):
+    """q [T][Hq][D]; caches [B][Hkv][S_max][D]; out like q; lse fp32 [T][Hq] or None."""
+    T, Hq, D = q.shape
+    B, Hkv, S_max, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or T != tree.T or B != tree.B:
+        raise ValueError("shape mismatch between q, caches and tree")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
+        _dev(t, name, q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _dev(prefix_len, "prefix_len", torch.int32, B)
+    _dev(mask, "mask", torch.int64, tree.T * tree.W)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, T * Hq)
+    need = st_tree_attention_workspace(tree, Hq, Hkv, D, q.dtype, max_prefix)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        raise ValueError(f"workspace needs {need} bytes")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(load_library().st_tree_attention(
+        tree.ref, Hq, Hkv, D, _dtype_code(q), scale, _ptr(q), _ptr(k_cache), _ptr(v_cache), S_max,
+        _ptr(prefix_len), max_prefix, _ptr(mask), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _ptr(status), _stream()), "st_tree_attention")
+
+
+def st_verify_greedy_workspace(tree: Tree, V: int) -> int:
+    return load_library().st_verify_greedy_workspace(tree.ref, V)
+
+
+def _path_outputs(tree: Tree, accept_len, accept_nodes, out_tokens):
+    _dev(accept_len, "accept_len", torch.int32, tree.B)
+    _dev(accept_nodes, "accept_nodes", torch.int32, tree.B * (tree.max_depth + 1))
+    _dev(out_tokens, "out_tokens", torch.int32, tree.B * (tree.max_depth + 2))
+
+
+def st_verify_greedy(tree: Tree, tokens, logits, accept_len, accept_nodes, out_tokens,
+                     workspace, status=None):
+    T, V = logits.shape
+    _dev(tokens, "tokens", torch.int32, tree.T)
+    _dev(logits, "logits", torch.float32)
+    _path_outputs(tree, accept_len, accept_nodes, out_tokens)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().st_verify_greedy(
+        tree.ref, V, _ptr(tokens), _ptr(logits), _ptr(accept_len), _ptr(accept_nodes),
+        _ptr(out_tokens), _ptr(workspace), ws_bytes, _ptr(status), _stream()), "st_verify_greedy")
+
+
+def st_verify_stochastic_workspace(tree: Tree, V: int) -> int:
+    return load_library().st_verify_stochastic_workspace(tree.ref, V)
+
+
+def st_verify_stochastic(tree: Tree, tokens, target_logits, draft_logits, temperature: float,
+                         seed: int, offset: int, accept_len, accept_nodes, out_tokens, workspace,
+                         near_ties=None, status=None):
+    T, V = target_logits.shape
+    _dev(tokens, "tokens", torch.int32, tree.T)
+    _dev(target_logits, "target_logits", torch.float32)
+    _dev(draft_logits, "draft_logits", torch.float32)
+    if draft_logits.shape != target_logits.shape:
+        raise ValueError("draft_logits must match target_logits")
+    _path_outputs(tree, accept_len, accept_nodes, out_tokens)
+    if near_ties is not None:
+        _dev(near_ties, "near_ties", torch.int32, tree.B)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().st_verify_stochastic(
+        tree.ref, V, _ptr(tokens), _ptr(target_logits), _ptr(draft_logits), float(temperature),
+        int(seed), int(offset), _ptr(accept_len), _ptr(accept_nodes), _ptr(out_tokens),
+        _ptr(near_ties), _ptr(workspace), ws_bytes, _ptr(status), _stream()),
+        "st_verify_stochastic")
+
+
+def st_kv_compact(k_cache, v_cache, prefix_len, accept_len, accept_nodes, src_slot, new_len,
+                  status=None):
+    """k_cache / v_cache [B][Hkv][S_max][D], updated in place."""
+    B, Hkv, S_max, D = k_cache.shape
+    _dev(k_cache, "k_cache")
+    _dev(v_cache, "v_cache", k_cache.dtype)
+    max_path = accept_nodes.shape[-1]
+    _dev(prefix_len, "prefix_len", torch.int32, B)
+    _dev(accept_len, "accept_len", torch.int32, B)
+    _dev(accept_nodes, "accept_nodes", torch.int32, B * max_path)
+    _dev(src_slot, "src_slot", torch.int32, B * max_path)
+    _dev(new_len, "new_len", torch.int32, B)
+    _check(load_library().st_kv_compact(
+        B, Hkv, D, _dtype_code(k_cache), _ptr(k_cache), _ptr(v_cache), S_max, _ptr(prefix_len),
+        _ptr(accept_len), _ptr(accept_nodes), max_path, _ptr(src_slot), _ptr(new_len),
+        _ptr(status), _stream()), "st_kv_compact")
+
+
+def st_status_str(code: int) -> str:
+    return load_library().st_status_str(code).decode()
