@@ -126,38 +126,48 @@ def main():
     torch.cuda.synchronize()
 
     # The K timed steps are captured into one HIP graph (replica i % R for step
-    # i), so host launch cost does not pace the GPU.  Event-record nodes
-    # between the calls give each call's duration inside the timed replay.
+    # i), so host launch cost does not pace the GPU; events on the stream
+    # bracket its replay.  Each call is then timed the same way from a graph
+    # of K back-to-back launches of that call alone (same replicas, same
+    # stream), which gives its average launch duration.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True, external=True) for _ in range(len(calls) + 1)]
-          for _ in range(K)]
-    graph = None
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             for i in range(K):
-                d = reps[i % R]
-                ev[i][0].record()
-                for j, c in enumerate(calls):
-                    fns[c](d)
-                    ev[i][j + 1].record()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if graph is not None:
-        graph.replay()
-    else:
+                fn(reps[i % R])
+        return g
+
+    def timed_replay(g):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t, e0.elapsed_time(e1)
+
+    step_fn = lambda d: stp.verification_step(d, stochastic=stochastic)
+    if args.eager:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
         for i in range(K):
-            d = reps[i % R]
-            ev[i][0].record()
-            for j, c in enumerate(calls):
-                fns[c](d)
-                ev[i][j + 1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_call = {c: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K * 1e3
-                for j, c in enumerate(calls)}  # us
-    gpu_span_ms = ev[0][0].elapsed_time(ev[K - 1][len(calls)])
+            step_fn(reps[i % R])
+        e1.record()
+        torch.cuda.synchronize()
+        wall, gpu_span_ms = time.perf_counter() - t0, e0.elapsed_time(e1)
+    else:
+        g_step = capture(step_fn)
+        wall, gpu_span_ms = timed_replay(g_step)
     ms_per_step = wall / K * 1e3
+    per_call = {}
+    for c in calls:
+        _, ms = timed_replay(capture(fns[c]))
+        per_call[c] = ms / K * 1e3  # us per launch
     st_words = [int(r.buf["status"].item()) for r in reps]
     assert not any(st_words), f"device status {st_words}"
 
@@ -171,7 +181,8 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "st_tree_attention", "algorithmic_bytes": attn_bytes,
-            "avg_launch_us": round(attn_us, 3)}
+            "avg_launch_us": round(attn_us, 3),
+            "timing": f"HIP events around a graph of {K} back-to-back st_tree_attention calls"}
     al = reps[0].buf["accept_len"].cpu().numpy() if wl.V else np.zeros(wl.B)
     line = {
         "metric": "verified tree tokens/s (7B-shaped layer, 64-node tree, 4K prefix); % HBM peak",
