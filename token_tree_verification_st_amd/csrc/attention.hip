@@ -35,10 +35,18 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kKT = 64;  // keys per tile
+// MFMA workgroup shapes (row-waves of 16 rows x key groups); the plan picks one
+struct Shape {
+  int rw, kw;
+};
+constexpr Shape kShapes[] = {{4, 1}, {4, 2}, {2, 2}, {2, 4}, {1, 4}};
 
 struct AttnArgs {
   const int32_t* node_off;
@@ -53,7 +61,7 @@ struct AttnArgs {
   float* ws_acc;   // [NS][T*Hq][D]
   int32_t* status;
   int B, T, Hq, Hkv, G, S_max, W, max_nodes, max_prefix;
-  int KS;          // keys per split (multiple of kKT)
+  int KS;          // keys per split (multiple of 16)
   int NS;          // splits of the longest request
   int RB;          // rows per workgroup
   int n_rblk;      // row blocks of the widest request
@@ -108,102 +116,88 @@ __device__ inline bool tree_bit(uint64_t w0, uint64_t w1, uint64_t w2, uint64_t 
 
 // ---------------------------------------------------------------- bf16 MFMA
 
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
+// memory, which makes every wave wait for all of its outstanding global loads
+// -- including the prefetch of later tiles that should stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// V tiles sit in LDS in their natural [key][dim] layout (256-byte rows, no
+// padding).  The MFMA operand V^T is read with ds_read_b64_tr_b16, which
+// hands each lane one dim of four keys.  Each 16-byte chunk c of key row r is
+// stored at chunk position c ^ vswz(r): the 16 lanes of one transposed read
+// touch four key rows x two chunks, which land on eight distinct positions.
+// (masked to the row's chunk count, so a position never leaves its row)
 template <int D>
-__global__ void __launch_bounds__(256)
-attn_mfma_kernel(AttnArgs a) {
-  constexpr int DP = D + 8;       // K row pitch (bf16): 16-byte pad
-  constexpr int KP = kKT + 4;     // V^T row pitch (bf16): 8-byte pad
-  constexpr int NKS = D / 32;     // k-steps of S^T
-  constexpr int NDB = D / 16;     // d-blocks of O^T
-  constexpr int CH = D / 8;       // 16-byte chunks per key row
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kKT * DP];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * KP];
+__device__ __forceinline__ int vswz(int key) {
+  return (((key & 3) << 1) | (((key >> 2) & 1) << 3)) & (D / 8 - 1);
+}
 
-  Item it;
-  if (!decode_item(a, it)) return;
-  const ReqInfo rq = request_info(a, it.b);
-  if (!rq.ok) {
-    if (threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
-      st::set_status(a.status, ST_STATUS_BAD_PREFIX);
-    return;
-  }
-  const int rows_b = rq.n * a.G;
-  if (it.rblk * 64 >= rows_b) return;
-  const int k0 = it.split * a.KS;
-  if (k0 >= rq.key_end) return;
-  const int k1 = min(k0 + a.KS, rq.key_end);
+// What one thread of a key group (GS threads) moves from global memory to LDS
+// for one 64-key tile: N 16-byte chunks of K rows and N of V rows.
+template <int D, int GS>
+struct TileRegs {
+  static constexpr int CH = D / 8;
+  static constexpr int TOT = kKT * CH;
+  static constexpr int N = (TOT + GS - 1) / GS;
+  u32x4 k[N];
+  u32x4 v[N];
+};
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r16 = lane & 15, grp = lane >> 4;
-  const int row = it.rblk * 64 + wave * 16 + r16;
-  const bool row_ok = row < rows_b;
-  const int node = row_ok ? row / a.G : 0;
-  const int hq = it.g * a.G + (row_ok ? row % a.G : 0);
-  const int grow = (rq.lo + node) * a.Hq + hq;
-
-  const uint16_t* qp = (const uint16_t*)a.q + (size_t)grow * D;
-  bf16x8 qf[NKS];
+// Every load is issued unconditionally (the compiler can then count them and
+// keep the next round in flight): key indices are clamped into [k0, k1 - 1],
+// so rows past the end of the range hold copies of valid rows, which the
+// score mask excludes and which meet a zero probability in P V.
+template <int D, int GS>
+__device__ __forceinline__ void tile_load(TileRegs<D, GS>& r, const uint16_t* kg, const uint16_t* vg,
+                                          int kt, int klast, int gt) {
+  using TR = TileRegs<D, GS>;
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    uint4 u = row_ok ? *(const uint4*)(qp + 32 * s + 8 * grp) : make_uint4(0, 0, 0, 0);
-    qf[s] = __builtin_bit_cast(bf16x8, u);
+  for (int i = 0; i < TR::N; ++i) {
+    const int e = min(gt + i * GS, TR::TOT - 1), row = e / TR::CH, c = e % TR::CH;
+    const size_t off = (size_t)min(kt + row, klast) * D + 8 * c;
+    r.k[i] = *(const u32x4*)(kg + off);
+    r.v[i] = *(const u32x4*)(vg + off);
   }
-  uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
-  if (row_ok) {
-    const uint64_t* mr = a.mask + (size_t)(rq.lo + node) * a.W;
-    mw0 = mr[0];
-    if (a.W > 1) mw1 = mr[1];
-    if (a.W > 2) mw2 = mr[2];
-    if (a.W > 3) mw3 = mr[3];
-  }
+}
 
-  const size_t head_off = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
-  const uint16_t* kg = (const uint16_t*)a.k + head_off;
-  const uint16_t* vg = (const uint16_t*)a.v + head_off;
-
-  f32x4 acc[NDB];
+template <int D, int GS>
+__device__ __forceinline__ void tile_store(const TileRegs<D, GS>& r, uint16_t* sK, uint16_t* sV,
+                                           int gt) {
+  using TR = TileRegs<D, GS>;
+  constexpr int DP = D + 8;
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
-
-  // cooperative tile loads: K rows straight, V rows as 4-key x 8-dim blocks
-  for (int kt = k0; kt < k1; kt += kKT) {
-    const int nk = min(kKT, k1 - kt);
-    __syncthreads();
-#pragma unroll
-    for (int e = tid; e < kKT * CH; e += 256) {
-      const int r = e / CH, c = e % CH;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (r < nk) u = *(const uint4*)(kg + (size_t)(kt + r) * D + 8 * c);
-      *(uint4*)(&sK[r * DP + 8 * c]) = u;
+  for (int i = 0; i < TR::N; ++i) {
+    const int e = gt + i * GS, row = e / TR::CH, c = e % TR::CH;
+    if (TR::N * GS == TR::TOT || e < TR::TOT) {
+      *(u32x4*)(&sK[row * DP + 8 * c]) = r.k[i];
+      *(u32x4*)(&sV[row * D + 8 * (c ^ vswz<D>(row))]) = r.v[i];
     }
-#pragma unroll
-    for (int e = tid; e < (kKT / 4) * CH; e += 256) {
-      const int quad = e / CH, c = e % CH;
-      uint4 x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * quad + i;
-        x[i] = r < nk ? *(const uint4*)(vg + (size_t)(kt + r) * D + 8 * c) : make_uint4(0, 0, 0, 0);
-      }
-      const uint32_t* x0 = (const uint32_t*)&x[0];
-      const uint32_t* x1 = (const uint32_t*)&x[1];
-      const uint32_t* x2 = (const uint32_t*)&x[2];
-      const uint32_t* x3 = (const uint32_t*)&x[3];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        uint2 lo2, hi2;  // dims 8c+2e2 and 8c+2e2+1, keys 4quad..4quad+3
-        lo2.x = (x0[e2] & 0xFFFFu) | (x1[e2] << 16);
-        lo2.y = (x2[e2] & 0xFFFFu) | (x3[e2] << 16);
-        hi2.x = (x0[e2] >> 16) | (x1[e2] & 0xFFFF0000u);
-        hi2.y = (x2[e2] >> 16) | (x3[e2] & 0xFFFF0000u);
-        *(uint2*)(&sVt[(8 * c + 2 * e2) * KP + 4 * quad]) = lo2;
-        *(uint2*)(&sVt[(8 * c + 2 * e2 + 1) * KP + 4 * quad]) = hi2;
-      }
-    }
-    __syncthreads();
+  }
+}
 
-    // S^T = K Q^T over four 16-key blocks
+struct TileCtx {
+  int P, k1, r16, grp;
+  float scale_log2;
+  uint64_t mw0, mw1, mw2, mw3;
+};
+
+// One wavefront's work on one 64-key tile in LDS: S^T = K Q^T, mask, online
+// softmax update of (m, lsum, acc), O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void tile_compute(const TileCtx& cx, const uint16_t* sK,
+                                             const uint16_t* sV, int kt,
+                                             const bf16x8 (&qf)[D / 32], f32x4 (&acc)[D / 16],
+                                             float& m, float& lsum) {
+  constexpr int DP = D + 8, NKS = D / 32, NDB = D / 16;
+  const int r16 = cx.r16, grp = cx.grp;
+
+    // S^T = K Q^T over four 16-key blocks; lane holds keys kt+16kb+4grp+j
     f32x4 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -215,17 +209,19 @@ attn_mfma_kernel(AttnArgs a) {
                                                         s[kb], 0, 0, 0);
       }
     }
-    // scale, mask, tile max (lane holds keys kt + 16kb + 4grp + j of its row)
-    const bool tree_tile = kt + kKT > rq.P;
+    const bool edge = kt + kKT > cx.P || kt + kKT > cx.k1;
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int key = kt + 16 * kb + 4 * grp + j;
-        bool vis = key < k1;
-        if (tree_tile && key >= rq.P) vis = vis && tree_bit(mw0, mw1, mw2, mw3, key - rq.P);
-        const float x = vis ? s[kb][j] * a.scale_log2 : -INFINITY;
+        float x = s[kb][j] * cx.scale_log2;
+        if (edge) {
+          const int key = kt + 16 * kb + 4 * grp + j;
+          bool vis = key < cx.k1;
+          if (key >= cx.P) vis = vis && tree_bit(cx.mw0, cx.mw1, cx.mw2, cx.mw3, key - cx.P);
+          x = vis ? x : -INFINITY;
+        }
         s[kb][j] = x;
         tmax = fmaxf(tmax, x);
       }
@@ -234,13 +230,13 @@ attn_mfma_kernel(AttnArgs a) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, ST_WAVE));
     const float m_new = fmaxf(m, tmax);
     const float mref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m - mref);
+    const float alpha = fast_exp2(m - mref);
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p = exp2f(s[kb][j] - mref);
+        const float p = fast_exp2(s[kb][j] - mref);
         s[kb][j] = p;
         psum += p;
       }
@@ -259,23 +255,169 @@ attn_mfma_kernel(AttnArgs a) {
         pb[t][4 + j] = (__bf16)s[2 * t + 1][j];
       }
     }
-    // O^T += V^T P^T
+    // O^T += V^T P^T.  Transposed reads: lane k = 4j + q of each 16-lane
+    // group points at V[key_j][16db + 4q .. +3]; lane i then receives dim
+    // 16db + i of key_0..key_3 (keys 32t + 4grp + j, and + 16 for slots 4-7).
+    const int jq = r16 >> 2, qq = r16 & 3;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const uint16_t* vr = &sVt[(16 * db + r16) * KP + 32 * t + 4 * grp];
-        const uint2 lo2 = *(const uint2*)vr;
-        const uint2 hi2 = *(const uint2*)(vr + 16);
-        const uint4 u = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+        const int key1 = 32 * t + 4 * grp + jq, key2 = key1 + 16;
+        const int c = 2 * db + (qq >> 1), sub = 4 * (qq & 1);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(sV + key1 * D + 8 * (c ^ vswz<D>(key1)) + sub));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(sV + key2 * D + 8 * (c ^ vswz<D>(key2)) + sub));
+        const v8i16 u = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), pb[t],
                                                          acc[db], 0, 0, 0);
       }
+    }
+}
+
+// One workgroup = RW row-waves x KW key groups.  Row-wave rw owns 16 query
+// rows; key group kg takes every KW-th 64-key tile of the workgroup's key
+// range, with its own LDS buffers and its own running softmax state.  The
+// tiles of the next round are loaded into registers while the current round
+// is computed.  At the end the key groups' states are merged through LDS.
+template <int D, int RW, int KW>
+__global__ void __launch_bounds__(64 * RW * KW)
+attn_mfma_kernel(AttnArgs a) {
+  constexpr int GS = 64 * RW;      // threads per key group
+  constexpr int ROWS = 16 * RW;    // query rows per workgroup
+  constexpr int DP = D + 8;        // K row pitch (bf16): 16-byte pad
+  constexpr int NKS = D / 32;      // k-steps of S^T
+  constexpr int NDB = D / 16;      // d-blocks of O^T
+  constexpr int KEL = kKT * DP, VEL = kKT * D;
+  constexpr int MERGE_FLOATS = (KW - 1) * RW * 64 * (4 * NDB + 2);
+  constexpr int TILE_BYTES = KW * (KEL + VEL) * 2;
+  constexpr int LDS_BYTES = TILE_BYTES > MERGE_FLOATS * 4 ? TILE_BYTES : MERGE_FLOATS * 4;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_BYTES / 2];
+
+  Item it;
+  if (!decode_item(a, it)) return;
+  const ReqInfo rq = request_info(a, it.b);
+  if (!rq.ok) {
+    if (threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
+      st::set_status(a.status, ST_STATUS_BAD_PREFIX);
+    return;
+  }
+  const int rows_b = rq.n * a.G;
+  if (it.rblk * ROWS >= rows_b) return;
+  const int k0 = it.split * a.KS;
+  if (k0 >= rq.key_end) return;
+  const int k1 = min(k0 + a.KS, rq.key_end);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rw = wave % RW, kg = wave / RW, gt = tid % GS;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int row = it.rblk * ROWS + rw * 16 + r16;
+  const bool row_ok = row < rows_b;
+  const int node = row_ok ? row / a.G : 0;
+  const int hq = it.g * a.G + (row_ok ? row % a.G : 0);
+  const int grow = (rq.lo + node) * a.Hq + hq;
+  uint16_t* sK = lds + kg * (KEL + VEL);
+  uint16_t* sV = sK + KEL;
+
+  const uint16_t* qp = (const uint16_t*)a.q + (size_t)grow * D;
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    uint4 u = row_ok ? *(const uint4*)(qp + 32 * s + 8 * grp) : make_uint4(0, 0, 0, 0);
+    qf[s] = __builtin_bit_cast(bf16x8, u);
+  }
+  uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
+  if (row_ok) {
+    const uint64_t* mr = a.mask + (size_t)(rq.lo + node) * a.W;
+    mw0 = mr[0];
+    if (a.W > 1) mw1 = mr[1];
+    if (a.W > 2) mw2 = mr[2];
+    if (a.W > 3) mw3 = mr[3];
+  }
+  const size_t head_off = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
+  const uint16_t* kgp = (const uint16_t*)a.k + head_off;
+  const uint16_t* vgp = (const uint16_t*)a.v + head_off;
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+
+  const int niters = (k1 - k0 + KW * kKT - 1) / (KW * kKT);
+  // Software pipeline two rounds deep: the tiles of round r+2 load into the
+  // register set that round r has just stored to LDS, so two rounds of loads
+  // are in flight while round r is computed.
+  auto tile_at = [&](int r) { return k0 + (r * KW + kg) * kKT; };
+  const TileCtx cx{rq.P, k1, r16, grp, a.scale_log2, mw0, mw1, mw2, mw3};
+  TileRegs<D, GS> ra, rb;
+  const int klast = k1 - 1;
+  // keep the two rounds' loads in program order (the wait before each store
+  // counts on it)
+  tile_load<D, GS>(ra, kgp, vgp, tile_at(0), klast, gt);
+  __builtin_amdgcn_sched_barrier(0);
+  tile_load<D, GS>(rb, kgp, vgp, tile_at(1), klast, gt);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int iter = 0; iter < niters; iter += 2) {
+    {
+      const int kt = tile_at(iter), nk = min(kKT, k1 - kt);
+      lds_barrier();
+      tile_store<D, GS>(ra, sK, sV, gt);
+      lds_barrier();
+      // unconditional (past the end it re-reads the clamped last row), so the
+      // compiler can wait for exactly the older round at the next store
+      __builtin_amdgcn_sched_barrier(0);
+      tile_load<D, GS>(ra, kgp, vgp, tile_at(iter + 2), klast, gt);
+      __builtin_amdgcn_sched_barrier(0);
+      if (nk > 0) tile_compute<D>(cx, sK, sV, kt, qf, acc, m, lsum);
+    }
+    {  // runs even past the last round (its compute is then skipped): no early
+       // exit, so the wait counts stay exact
+      const int kt = tile_at(iter + 1), nk = min(kKT, k1 - kt);
+      lds_barrier();
+      tile_store<D, GS>(rb, sK, sV, gt);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      tile_load<D, GS>(rb, kgp, vgp, tile_at(iter + 3), klast, gt);
+      __builtin_amdgcn_sched_barrier(0);
+      if (nk > 0) tile_compute<D>(cx, sK, sV, kt, qf, acc, m, lsum);
     }
   }
 
   lsum += __shfl_xor(lsum, 16, ST_WAVE);
   lsum += __shfl_xor(lsum, 32, ST_WAVE);
+  if constexpr (KW > 1) {
+    // merge the key groups' states into group 0 (struct of arrays, lane-major)
+    float* mb = (float*)lds;
+    constexpr int SLOTS = (KW - 1) * RW * 64;
+    __syncthreads();
+    if (kg > 0) {
+      const int sl = ((kg - 1) * RW + rw) * 64 + lane;
+      mb[sl] = m;
+      mb[SLOTS + sl] = lsum;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mb[(2 + 4 * db + j) * SLOTS + sl] = acc[db][j];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int k = 1; k < KW; ++k) {
+      const int sl = ((k - 1) * RW + rw) * 64 + lane;
+      const float mk = mb[sl], lk = mb[SLOTS + sl];
+      const float M = fmaxf(m, mk);
+      const float ref = M == -INFINITY ? 0.f : M;
+      const float e0 = fast_exp2(m - ref), e1 = fast_exp2(mk - ref);
+      lsum = lsum * e0 + lk * e1;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[db][j] = acc[db][j] * e0 + mb[(2 + 4 * db + j) * SLOTS + sl] * e1;
+      m = M;
+    }
+  }
   if (!row_ok) return;
   if (rq.nsplit == 1) {
     const float inv = 1.f / lsum;
@@ -445,11 +587,14 @@ attn_valu_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- combine
 
+// Merge the splits of every row: the partial (m, l) pairs and 4 dims of the
+// partial outputs of up to 8 splits are all loaded before any is used.
 template <typename Tout, int D>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(AttnArgs a) {
   constexpr int LPR = D / 4;        // lanes per row, 4 dims each
   constexpr int RPB = 256 / LPR;    // rows per block
+  constexpr int CHUNK = 8;
   const int grow = blockIdx.x * RPB + threadIdx.x / LPR;
   const int d = 4 * (threadIdx.x % LPR);
   const int TH = a.T * a.Hq;
@@ -458,17 +603,36 @@ attn_combine_kernel(AttnArgs a) {
   const int b = st::request_of(a.node_off, a.B, t);
   const ReqInfo rq = request_info(a, b);
   if (!rq.ok || rq.nsplit <= 1) return;
-  float M = -INFINITY;
-  for (int s = 0; s < rq.nsplit; ++s) M = fmaxf(M, a.ws_ml[(size_t)s * TH + grow].x);
-  float L = 0.f;
+  const int ns = rq.nsplit;
+  float M = -INFINITY, L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < rq.nsplit; ++s) {
-    const size_t pr = (size_t)s * TH + grow;
-    const float2 ml = a.ws_ml[pr];
-    const float w = exp2f(ml.x - M);  // empty split: exp2(-inf) = 0
-    L += w * ml.y;
-    const f32x4 x = *(const f32x4*)(a.ws_acc + pr * D + d);
-    o += w * x;
+  for (int s0 = 0; s0 < ns; s0 += CHUNK) {
+    float2 ml[CHUNK];
+    f32x4 x[CHUNK];
+#pragma unroll
+    for (int j = 0; j < CHUNK; ++j) {
+      const int s = min(s0 + j, ns - 1);
+      const size_t pr = (size_t)s * TH + grow;
+      ml[j] = a.ws_ml[pr];
+      x[j] = *(const f32x4*)(a.ws_acc + pr * D + d);
+    }
+    float Mc = M;
+#pragma unroll
+    for (int j = 0; j < CHUNK; ++j)
+      if (s0 + j < ns) Mc = fmaxf(Mc, ml[j].x);
+    const float ref = Mc == -INFINITY ? 0.f : Mc;
+    const float sc = exp2f(M - ref);  // rescale what is merged so far
+    L *= sc;
+    o *= sc;
+#pragma unroll
+    for (int j = 0; j < CHUNK; ++j) {
+      if (s0 + j < ns) {
+        const float w = exp2f(ml[j].x - ref);  // empty split: exp2(-inf) = 0
+        L += w * ml[j].y;
+        o += w * x[j];
+      }
+    }
+    M = Mc;
   }
   const float inv = 1.f / L;
   Tout* op = (Tout*)a.out + (size_t)grow * D + d;
@@ -481,6 +645,7 @@ attn_combine_kernel(AttnArgs a) {
 
 struct Plan {
   bool mfma;
+  int shape;
   int RB, n_rblk, KS, NS, items, per_xcd;
   size_t ml_bytes, ws_bytes;
 };
@@ -499,19 +664,23 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
   if (Hq % Hkv || (D != 64 && D != 128)) return ST_E_UNSUPPORTED;
   const int G = Hq / Hkv;
   p.mfma = dtype == ST_BF16;
-  p.RB = p.mfma ? 64 : 16;
+  p.shape = env_int("ST_ATTN_SHAPE", 0);
+  if (p.shape < 0 || p.shape >= (int)(sizeof(kShapes) / sizeof(kShapes[0]))) p.shape = 0;
+  p.RB = p.mfma ? 16 * kShapes[p.shape].rw : 16;
   p.n_rblk = (t->max_nodes * G + p.RB - 1) / p.RB;
   const long keys_max = (long)max_prefix + t->max_nodes;
   const long base = (long)t->B * Hkv * p.n_rblk;
-  // aim for about `target` workgroups over the whole batch; the key range of
-  // one split is a whole number of tiles
-  const long target = env_int("ST_ATTN_TARGET_WG", 512);
-  long ks = (keys_max * base + target - 1) / target;
-  ks = (ks + kKT - 1) / kKT * kKT;
+  // aim for about `target` workgroups over the whole batch (one per CU for
+  // the MFMA kernel); splits are even, in multiples of 16 keys
+  const long target = env_int("ST_ATTN_TARGET_WG", p.mfma ? 256 : 512);
+  long ns = (target + base - 1) / base;
+  if (ns < 1) ns = 1;
+  long ks = (keys_max + ns - 1) / ns;
+  ks = (ks + 15) / 16 * 16;
   const int forced = env_int("ST_ATTN_SPLIT_KEYS", 0);
-  if (forced > 0) ks = (forced + kKT - 1) / kKT * kKT;
-  const long kmax = (keys_max + kKT - 1) / kKT * kKT;
-  if (ks < kKT) ks = kKT;
+  if (forced > 0) ks = (forced + 15) / 16 * 16;
+  const long kmax = (keys_max + 15) / 16 * 16;
+  if (ks < 64) ks = 64;
   if (ks > kmax) ks = kmax;
   p.KS = (int)ks;
   p.NS = (int)((keys_max + ks - 1) / ks);
@@ -580,8 +749,19 @@ extern "C" int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(8 * p.per_xcd), block(256);
   if (p.mfma) {
-    if (D == 128) hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, block, 0, s, a);
+    const Shape sh = kShapes[p.shape];
+    const dim3 mblock(64 * sh.rw * sh.kw);
+#define ST_LAUNCH_MFMA(RW_, KW_)                                                             \
+  if (sh.rw == RW_ && sh.kw == KW_) {                                                       \
+    if (D == 128) hipLaunchKernelGGL((attn_mfma_kernel<128, RW_, KW_>), grid, mblock, 0, s, a); \
+    else hipLaunchKernelGGL((attn_mfma_kernel<64, RW_, KW_>), grid, mblock, 0, s, a);          \
+  }
+    ST_LAUNCH_MFMA(4, 2)
+    ST_LAUNCH_MFMA(4, 1)
+    ST_LAUNCH_MFMA(2, 2)
+    ST_LAUNCH_MFMA(2, 4)
+    ST_LAUNCH_MFMA(1, 4)
+#undef ST_LAUNCH_MFMA
   } else {
     if (D == 128) hipLaunchKernelGGL((attn_valu_kernel<float, 128>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((attn_valu_kernel<float, 64>), grid, block, 0, s, a);

@@ -2,10 +2,11 @@
 // each node attends along its own root path through a constructed mask; the
 // parent pointer per node is from §2.1 of the SpecInfer developer article).
 //
-// One workgroup per request, one thread per node: the thread follows parent
-// pointers from its node to the root, setting one bit per node reached.  A
-// request holds at most 256 nodes, so a row is at most four 64-bit words and
-// the walk at most 255 steps; this is latency-bound work of a few microseconds.
+// One workgroup per request, one thread per node: the request's parent array
+// is staged in LDS, then each thread follows parent pointers from its node to
+// the root, setting one bit per node reached.  A request holds at most 256
+// nodes, so a row is at most four 64-bit words and the walk at most 255 steps;
+// this is latency-bound work of a few microseconds.
 #include "st_internal.h"
 
 namespace {
@@ -24,6 +25,7 @@ __global__ void __launch_bounds__(256)
 tree_mask_kernel(const int32_t* __restrict__ node_off, const int32_t* __restrict__ parent, int T,
                  int max_nodes, int W, uint64_t* __restrict__ mask, int32_t* __restrict__ depth,
                  int32_t* status) {
+  __shared__ int sp[ST_MAX_NODES];
   const int b = blockIdx.x;
   const int lo = node_off[b], hi = node_off[b + 1];
   const int n = hi - lo;
@@ -31,12 +33,14 @@ tree_mask_kernel(const int32_t* __restrict__ node_off, const int32_t* __restrict
     if (threadIdx.x == 0) st::set_status(status, ST_STATUS_BAD_PARENT);
     return;
   }
+  for (int i = threadIdx.x; i < n; i += blockDim.x) sp[i] = parent[lo + i];
+  __syncthreads();
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     uint64_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
     int j = i, d = 0, bad = 0;
     set_bit4(w0, w1, w2, w3, j);
     for (int steps = 0; steps < n; ++steps) {
-      const int p = parent[lo + j];
+      const int p = sp[j];
       if (j == 0) {
         bad = (p != -1);
         break;

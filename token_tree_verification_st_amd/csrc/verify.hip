@@ -1,9 +1,10 @@
 // Acceptance of a verified token tree.
 //
-// Greedy (SpecInfer developer article §2.1, longest verified prefix): one
-// workgroup per node computes the vocab-wide argmax of that node's target
-// logits (a wavefront reduction over coalesced loads), then one wavefront per
-// request walks down the tree.
+// Greedy (SpecInfer developer article §2.1, longest verified prefix): the
+// vocab-wide argmax of every node's target logits is reduced by workgroups
+// that each own an 8192-entry slice of one row (coalesced 16-byte loads, all
+// issued up front, then wavefront and workgroup reductions); one wavefront
+// per request then merges the slices and walks down the tree.
 //
 // Stochastic (speculative-decoding explainer §2.2: accept with probability
 // min(1, p/q), check left to right, resample from the residual at the first
@@ -70,31 +71,60 @@ __device__ inline void argmax_merge(float& v, int& i, float v2, int i2) {
 // ---------------------------------------------------------------- greedy
 
 constexpr int kArgmaxBlock = 256;
+constexpr int kArgmaxPerThread = 32;                          // logits per thread
+constexpr int kArgmaxSlice = kArgmaxBlock * kArgmaxPerThread;  // vocab entries per workgroup
 
+struct ArgmaxPart {
+  float v;
+  int i;
+};
+
+// Workgroup (t, slice) reduces logits[t][slice*8192 .. +8192) to its maximum
+// and lowest index; all of a thread's loads are issued before any is used.
 __global__ void __launch_bounds__(kArgmaxBlock)
-row_argmax_kernel(const float* __restrict__ logits, int V, int32_t* __restrict__ amax,
+row_argmax_kernel(const float* __restrict__ logits, int V, ArgmaxPart* __restrict__ part,
                   int32_t* status) {
-  const int t = blockIdx.x;
+  const int t = blockIdx.x, slice = blockIdx.y, nslices = gridDim.y;
   const float* row = logits + (size_t)t * V;
+  const int base = slice * kArgmaxSlice;
   float best = -INFINITY;
   int bidx = INT_MAX;
   bool finite = true;
   if ((V & 3) == 0) {
-    const f32x4* r4 = reinterpret_cast<const f32x4*>(row);
-    const int n4 = V >> 2;
-    for (int k = threadIdx.x; k < n4; k += kArgmaxBlock) {
-      const f32x4 x = __builtin_nontemporal_load(r4 + k);
-      finite = finite && isfinite(x.x) && isfinite(x.y) && isfinite(x.z) && isfinite(x.w);
-      argmax_merge(best, bidx, x.x, 4 * k);
-      argmax_merge(best, bidx, x.y, 4 * k + 1);
-      argmax_merge(best, bidx, x.z, 4 * k + 2);
-      argmax_merge(best, bidx, x.w, 4 * k + 3);
+    constexpr int N4 = kArgmaxPerThread / 4;
+    f32x4 x[N4];
+#pragma unroll
+    for (int k = 0; k < N4; ++k) {
+      const int v = base + 4 * (threadIdx.x + k * kArgmaxBlock);
+      x[k] = v < V ? __builtin_nontemporal_load((const f32x4*)(row + v))
+                   : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+#pragma unroll
+    for (int k = 0; k < N4; ++k) {
+      const int v = base + 4 * (threadIdx.x + k * kArgmaxBlock);
+      if (v < V) {
+        finite = finite && isfinite(x[k].x) && isfinite(x[k].y) && isfinite(x[k].z) &&
+                 isfinite(x[k].w);
+        argmax_merge(best, bidx, x[k].x, v);
+        argmax_merge(best, bidx, x[k].y, v + 1);
+        argmax_merge(best, bidx, x[k].z, v + 2);
+        argmax_merge(best, bidx, x[k].w, v + 3);
+      }
     }
   } else {
-    for (int k = threadIdx.x; k < V; k += kArgmaxBlock) {
-      const float x = row[k];
-      finite = finite && isfinite(x);
-      argmax_merge(best, bidx, x, k);
+    float x[kArgmaxPerThread];
+#pragma unroll
+    for (int k = 0; k < kArgmaxPerThread; ++k) {
+      const int v = base + threadIdx.x + k * kArgmaxBlock;
+      x[k] = v < V ? row[v] : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < kArgmaxPerThread; ++k) {
+      const int v = base + threadIdx.x + k * kArgmaxBlock;
+      if (v < V) {
+        finite = finite && isfinite(x[k]);
+        argmax_merge(best, bidx, x[k], v);
+      }
     }
   }
 #pragma unroll
@@ -117,7 +147,7 @@ row_argmax_kernel(const float* __restrict__ logits, int V, int32_t* __restrict__
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int k = 1; k < kArgmaxBlock / ST_WAVE; ++k) argmax_merge(best, bidx, sv[k], si[k]);
-    amax[t] = (bidx == INT_MAX) ? 0 : bidx;
+    part[(size_t)t * nslices + slice] = ArgmaxPart{best, bidx};
     if (!sf) st::set_status(status, ST_STATUS_NONFINITE);
   }
 }
@@ -154,32 +184,50 @@ __device__ inline void write_path_outputs(int b, int L, int max_depth, const int
 
 constexpr int kMaxPath = ST_MAX_NODES;
 
+// One wavefront per request: the request's parents, tokens and merged argmax
+// are staged in LDS, then the walk moves from node to node with the lowest
+// matching child found by a ballot over the wavefront.
 __global__ void __launch_bounds__(ST_WAVE)
 greedy_walk_kernel(const int32_t* __restrict__ node_off, const int32_t* __restrict__ parent,
-                   const int32_t* __restrict__ tokens, const int32_t* __restrict__ amax, int T,
-                   int V, int max_nodes, int max_depth, int32_t* accept_len,
-                   int32_t* accept_nodes, int32_t* out_tokens, int32_t* status) {
+                   const int32_t* __restrict__ tokens, const ArgmaxPart* __restrict__ part,
+                   int nslices, int T, int V, int max_nodes, int max_depth,
+                   int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                   int32_t* status) {
   __shared__ int path[kMaxPath + 1];
+  __shared__ int sp[ST_MAX_NODES], stok[ST_MAX_NODES], sa[ST_MAX_NODES];
   const int b = blockIdx.x, lane = threadIdx.x;
   const int lo = node_off[b], hi = node_off[b + 1], n = hi - lo;
   if (lo < 0 || hi > T || n < 1 || n > max_nodes) {
     if (lane == 0) st::set_status(status, ST_STATUS_BAD_PARENT);
     return;
   }
-  int bits = check_request(parent, tokens, lo, n, V);
+  int bits = 0;
+  for (int i = lane; i < n; i += ST_WAVE) {
+    const int p = parent[lo + i], tok = tokens[lo + i];
+    sp[i] = p;
+    stok[i] = tok;
+    if (i == 0 ? (p != -1) : (p < 0 || p >= i)) bits |= ST_STATUS_BAD_PARENT;
+    if (i > 0 && (tok < 0 || tok >= V)) bits |= ST_STATUS_BAD_TOKEN;
+    const ArgmaxPart* pp = part + (size_t)(lo + i) * nslices;
+    float bv = pp[0].v;
+    int bi = pp[0].i;
+    for (int k = 1; k < nslices; ++k) argmax_merge(bv, bi, pp[k].v, pp[k].i);
+    sa[i] = (bi == INT_MAX) ? 0 : bi;
+  }
   for (int o = 32; o > 0; o >>= 1) bits |= __shfl_xor(bits, o, ST_WAVE);
   if (lane == 0) st::set_status(status, bits);
+  __syncthreads();
 
   int u = 0, L = 0;
   bool overflow = false;
   if (lane == 0) path[0] = 0;
   while (true) {
-    const int a = amax[lo + u];
+    const int a = sa[u];
     int found = -1;
     // children of u have larger indices; the lowest matching index wins
     for (int c0 = u + 1; c0 < n && found < 0; c0 += ST_WAVE) {
       const int c = c0 + lane;
-      const bool hit = c < n && parent[lo + c] == u && tokens[lo + c] == a;
+      const bool hit = c < n && sp[c] == u && stok[c] == a;
       const uint64_t m = __ballot(hit);
       if (m) found = c0 + __ffsll((unsigned long long)m) - 1;
     }
@@ -194,7 +242,7 @@ greedy_walk_kernel(const int32_t* __restrict__ node_off, const int32_t* __restri
   }
   __syncthreads();
   if (overflow && lane == 0) st::set_status(status, ST_STATUS_PATH_OVERFLOW);
-  write_path_outputs(b, L, max_depth, path, tokens, lo, overflow ? -1 : amax[lo + u], accept_len,
+  write_path_outputs(b, L, max_depth, path, tokens, lo, overflow ? -1 : sa[u], accept_len,
                      accept_nodes, out_tokens);
 }
 
@@ -489,10 +537,11 @@ stoch_walk_kernel(const int32_t* __restrict__ node_off, const int32_t* __restric
 
 // ---------------------------------------------------------------- entry points
 
+static int argmax_slices(int V) { return (V + kArgmaxSlice - 1) / kArgmaxSlice; }
+
 extern "C" size_t st_verify_greedy_workspace(const st_tree* tree, int V) {
-  (void)V;
-  if (st::check_tree_host(tree)) return 0;
-  return st::align_up((size_t)tree->total_nodes * sizeof(int32_t), 256);
+  if (st::check_tree_host(tree) || V < 1) return 0;
+  return st::align_up((size_t)tree->total_nodes * argmax_slices(V) * sizeof(ArgmaxPart), 256);
 }
 
 extern "C" int st_verify_greedy(const st_tree* tree, int V, const int32_t* tokens,
@@ -505,13 +554,14 @@ extern "C" int st_verify_greedy(const st_tree* tree, int V, const int32_t* token
     return ST_E_INVALID;
   if (tree->max_depth + 1 > kMaxPath) return ST_E_UNSUPPORTED;
   if (ws_bytes < st_verify_greedy_workspace(tree, V)) return ST_E_WORKSPACE;
-  int32_t* amax = (int32_t*)workspace;
+  ArgmaxPart* part = (ArgmaxPart*)workspace;
+  const int ns = argmax_slices(V);
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(row_argmax_kernel, dim3(tree->total_nodes), dim3(kArgmaxBlock), 0, s,
-                     logits, V, amax, status);
+  hipLaunchKernelGGL(row_argmax_kernel, dim3(tree->total_nodes, ns), dim3(kArgmaxBlock), 0, s,
+                     logits, V, part, status);
   if ((rc = st::check_launch())) return rc;
   hipLaunchKernelGGL(greedy_walk_kernel, dim3(tree->B), dim3(ST_WAVE), 0, s, tree->node_off,
-                     tree->parent, tokens, amax, tree->total_nodes, V, tree->max_nodes,
+                     tree->parent, tokens, part, ns, tree->total_nodes, V, tree->max_nodes,
                      tree->max_depth, accept_len, accept_nodes, out_tokens, status);
   return st::check_launch();
 }
