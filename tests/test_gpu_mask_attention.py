@@ -103,6 +103,38 @@ def test_attention_forced_splits_and_combine(split_keys, monkeypatch):
         assert err <= tol and lerr <= (F32_TOL if dtype == "f32" else 1e-3)
 
 
+# bf16 kernel variants by plan shape: (64-row groups per workgroup, 16-row
+# blocks per wavefront) = (1,1) (1,2) (1,4) (2,4) (4,4) for shapes 0..4
+@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4])
+def test_attention_every_kernel_shape(shape, monkeypatch):
+    monkeypatch.setenv("ST_ATTN_SHAPE", str(shape))
+    for i, (D, Hq, Hkv, nmax) in enumerate([(128, 4, 4, 90), (64, 6, 3, 40), (128, 16, 2, 25)]):
+        wl = _small_case(70 + i, D=D, Hq=Hq, Hkv=Hkv, nmax=nmax)
+        err, lerr = attention_errors(wl, to_device(wl))
+        say(f"shape {shape} D {D} Hq {Hq} Hkv {Hkv}: max-abs {err:.2e} lse {lerr:.2e}")
+        assert err <= BF16_TOL and lerr <= 1e-3
+    # forced short splits: some key groups get no chunk, tails are partial chunks
+    monkeypatch.setenv("ST_ATTN_SPLIT_KEYS", "80")
+    wl = _small_case(79, D=128, Hq=8, Hkv=2, nmax=70)
+    err, lerr = attention_errors(wl, to_device(wl))
+    say(f"shape {shape} split 80: max-abs {err:.2e} lse {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= 1e-3
+
+
+def test_attention_workspace_reused_across_calls(monkeypatch):
+    """One workspace serves calls with different trees and split counts."""
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    for i, sk in enumerate(["96", "64", "200", "96"]):
+        monkeypatch.setenv("ST_ATTN_SPLIT_KEYS", sk)
+        wl = _small_case(90 + i, D=128, Hq=4, Hkv=2, nmax=60)
+        dw = to_device(wl)
+        dw.buf["attn_ws"] = ws
+        for _ in range(2):
+            err, lerr = attention_errors(wl, dw)
+            assert err <= BF16_TOL and lerr <= 1e-3
+        assert status_of(dw) == 0
+
+
 def test_attention_peaked_softmax_exercises_rescaling():
     wl = _small_case(21, q_sigma=8.0, pmax=1500)
     err, lerr = attention_errors(wl, to_device(wl))

@@ -29,6 +29,13 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# Per-file device flags.  The streaming attention kernel keeps 128 fp32
+# accumulators per lane; letting the register allocator place MFMA results in
+# ordinary VGPRs (spilling the remainder to AGPRs) avoids copying the
+# accumulators between the two files on every loop iteration.
+PER_FILE = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
 
 
 def hipcc() -> str:
@@ -40,7 +47,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -7,22 +7,22 @@
 // are the N_b tree nodes times the G = Hq/Hkv query heads sharing g; every one
 // of them reads the same keys, so a workgroup takes a block of rows and a
 // contiguous range of keys ("split") and streams that range once.  Splits
-// produce fp32 partials (running max m, sum l, unnormalised output) that a
-// combine kernel merges with a log-sum-exp rescale; a request whose keys fit in
-// one split writes its output directly.
+// produce fp32 partials (running max m, sum l, unnormalised output); a request
+// whose keys fit in one split writes its output directly.
 //
-// bf16 path (MFMA, gfx950).  One workgroup = 4 wavefronts = 64 query rows, 16
-// per wavefront.  Each 64-key tile of K is copied to LDS with padded rows; the
-// V tile is transposed on its way into LDS.  Per wavefront and tile:
-//   S^T (keys x rows) = K . Q^T    with v_mfma_f32_16x16x32_bf16, A = K from
-//                                  LDS, B = Q^T held in registers
+// bf16 path (MFMA, gfx950), the streaming kernel.  A wavefront owns up to 64
+// query rows with Q^T held in registers and walks 32-key chunks of K and V,
+// copied to LDS by direct global-to-LDS loads.  Per chunk:
+//   S^T (keys x rows) = K . Q^T    v_mfma_f32_16x16x32_bf16, A = K from LDS
 //   online softmax on S^T          each lane holds 4 keys of one row, so the
-//                                  row statistics live in that lane and need
-//                                  only two cross-lane steps per tile
-//   O^T (dims x rows) += V^T . P^T A = V^T from LDS, B = P^T straight from
-//                                  the S^T accumulators converted to bf16
+//                                  row statistics stay in that lane and need
+//                                  two permlane swaps per chunk
+//   O^T (dims x rows) += V^T . P^T A = V^T from LDS by transposing reads,
+//                                  B = P^T straight from the S^T accumulators
 // Keys beyond the prefix are tree keys: key P_b + j is visible to a row iff
-// bit j of its node's ancestor mask is set.
+// bit j of its node's ancestor mask is set.  A combine kernel merges the
+// splits of every row (spread over the whole chip: one workgroup merging all
+// splits of a row block would pull them through a single CU).
 //
 // fp32 path (VALU).  The same decomposition with 16 rows per workgroup and
 // plain fp32 dot products; it serves fp32 inputs, which need 1e-5 accuracy.
@@ -41,13 +41,6 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kKT = 64;  // keys per tile
-// MFMA workgroup shapes (row-waves of 16 rows x key groups); the plan picks one
-struct Shape {
-  int rw, kw;
-};
-constexpr Shape kShapes[] = {{4, 1}, {4, 2}, {2, 2}, {2, 4}, {1, 4}};
-
 struct AttnArgs {
   const int32_t* node_off;
   const int32_t* prefix_len;
@@ -114,7 +107,7 @@ __device__ inline bool tree_bit(uint64_t w0, uint64_t w1, uint64_t w2, uint64_t 
   return (w >> (j & 63)) & 1ull;
 }
 
-// ---------------------------------------------------------------- bf16 MFMA
+// ---------------------------------------------------------------- bf16 MFMA, shared pieces
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -138,162 +131,239 @@ __device__ __forceinline__ int vswz(int key) {
   return (((key & 3) << 1) | (((key >> 2) & 1) << 3)) & (D / 8 - 1);
 }
 
-// What one thread of a key group (GS threads) moves from global memory to LDS
-// for one 64-key tile: N 16-byte chunks of K rows and N of V rows.
-template <int D, int GS>
-struct TileRegs {
-  static constexpr int CH = D / 8;
-  static constexpr int TOT = kKT * CH;
-  static constexpr int N = (TOT + GS - 1) / GS;
-  u32x4 k[N];
-  u32x4 v[N];
-};
 
-// Every load is issued unconditionally (the compiler can then count them and
-// keep the next round in flight): key indices are clamped into [k0, k1 - 1],
-// so rows past the end of the range hold copies of valid rows, which the
-// score mask excludes and which meet a zero probability in P V.
-template <int D, int GS>
-__device__ __forceinline__ void tile_load(TileRegs<D, GS>& r, const uint16_t* kg, const uint16_t* vg,
-                                          int kt, int klast, int gt) {
-  using TR = TileRegs<D, GS>;
-#pragma unroll
-  for (int i = 0; i < TR::N; ++i) {
-    const int e = min(gt + i * GS, TR::TOT - 1), row = e / TR::CH, c = e % TR::CH;
-    const size_t off = (size_t)min(kt + row, klast) * D + 8 * c;
-    r.k[i] = *(const u32x4*)(kg + off);
-    r.v[i] = *(const u32x4*)(vg + off);
-  }
-}
+#define ST_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int D, int GS>
-__device__ __forceinline__ void tile_store(const TileRegs<D, GS>& r, uint16_t* sK, uint16_t* sV,
-                                           int gt) {
-  using TR = TileRegs<D, GS>;
-  constexpr int DP = D + 8;
-#pragma unroll
-  for (int i = 0; i < TR::N; ++i) {
-    const int e = gt + i * GS, row = e / TR::CH, c = e % TR::CH;
-    if (TR::N * GS == TR::TOT || e < TR::TOT) {
-      *(u32x4*)(&sK[row * DP + 8 * c]) = r.k[i];
-      *(u32x4*)(&sV[row * D + 8 * (c ^ vswz<D>(row))]) = r.v[i];
-    }
-  }
-}
-
-struct TileCtx {
-  int P, k1, r16, grp;
-  float scale_log2;
-  uint64_t mw0, mw1, mw2, mw3;
-};
-
-// One wavefront's work on one 64-key tile in LDS: S^T = K Q^T, mask, online
-// softmax update of (m, lsum, acc), O^T += V^T P^T.
+// K rows are stored unpadded (D*2 bytes) with 16-byte chunk c at position
+// c ^ kswz(row): the 16 lanes that read one chunk of 16 consecutive keys hit
+// 16 distinct bank groups.
 template <int D>
-__device__ __forceinline__ void tile_compute(const TileCtx& cx, const uint16_t* sK,
-                                             const uint16_t* sV, int kt,
-                                             const bf16x8 (&qf)[D / 32], f32x4 (&acc)[D / 16],
-                                             float& m, float& lsum) {
-  constexpr int DP = D + 8, NKS = D / 32, NDB = D / 16;
-  const int r16 = cx.r16, grp = cx.grp;
-
-    // S^T = K Q^T over four 16-key blocks; lane holds keys kt+16kb+4grp+j
-    f32x4 s[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const uint4 u = *(const uint4*)(&sK[(16 * kb + r16) * DP + 32 * ks + 8 * grp]);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), qf[ks],
-                                                        s[kb], 0, 0, 0);
-      }
-    }
-    const bool edge = kt + kKT > cx.P || kt + kKT > cx.k1;
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x = s[kb][j] * cx.scale_log2;
-        if (edge) {
-          const int key = kt + 16 * kb + 4 * grp + j;
-          bool vis = key < cx.k1;
-          if (key >= cx.P) vis = vis && tree_bit(cx.mw0, cx.mw1, cx.mw2, cx.mw3, key - cx.P);
-          x = vis ? x : -INFINITY;
-        }
-        s[kb][j] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, ST_WAVE));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, ST_WAVE));
-    const float m_new = fmaxf(m, tmax);
-    const float mref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - mref);
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = fast_exp2(s[kb][j] - mref);
-        s[kb][j] = p;
-        psum += p;
-      }
-    }
-    lsum = lsum * alpha + psum;
-    m = m_new;
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
-
-    bf16x8 pb[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pb[t][j] = (__bf16)s[2 * t][j];
-        pb[t][4 + j] = (__bf16)s[2 * t + 1][j];
-      }
-    }
-    // O^T += V^T P^T.  Transposed reads: lane k = 4j + q of each 16-lane
-    // group points at V[key_j][16db + 4q .. +3]; lane i then receives dim
-    // 16db + i of key_0..key_3 (keys 32t + 4grp + j, and + 16 for slots 4-7).
-    const int jq = r16 >> 2, qq = r16 & 3;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int key1 = 32 * t + 4 * grp + jq, key2 = key1 + 16;
-        const int c = 2 * db + (qq >> 1), sub = 4 * (qq & 1);
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(sV + key1 * D + 8 * (c ^ vswz<D>(key1)) + sub));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(sV + key2 * D + 8 * (c ^ vswz<D>(key2)) + sub));
-        const v8i16 u = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), pb[t],
-                                                         acc[db], 0, 0, 0);
-      }
-    }
+__device__ __forceinline__ int kswz(int key) {
+  return D >= 128 ? (key & (D / 8 - 1)) : ((key >> 1) & (D / 8 - 1));
 }
 
-// One workgroup = RW row-waves x KW key groups.  Row-wave rw owns 16 query
-// rows; key group kg takes every KW-th 64-key tile of the workgroup's key
-// range, with its own LDS buffers and its own running softmax state.  The
-// tiles of the next round are loaded into registers while the current round
-// is computed.  At the end the key groups' states are merged through LDS.
-template <int D, int RW, int KW>
-__global__ void __launch_bounds__(64 * RW * KW)
-attn_mfma_kernel(AttnArgs a) {
-  constexpr int GS = 64 * RW;      // threads per key group
-  constexpr int ROWS = 16 * RW;    // query rows per workgroup
-  constexpr int DP = D + 8;        // K row pitch (bf16): 16-byte pad
-  constexpr int NKS = D / 32;      // k-steps of S^T
-  constexpr int NDB = D / 16;      // d-blocks of O^T
-  constexpr int KEL = kKT * DP, VEL = kKT * D;
-  constexpr int MERGE_FLOATS = (KW - 1) * RW * 64 * (4 * NDB + 2);
-  constexpr int TILE_BYTES = KW * (KEL + VEL) * 2;
-  constexpr int LDS_BYTES = TILE_BYTES > MERGE_FLOATS * 4 ? TILE_BYTES : MERGE_FLOATS * 4;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_BYTES / 2];
+// vmcnt(n) with the other counters left alone (gfx9 encoding).
+#define ST_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+
+// ---------------------------------------------------------------- bf16 MFMA, 64 rows per wavefront
+
+// Each wavefront owns 64 query rows (four 16-row blocks, Q held in registers)
+// and walks its keys in 32-key chunks, one k-step of the P V product.  A chunk
+// of K and V is copied to LDS with direct global-to-LDS loads and read from
+// there once per wavefront: K as the MFMA A operand, V through the transposing
+// read.  Every K and V fragment read from LDS serves all four row blocks.
+//
+// A workgroup is RWV row groups (64 rows each) x KWV = 4 / RWV key groups.  Key
+// group kg takes chunks kg, kg + KWV, ... of the workgroup's key range through
+// its own NSTAGE-deep ring.  With RWV = 1 every wavefront has a ring of its
+// own and never waits for another one; with RWV > 1 the row groups share the
+// ring of their key group, split its loads and meet at one barrier per chunk.
+// Key groups merge their softmax states through LDS at the end.
+//
+// The running max is moved only when a row's new scores exceed it by more
+// than kLazy (log2 units), so most chunks skip the rescale of the 128
+// accumulators; probabilities are then at most 2^kLazy before normalisation,
+// and the final division uses the same reference, so the result is unchanged.
+constexpr int kCK = 32;
+constexpr float kLazy = 8.f;
+
+// Cross-lane reductions over the lane groups l, l^16, l^32, l^48, which hold
+// the same query row: gfx950 permlane swaps exchange 16-lane rows in VALU.
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_add(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wait until at most n chunks (DPC loads each) of this wavefront are in flight.
+template <int N, int DPC>
+__device__ __forceinline__ void wait_chunks(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      ST_WAIT_VMCNT(N * DPC);
+      return;
+    }
+    wait_chunks<N - 1, DPC>(n);
+  } else {
+    ST_WAIT_VMCNT(0);
+  }
+}
+
+// This wavefront's share (row group rw of RWV) of the direct loads of one
+// 32-key chunk starting at key kt; key rows past klast are clamped to it.  The
+// chunk base is wave-uniform, each lane adds a 32-bit offset.
+template <int D, int RWV>
+__device__ __forceinline__ void chunk_dma(uint16_t* sK, uint16_t* sV, const uint16_t* kg,
+                                          const uint16_t* vg, int kt, int klast, int rw,
+                                          int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass never runs this body
+  constexpr int CH = D / 8, RPI = 64 / CH, INST = kCK / RPI, PER = INST / RWV;
+  const uint16_t* kb = kg + (size_t)kt * D;
+  const uint16_t* vb = vg + (size_t)kt * D;
+  const int lim = klast - kt;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int inst = rw * PER + i;
+    const int row = inst * RPI + lane / CH, pos = lane % CH;
+    const uint32_t ro = (uint32_t)min(row, lim) * D;
+    __builtin_amdgcn_global_load_lds(kb + (ro + 8 * (pos ^ kswz<D>(row))),
+                                     ST_LDS_PTR(sK + inst * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + (ro + 8 * (pos ^ vswz<D>(row))),
+                                     ST_LDS_PTR(sV + inst * 512), 16, 0, 0);
+  }
+#endif
+}
+
+// One wavefront's work on one 32-key chunk for its RBW row blocks.
+template <int D, int RBW>
+__device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t* sV,
+                                              const uint64_t* sM, int kt, int P, int k1,
+                                              float c, int r16, int grp,
+                                              const bf16x8 (&qf)[RBW][D / 32],
+                                              f32x4 (&acc)[RBW][D / 16], float (&m)[RBW],
+                                              float (&l)[RBW]) {
+  constexpr int NKS = D / 32, NDB = D / 16;
+  u32x4 kf[2][NKS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = 16 * kb + r16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kf[kb][ks] = *(const u32x4*)(sK + key * D + 8 * ((4 * ks + grp) ^ kswz<D>(key)));
+  }
+  f32x4 s[RBW][2];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, kf[kb][ks]), qf[rb][ks], s[rb][kb], 0, 0, 0);
+    }
+  if (kt + kCK > P || kt + kCK > k1) {  // the chunk reaches tree keys or the range end
+    // bit o of win: key kt + o is visible to this lane's row; the shift
+    // amounts are the same for the whole wavefront
+    const int t0 = kt - P, nv = k1 - kt;
+    const uint32_t in_range = nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      const uint64_t* mr = sM + (rb * 16 + r16) * 4;
+      uint32_t win;
+      if (t0 >= 0) {
+        const int wi = t0 >> 6, sh = t0 & 63;
+        const uint64_t lo = mr[wi], hi = wi < 3 ? mr[wi + 1] : 0ull;
+        win = (uint32_t)((lo >> sh) | (sh ? hi << (64 - sh) : 0ull));
+      } else {
+        const int np = -t0;  // prefix keys at the start of the chunk
+        win = np >= 32 ? 0xFFFFFFFFu : (uint32_t)(mr[0] << np) | ((1u << np) - 1u);
+      }
+      win &= in_range;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          s[rb][kb][j] = (win >> (16 * kb + 4 * grp + j)) & 1u ? s[rb][kb][j] : -INFINITY;
+    }
+  }
+  bf16x8 pb[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    float t = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
+                    fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
+    t = xor16_max(t);
+    t = xor32_max(t);
+    const float mc = t * c;  // c > 0: the max of the scaled scores
+    const bool need = mc > m[rb] + kLazy;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m[rb] - mc) : 1.f;
+      m[rb] = need ? mc : m[rb];
+      l[rb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[rb][db] *= alpha;
+    }
+    const float nm = m[rb] == -INFINITY ? 0.f : -m[rb];
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = fast_exp2(fmaf(s[rb][kb][j], c, nm));
+        pb[rb][4 * kb + j] = (__bf16)p;
+        ps += p;
+      }
+    l[rb] += ps;
+  }
+  const int jq = r16 >> 2, qq = r16 & 3;
+  const int key1 = 4 * grp + jq, key2 = key1 + 16;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int ch = 2 * db + (qq >> 1), sub = 4 * (qq & 1);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(sV + key1 * D + 8 * (ch ^ vswz<D>(key1)) + sub));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(sV + key2 * D + 8 * (ch ^ vswz<D>(key2)) + sub));
+    const bf16x8 vf =
+        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb)
+      acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb], acc[rb][db], 0, 0, 0);
+  }
+}
+
+// Normalise and store one row's output (16 dims per MFMA block, 4 per lane
+// group) and its log-sum-exp.
+template <int D>
+__device__ __forceinline__ void write_row_out(const AttnArgs& a, int grow, int grp, float m,
+                                              float l, const f32x4 (&acc)[D / 16]) {
+  const float inv = 1.f / l;
+  uint16_t* op = (uint16_t*)a.out + (size_t)grow * D;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    uint2 o;
+    o.x = (uint32_t)st::f32_to_bf16_rne(acc[db][0] * inv) |
+          ((uint32_t)st::f32_to_bf16_rne(acc[db][1] * inv) << 16);
+    o.y = (uint32_t)st::f32_to_bf16_rne(acc[db][2] * inv) |
+          ((uint32_t)st::f32_to_bf16_rne(acc[db][3] * inv) << 16);
+    *(uint2*)(op + 16 * db + 4 * grp) = o;
+  }
+  if (a.lse && grp == 0) a.lse[grow] = (m + log2f(l)) * kLn2;
+}
+
+// RWV row groups of RBW 16-row blocks; KWV = 4 / RWV key groups.
+template <int D, int NSTAGE, int RWV, int RBW>
+__global__ void __launch_bounds__(256, 1)
+attn_stream_kernel(AttnArgs a) {
+  constexpr int KWV = 4 / RWV;
+  constexpr int NKS = D / 32, NDB = D / 16, CH = D / 8;
+  constexpr int WROWS = 16 * RBW, ROWS = WROWS * RWV;
+  constexpr int STAGE = 2 * kCK * D;                  // bf16 elements: K then V
+  constexpr int DPC = 2 * (kCK * CH / 64) / RWV;      // direct loads per chunk and wavefront
+  constexpr int RING_BYTES = KWV * NSTAGE * STAGE * 2;
+  constexpr int SLOT = (NDB * 4 + 2) * 64;            // floats: one row block of one wave
+  constexpr int MERGE_BYTES = KWV > 1 ? RWV * RBW * KWV * SLOT * 4 : 0;
+  constexpr int BODY = RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES;
+  constexpr int MWORDS = ROWS * 4;
+  constexpr int MPT = (MWORDS + 255) / 256;           // mask words per thread
+  static_assert(DPC * (NSTAGE - 1) <= 63, "in-flight loads exceed the vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[BODY + MWORDS * 8];
+  uint64_t* sMask = (uint64_t*)(lds + BODY);
 
   Item it;
   if (!decode_item(a, it)) return;
@@ -304,141 +374,156 @@ attn_mfma_kernel(AttnArgs a) {
     return;
   }
   const int rows_b = rq.n * a.G;
-  if (it.rblk * ROWS >= rows_b) return;
+  const int row0 = it.rblk * ROWS;
+  if (row0 >= rows_b) return;
   const int k0 = it.split * a.KS;
   if (k0 >= rq.key_end) return;
   const int k1 = min(k0 + a.KS, rq.key_end);
+  const int klast = k1 - 1;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int rw = wave % RW, kg = wave / RW, gt = tid % GS;
+  // the wavefront index is uniform: keep it (and all that derives from it) scalar
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = wave % RWV, kg = wave / RWV;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int row = it.rblk * ROWS + rw * 16 + r16;
-  const bool row_ok = row < rows_b;
-  const int node = row_ok ? row / a.G : 0;
-  const int hq = it.g * a.G + (row_ok ? row % a.G : 0);
-  const int grow = (rq.lo + node) * a.Hq + hq;
-  uint16_t* sK = lds + kg * (KEL + VEL);
-  uint16_t* sV = sK + KEL;
-
-  const uint16_t* qp = (const uint16_t*)a.q + (size_t)grow * D;
-  bf16x8 qf[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    uint4 u = row_ok ? *(const uint4*)(qp + 32 * s + 8 * grp) : make_uint4(0, 0, 0, 0);
-    qf[s] = __builtin_bit_cast(bf16x8, u);
-  }
-  uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
-  if (row_ok) {
-    const uint64_t* mr = a.mask + (size_t)(rq.lo + node) * a.W;
-    mw0 = mr[0];
-    if (a.W > 1) mw1 = mr[1];
-    if (a.W > 2) mw2 = mr[2];
-    if (a.W > 3) mw3 = mr[3];
-  }
+  const int wrow0 = row0 + rw * WROWS;
   const size_t head_off = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
   const uint16_t* kgp = (const uint16_t*)a.k + head_off;
   const uint16_t* vgp = (const uint16_t*)a.v + head_off;
+  const int nch = (k1 - k0 + kCK - 1) / kCK;
+  const int nmine = (nch - kg + KWV - 1) / KWV;  // chunks kg, kg + KWV, ...
+  const int niter = (nch + KWV - 1) / KWV;       // the same for every wavefront
+  uint16_t* ring = (uint16_t*)lds + kg * NSTAGE * STAGE;
 
-  f32x4 acc[NDB];
+  // Ancestor-mask words of the workgroup's rows (clamped, unconditional loads)
+  uint64_t mword[MPT];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
+  for (int i = 0; i < MPT; ++i) {
+    const int idx = min(tid + 256 * i, MWORDS - 1), row = row0 + idx / 4, w = idx % 4;
+    const int node = min(row, rows_b - 1) / a.G;
+    mword[i] = a.mask[(size_t)(rq.lo + node) * a.W + min(w, a.W - 1)];
+    mword[i] = (row < rows_b && w < a.W) ? mword[i] : 0ull;
+  }
+  // Q^T fragments of this wavefront's rows (rows past the end repeat the last)
+  bf16x8 qf[RBW][NKS];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    const int row = min(wrow0 + rb * 16 + r16, rows_b - 1);
+    const int node = row / a.G, hq = it.g * a.G + row % a.G;
+    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(rq.lo + node) * a.Hq + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[rb][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * ks + 8 * grp));
+  }
+  // prime the ring
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < nmine)
+      chunk_dma<D, RWV>(ring + s * STAGE, ring + s * STAGE + kCK * D, kgp, vgp,
+                        k0 + (s * KWV + kg) * kCK, klast, rw, lane);
+  wait_chunks<NSTAGE - 1, DPC>(min(NSTAGE - 1, nmine));  // the q and mask loads are older
+#pragma unroll
+  for (int i = 0; i < MPT; ++i)
+    if (tid + 256 * i < MWORDS) sMask[tid + 256 * i] = mword[i];
+  lds_barrier();
 
-  const int niters = (k1 - k0 + KW * kKT - 1) / (KW * kKT);
-  // Software pipeline two rounds deep: the tiles of round r+2 load into the
-  // register set that round r has just stored to LDS, so two rounds of loads
-  // are in flight while round r is computed.
-  auto tile_at = [&](int r) { return k0 + (r * KW + kg) * kKT; };
-  const TileCtx cx{rq.P, k1, r16, grp, a.scale_log2, mw0, mw1, mw2, mw3};
-  TileRegs<D, GS> ra, rb;
-  const int klast = k1 - 1;
-  // keep the two rounds' loads in program order (the wait before each store
-  // counts on it)
-  tile_load<D, GS>(ra, kgp, vgp, tile_at(0), klast, gt);
-  __builtin_amdgcn_sched_barrier(0);
-  tile_load<D, GS>(rb, kgp, vgp, tile_at(1), klast, gt);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int iter = 0; iter < niters; iter += 2) {
-    {
-      const int kt = tile_at(iter), nk = min(kKT, k1 - kt);
-      lds_barrier();
-      tile_store<D, GS>(ra, sK, sV, gt);
-      lds_barrier();
-      // unconditional (past the end it re-reads the clamped last row), so the
-      // compiler can wait for exactly the older round at the next store
-      __builtin_amdgcn_sched_barrier(0);
-      tile_load<D, GS>(ra, kgp, vgp, tile_at(iter + 2), klast, gt);
-      __builtin_amdgcn_sched_barrier(0);
-      if (nk > 0) tile_compute<D>(cx, sK, sV, kt, qf, acc, m, lsum);
+  f32x4 acc[RBW][NDB];
+  float m[RBW], l[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const uint64_t* sMw = sMask + rw * WROWS * 4;
+  int stage = 0, refill = NSTAGE - 1;
+  for (int r = 0; r < niter; ++r) {
+    // chunk r is the oldest outstanding; up to NSTAGE - 2 newer ones stay in flight
+    wait_chunks<NSTAGE - 2, DPC>(min(NSTAGE - 2, nmine - r - 1));
+    if constexpr (RWV > 1) lds_barrier();  // every row group is done with chunk r - 1
+    __builtin_amdgcn_sched_barrier(0);
+    if (r + NSTAGE - 1 < nmine) {
+      uint16_t* sb = ring + refill * STAGE;
+      chunk_dma<D, RWV>(sb, sb + kCK * D, kgp, vgp, k0 + ((r + NSTAGE - 1) * KWV + kg) * kCK,
+                        klast, rw, lane);
     }
-    {  // runs even past the last round (its compute is then skipped): no early
-       // exit, so the wait counts stay exact
-      const int kt = tile_at(iter + 1), nk = min(kKT, k1 - kt);
-      lds_barrier();
-      tile_store<D, GS>(rb, sK, sV, gt);
-      lds_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      tile_load<D, GS>(rb, kgp, vgp, tile_at(iter + 3), klast, gt);
-      __builtin_amdgcn_sched_barrier(0);
-      if (nk > 0) tile_compute<D>(cx, sK, sV, kt, qf, acc, m, lsum);
+    __builtin_amdgcn_sched_barrier(0);
+    if (r < nmine) {
+      const uint16_t* sK = ring + stage * STAGE;
+      chunk_compute<D, RBW>(sK, sK + kCK * D, sMw, k0 + (r * KWV + kg) * kCK, rq.P, k1,
+                            a.scale_log2, r16, grp, qf, acc, m, l);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    stage = stage + 1 == NSTAGE ? 0 : stage + 1;
+    refill = refill + 1 == NSTAGE ? 0 : refill + 1;
+  }
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    l[rb] = xor16_add(l[rb]);
+    l[rb] = xor32_add(l[rb]);
   }
 
-  lsum += __shfl_xor(lsum, 16, ST_WAVE);
-  lsum += __shfl_xor(lsum, 32, ST_WAVE);
-  if constexpr (KW > 1) {
-    // merge the key groups' states into group 0 (struct of arrays, lane-major)
+  // row block rb of a row group is finalised by key group owner(rb)
+  auto owner = [](int rb) { return RBW >= KWV ? rb * KWV / RBW : rb; };
+  if constexpr (KWV > 1) {
     float* mb = (float*)lds;
-    constexpr int SLOTS = (KW - 1) * RW * 64;
-    __syncthreads();
-    if (kg > 0) {
-      const int sl = ((kg - 1) * RW + rw) * 64 + lane;
-      mb[sl] = m;
-      mb[SLOTS + sl] = lsum;
+    lds_barrier();  // every ring is idle
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int rb = 0; rb < RBW; ++rb) {
+      if (owner(rb) != kg) {
+        float* sl = mb + ((rw * RBW + rb) * KWV + kg) * SLOT;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mb[(2 + 4 * db + j) * SLOTS + sl] = acc[db][j];
+        for (int db = 0; db < NDB; ++db) *(f32x4*)(sl + (db * 64 + lane) * 4) = acc[rb][db];
+        sl[NDB * 256 + lane] = m[rb];
+        sl[NDB * 256 + 64 + lane] = l[rb];
+      }
     }
-    __syncthreads();
-    if (kg > 0) return;
+    lds_barrier();
 #pragma unroll
-    for (int k = 1; k < KW; ++k) {
-      const int sl = ((k - 1) * RW + rw) * 64 + lane;
-      const float mk = mb[sl], lk = mb[SLOTS + sl];
-      const float M = fmaxf(m, mk);
-      const float ref = M == -INFINITY ? 0.f : M;
-      const float e0 = fast_exp2(m - ref), e1 = fast_exp2(mk - ref);
-      lsum = lsum * e0 + lk * e1;
+    for (int rb = 0; rb < RBW; ++rb) {
+      if (owner(rb) == kg) {
+        float M = m[rb];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int k = 0; k < KWV; ++k)
+          if (k != kg) M = fmaxf(M, mb[((rw * RBW + rb) * KWV + k) * SLOT + NDB * 256 + lane]);
+        const float ref = M == -INFINITY ? 0.f : M;
+        const float w0 = fast_exp2(m[rb] - ref);
+        l[rb] *= w0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[db][j] = acc[db][j] * e0 + mb[(2 + 4 * db + j) * SLOTS + sl] * e1;
-      m = M;
+        for (int db = 0; db < NDB; ++db) acc[rb][db] *= w0;
+#pragma unroll
+        for (int k = 0; k < KWV; ++k) {
+          if (k != kg) {
+            const float* sl = mb + ((rw * RBW + rb) * KWV + k) * SLOT;
+            const float wk = fast_exp2(sl[NDB * 256 + lane] - ref);
+            l[rb] += wk * sl[NDB * 256 + 64 + lane];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+              acc[rb][db] += wk * *(const f32x4*)(sl + (db * 64 + lane) * 4);
+          }
+        }
+        m[rb] = M;
+      }
     }
   }
-  if (!row_ok) return;
-  if (rq.nsplit == 1) {
-    const float inv = 1.f / lsum;
-    uint16_t* op = (uint16_t*)a.out + (size_t)grow * D;
+
+  const size_t TH = (size_t)a.T * a.Hq;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      uint2 o;
-      o.x = (uint32_t)st::f32_to_bf16_rne(acc[db][0] * inv) |
-            ((uint32_t)st::f32_to_bf16_rne(acc[db][1] * inv) << 16);
-      o.y = (uint32_t)st::f32_to_bf16_rne(acc[db][2] * inv) |
-            ((uint32_t)st::f32_to_bf16_rne(acc[db][3] * inv) << 16);
-      *(uint2*)(op + 16 * db + 4 * grp) = o;
+  for (int rb = 0; rb < RBW; ++rb) {
+    if (owner(rb) != kg) continue;
+    const int row = wrow0 + rb * 16 + r16;
+    if (row >= rows_b) continue;
+    const int grow = (rq.lo + row / a.G) * a.Hq + it.g * a.G + row % a.G;
+    if (rq.nsplit == 1) {
+      write_row_out<D>(a, grow, grp, m[rb], l[rb], acc[rb]);
+    } else {
+      const size_t pr = (size_t)it.split * TH + grow;
+      float* wp = a.ws_acc + pr * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) *(f32x4*)(wp + 16 * db + 4 * grp) = acc[rb][db];
+      if (grp == 0) a.ws_ml[pr] = make_float2(m[rb], l[rb]);
     }
-    if (a.lse && grp == 0) a.lse[grow] = (m + log2f(lsum)) * kLn2;
-  } else {
-    const size_t TH = (size_t)a.T * a.Hq;
-    const size_t pr = (size_t)it.split * TH + grow;
-    float* wp = a.ws_acc + pr * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) *(f32x4*)(wp + 16 * db + 4 * grp) = acc[db];
-    if (grp == 0) a.ws_ml[pr] = make_float2(m, lsum);
   }
 }
 
@@ -644,8 +729,8 @@ attn_combine_kernel(AttnArgs a) {
 // ---------------------------------------------------------------- planning
 
 struct Plan {
-  bool mfma;
-  int shape;
+  bool stream;  // bf16 streaming MFMA kernel (else fp32 VALU kernel + combine)
+  int rwv, rbw; // streaming kernel: 64-row groups per workgroup, 16-row blocks per wave
   int RB, n_rblk, KS, NS, items, per_xcd;
   size_t ml_bytes, ws_bytes;
 };
@@ -663,23 +748,39 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
   if (dtype != ST_F32 && dtype != ST_BF16) return ST_E_INVALID;
   if (Hq % Hkv || (D != 64 && D != 128)) return ST_E_UNSUPPORTED;
   const int G = Hq / Hkv;
-  p.mfma = dtype == ST_BF16;
-  p.shape = env_int("ST_ATTN_SHAPE", 0);
-  if (p.shape < 0 || p.shape >= (int)(sizeof(kShapes) / sizeof(kShapes[0]))) p.shape = 0;
-  p.RB = p.mfma ? 16 * kShapes[p.shape].rw : 16;
-  p.n_rblk = (t->max_nodes * G + p.RB - 1) / p.RB;
+  const long rows_max = (long)t->max_nodes * G;
+  long gran = 16;  // split granularity in keys
+  p.stream = dtype == ST_BF16;
+  if (!p.stream) {
+    p.rwv = p.rbw = 0;
+    p.RB = 16;
+  } else {
+    // Row groups: enough to hold every row of a kv head, so K and V are read
+    // once per key range (at most 4); row blocks per wave: as many as the
+    // rows need (a tree of 6 nodes uses one 16-row block, not four).
+    p.rwv = rows_max <= 64 ? 1 : rows_max <= 128 ? 2 : 4;
+    p.rbw = rows_max <= 16 ? 1 : rows_max <= 32 ? 2 : 4;
+    const int forced = env_int("ST_ATTN_SHAPE", -1);  // 0..4: (1,1) (1,2) (1,4) (2,4) (4,4)
+    if (forced >= 0 && forced <= 4) {
+      p.rwv = forced <= 2 ? 1 : forced == 3 ? 2 : 4;
+      p.rbw = forced == 0 ? 1 : forced == 1 ? 2 : 4;
+    }
+    p.RB = 16 * p.rbw * p.rwv;
+    gran = 32;
+  }
+  p.n_rblk = (int)((rows_max + p.RB - 1) / p.RB);
   const long keys_max = (long)max_prefix + t->max_nodes;
   const long base = (long)t->B * Hkv * p.n_rblk;
   // aim for about `target` workgroups over the whole batch (one per CU for
-  // the MFMA kernel); splits are even, in multiples of 16 keys
-  const long target = env_int("ST_ATTN_TARGET_WG", p.mfma ? 256 : 512);
+  // the streaming kernel); splits are even, in multiples of `gran` keys
+  const long target = env_int("ST_ATTN_TARGET_WG", p.stream ? 256 : 512);
   long ns = (target + base - 1) / base;
   if (ns < 1) ns = 1;
   long ks = (keys_max + ns - 1) / ns;
-  ks = (ks + 15) / 16 * 16;
-  const int forced = env_int("ST_ATTN_SPLIT_KEYS", 0);
-  if (forced > 0) ks = (forced + 15) / 16 * 16;
-  const long kmax = (keys_max + 15) / 16 * 16;
+  ks = (ks + gran - 1) / gran * gran;
+  const int forced_ks = env_int("ST_ATTN_SPLIT_KEYS", 0);
+  if (forced_ks > 0) ks = (forced_ks + gran - 1) / gran * gran;
+  const long kmax = (keys_max + gran - 1) / gran * gran;
   if (ks < 64) ks = 64;
   if (ks > kmax) ks = kmax;
   p.KS = (int)ks;
@@ -748,20 +849,22 @@ extern "C" int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st
   a.scale_log2 = scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(8 * p.per_xcd), block(256);
-  if (p.mfma) {
-    const Shape sh = kShapes[p.shape];
-    const dim3 mblock(64 * sh.rw * sh.kw);
-#define ST_LAUNCH_MFMA(RW_, KW_)                                                             \
-  if (sh.rw == RW_ && sh.kw == KW_) {                                                       \
-    if (D == 128) hipLaunchKernelGGL((attn_mfma_kernel<128, RW_, KW_>), grid, mblock, 0, s, a); \
-    else hipLaunchKernelGGL((attn_mfma_kernel<64, RW_, KW_>), grid, mblock, 0, s, a);          \
+  if (p.stream) {
+    const dim3 sblock(256);
+    const int shape = p.rwv * 8 + p.rbw;
+#define ST_LAUNCH_STREAM(RWV_, RBW_, NS128_, NS64_)                                          \
+  if (shape == RWV_ * 8 + RBW_) {                                                            \
+    if (D == 128)                                                                            \
+      hipLaunchKernelGGL((attn_stream_kernel<128, NS128_, RWV_, RBW_>), grid, sblock, 0, s, a); \
+    else                                                                                     \
+      hipLaunchKernelGGL((attn_stream_kernel<64, NS64_, RWV_, RBW_>), grid, sblock, 0, s, a);   \
   }
-    ST_LAUNCH_MFMA(4, 2)
-    ST_LAUNCH_MFMA(4, 1)
-    ST_LAUNCH_MFMA(2, 2)
-    ST_LAUNCH_MFMA(2, 4)
-    ST_LAUNCH_MFMA(1, 4)
-#undef ST_LAUNCH_MFMA
+    ST_LAUNCH_STREAM(1, 1, 2, 4)
+    ST_LAUNCH_STREAM(1, 2, 2, 4)
+    ST_LAUNCH_STREAM(1, 4, 2, 4)
+    ST_LAUNCH_STREAM(2, 4, 4, 8)
+    ST_LAUNCH_STREAM(4, 4, 8, 16)
+#undef ST_LAUNCH_STREAM
   } else {
     if (D == 128) hipLaunchKernelGGL((attn_valu_kernel<float, 128>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((attn_valu_kernel<float, 64>), grid, block, 0, s, a);
@@ -771,7 +874,7 @@ extern "C" int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st
     const int TH = tree->total_nodes * Hq;
     const int rpb = 256 / (D / 4);
     const dim3 cg((TH + rpb - 1) / rpb);
-    if (p.mfma) {
+    if (p.stream) {
       if (D == 128) hipLaunchKernelGGL((attn_combine_kernel<uint16_t, 128>), cg, block, 0, s, a);
       else hipLaunchKernelGGL((attn_combine_kernel<uint16_t, 64>), cg, block, 0, s, a);
     } else {
