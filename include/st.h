@@ -107,7 +107,10 @@ size_t st_tree_attention_workspace(const st_tree* tree, int Hq, int Hkv, int D, 
  *   k_cache, v_cache  [B][Hkv][S_max][D] of `dtype`; S_max >= every
  *            prefix_len[b] + N_b; only slots below that are read
  *   prefix_len [B] int32 in [0, max_prefix]
- *   mask     [T][W] from st_tree_mask
+ *   mask     [T][W] from st_tree_mask, or NULL: the kernel then derives each
+ *            row's ancestor mask from tree->parent itself (the same relation
+ *            st_tree_mask writes out), setting ST_STATUS_BAD_PARENT on a bad
+ *            parent array
  *   out      [T][Hq][D] of `dtype` (bf16 stored round-to-nearest-even)
  *   lse      [T][Hq] fp32 natural-log sum of exp of the scaled scores, or NULL
  *   scale    the score scale; 1/sqrt(D) reproduces standard attention
@@ -191,6 +194,53 @@ int st_kv_compact(int B, int Hkv, int D, st_dtype dtype, void* k_cache, void* v_
                   const int32_t* prefix_len, const int32_t* accept_len,
                   const int32_t* accept_nodes, int max_path, int32_t* src_slot, int32_t* new_len,
                   int32_t* status, void* stream);
+
+/*
+ * st_verification_step -- one verification step of one layer in one call:
+ * acceptance of the tree (greedy, or stochastic when draft_logits is set),
+ * tree attention of every node with the ancestor masks derived from
+ * tree->parent inside the attention kernel, then compaction of the accepted
+ * paths' KV rows (SpecInfer developer article §2.1: one pass decodes all tree
+ * paths; the news article's depth-first KV-cache update).  Every field means
+ * what the argument of the same name means for st_verify_greedy /
+ * st_verify_stochastic, st_tree_attention and st_kv_compact; the results are
+ * those of calling them in that order.  Acceptance reads neither the caches
+ * nor the attention output; compaction runs after attention has read the
+ * tree slots (it shares the launch that merges the attention splits), so the
+ * three kernels need no other ordering.  All fields are checked before
+ * anything is enqueued.
+ */
+typedef struct {
+  int32_t Hq, Hkv, D;
+  st_dtype dtype;
+  float scale;                      /* 1/sqrt(D) reproduces standard attention */
+  const void* q;                    /* [T][Hq][D]                              */
+  void* k_cache;                    /* [B][Hkv][S_max][D], compacted in place  */
+  void* v_cache;
+  int32_t S_max;
+  const int32_t* prefix_len;        /* [B]                                     */
+  int32_t max_prefix;               /* [host]                                  */
+  void* out;                        /* [T][Hq][D] of dtype                     */
+  float* lse;                       /* [T][Hq] or NULL                         */
+  int32_t V;
+  const int32_t* tokens;            /* [T]                                     */
+  const float* logits;              /* [T][V] target                           */
+  const float* draft_logits;        /* [T][V], or NULL for greedy acceptance   */
+  float temperature;                /* stochastic only                         */
+  uint64_t seed, offset;            /* stochastic only                         */
+  int32_t* accept_len;              /* [B]                                     */
+  int32_t* accept_nodes;            /* [B][max_depth+1]                        */
+  int32_t* out_tokens;              /* [B][max_depth+2]                        */
+  int32_t* near_ties;               /* [B] or NULL (stochastic only)           */
+  int32_t* src_slot;                /* [B][max_depth+1]                        */
+  int32_t* new_len;                 /* [B]                                     */
+} st_step;
+
+/* Bytes of workspace st_verification_step needs (0 on invalid arguments). */
+size_t st_verification_step_workspace(const st_tree* tree, const st_step* step);
+
+int st_verification_step(const st_tree* tree, const st_step* step, void* workspace,
+                         size_t ws_bytes, int32_t* status, void* stream);
 
 /* Text for a return code or for a status bit (host memory, static). */
 const char* st_status_str(int code);

@@ -52,11 +52,15 @@ def sample_rows(wl, per_req=4, heads=3, seed=0):
     return nodes, hs
 
 
-def attention_errors(wl, dw, nodes=None, heads=None):
-    """Run mask + attention on the GPU; return (max-abs out error, max-abs lse
+def attention_errors(wl, dw, nodes=None, heads=None, derive_mask=False):
+    """Run mask + attention on the GPU (or attention alone, deriving the
+    ancestor masks in the kernel); return (max-abs out error, max-abs lse
     error) against the oracle over the given (or all) rows."""
-    stp.run_mask(dw)
-    stp.run_attention(dw)
+    if derive_mask:
+        stp.run_attention(dw, derive_mask=True)
+    else:
+        stp.run_mask(dw)
+        stp.run_attention(dw)
     torch.cuda.synchronize()
     out = dw.buf["out"].float().cpu().numpy().astype(np.float64)
     lse = dw.buf["lse"].cpu().numpy().astype(np.float64)

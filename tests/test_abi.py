@@ -51,3 +51,24 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         binding.load_library(str(tmp_path / "nope.so"))
+
+
+def test_step_struct_layout_matches_header(tmp_path):
+    """The binding's st_step mirror has the header's size and field offsets
+    (compiled with the host C compiler; no GPU)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    names = [f for f, _ in binding.StStep._fields_]
+    body = "".join(f'printf("%s %zu\\n", "{n}", offsetof(st_step, {n}));\n' for n in names)
+    src = tmp_path / "off.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "st.h"\nint main(void){\n'
+                   + body + 'printf("sizeof %zu\\n", sizeof(st_step));\nreturn 0;}\n')
+    exe = tmp_path / "off"
+    subprocess.check_call([cc, "-I" + os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = dict(line.split() for line in subprocess.check_output([str(exe)]).decode().splitlines())
+    assert int(got["sizeof"]) == ctypes.sizeof(binding.StStep)
+    for n in names:
+        assert int(got[n]) == getattr(binding.StStep, n).offset, n

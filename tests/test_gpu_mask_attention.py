@@ -105,20 +105,56 @@ def test_attention_forced_splits_and_combine(split_keys, monkeypatch):
 
 # bf16 kernel variants by plan shape: (64-row groups per workgroup, 16-row
 # blocks per wavefront) = (1,1) (1,2) (1,4) (2,4) (4,4) for shapes 0..4
+@pytest.mark.parametrize("derive", [False, True])
 @pytest.mark.parametrize("shape", [0, 1, 2, 3, 4])
-def test_attention_every_kernel_shape(shape, monkeypatch):
+def test_attention_every_kernel_shape(shape, derive, monkeypatch):
+    """derive: no mask is passed, the kernel builds it from the parent array."""
     monkeypatch.setenv("ST_ATTN_SHAPE", str(shape))
     for i, (D, Hq, Hkv, nmax) in enumerate([(128, 4, 4, 90), (64, 6, 3, 40), (128, 16, 2, 25)]):
         wl = _small_case(70 + i, D=D, Hq=Hq, Hkv=Hkv, nmax=nmax)
-        err, lerr = attention_errors(wl, to_device(wl))
+        err, lerr = attention_errors(wl, to_device(wl), derive_mask=derive)
         say(f"shape {shape} D {D} Hq {Hq} Hkv {Hkv}: max-abs {err:.2e} lse {lerr:.2e}")
         assert err <= BF16_TOL and lerr <= 1e-3
     # forced short splits: some key groups get no chunk, tails are partial chunks
     monkeypatch.setenv("ST_ATTN_SPLIT_KEYS", "80")
     wl = _small_case(79, D=128, Hq=8, Hkv=2, nmax=70)
-    err, lerr = attention_errors(wl, to_device(wl))
+    err, lerr = attention_errors(wl, to_device(wl), derive_mask=derive)
     say(f"shape {shape} split 80: max-abs {err:.2e} lse {lerr:.2e}")
     assert err <= BF16_TOL and lerr <= 1e-3
+
+
+def test_attention_derived_mask_fp32_and_edges():
+    """The in-kernel ancestor masks on the fp32 path and on the edge trees:
+    a single node with no prefix, a 256-node tree (four mask words), a chain."""
+    wl = make_workload("tiny_fp32", 0)
+    err, lerr = attention_errors(wl, to_device(wl), derive_mask=True)
+    assert err <= F32_TOL and lerr <= F32_TOL
+    wl = _small_case(33, dtype="f32", D=64)
+    err, _ = attention_errors(wl, to_device(wl), derive_mask=True)
+    assert err <= F32_TOL
+    rng = np.random.default_rng(42)
+    trees = [tree_chain(1), tree_random_attach(rng, 17, 5), tree_random_attach(rng, 256, 30),
+             tree_chain(64), tree_chain(256)]
+    for dtype in ("bf16", "f32"):
+        wl = build_workload("edges_d", rng, dtype=dtype, Hq=4, Hkv=2, D=128 if dtype == "bf16" else 64,
+                            V=0, prefix_lens=[0, 128, 63, 1, 40], trees=trees, max_depth=255)
+        dw = to_device(wl)
+        err, lerr = attention_errors(wl, dw, derive_mask=True)
+        say(f"derived edges {dtype}: max-abs {err:.2e} lse {lerr:.2e}")
+        assert err <= (BF16_TOL if dtype == "bf16" else F32_TOL) and status_of(dw) == 0
+
+
+def test_attention_derived_mask_bad_parent_sets_status():
+    from token_tree_verification_st_amd import step
+    for dtype in ("bf16", "f32"):
+        rng = np.random.default_rng(3)
+        wl = build_workload("badp", rng, dtype=dtype, Hq=2, Hkv=2, D=64, V=0, prefix_lens=[5, 7],
+                            trees=[tree_chain(6), tree_chain(9)], max_depth=8)
+        wl.parent[wl.node_off[1] + 4] = 6   # request 1, node 4 points forward
+        dw = to_device(wl)
+        step.run_attention(dw, derive_mask=True)
+        torch.cuda.synchronize()
+        assert status_of(dw) & 1
 
 
 def test_attention_workspace_reused_across_calls(monkeypatch):
@@ -176,7 +212,8 @@ def test_attention_bad_prefix_sets_status():
 def test_attention_full_size_sampled_rows(name):
     wl = make_workload(name, 0)
     nodes, heads = sample_rows(wl)
-    err, lerr = attention_errors(wl, to_device(wl), nodes=nodes, heads=heads)
+    err, lerr = attention_errors(wl, to_device(wl), nodes=nodes, heads=heads,
+                                 derive_mask=name in ("llama7b", "stochastic_tree"))
     say(f"{name}: {len(nodes)} nodes x {len(heads)} heads, max-abs {err:.2e} lse {lerr:.2e}")
     assert err <= BF16_TOL and lerr <= 1e-3
 

@@ -233,3 +233,53 @@ def test_whole_step_matches_oracle(name, stochastic):
                           wl.prefix_len + al + 1)
     assert status_of(dw) == 0
     say(f"{name}: step ok, accept_len {al.tolist()}")
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama7b", "ragged_batch", "stochastic_tree",
+                                  "stochastic_chain"])
+def test_one_call_step_equals_separate_calls(name):
+    """st_verification_step (masks derived in the attention kernel, compaction
+    in the merge launch) gives what the separate entry points give."""
+    wl = make_workload(name, 0)
+    stochastic = "stochastic" in wl.steps
+    a, b = to_device(wl), to_device(wl)
+    stp.verification_step(a, stochastic=stochastic, fused=False)
+    stp.verification_step(b, stochastic=stochastic, fused=True)
+    torch.cuda.synchronize()
+    for k in ("accept_len", "accept_nodes", "out_tokens", "src_slot", "new_len", "status"):
+        assert torch.equal(a.buf[k], b.buf[k]), k
+    if stochastic:
+        assert torch.equal(a.buf["near_ties"], b.buf["near_ties"])
+    # same kernels, same arithmetic: the attention output and lse agree bit for bit
+    assert torch.equal(a.buf["out"], b.buf["out"]) and torch.equal(a.buf["lse"], b.buf["lse"])
+    assert torch.equal(a.k_cache, b.k_cache) and torch.equal(a.v_cache, b.v_cache)
+    say(f"{name}: one-call step equals separate calls, accept_len "
+        f"{b.buf['accept_len'].tolist()[:4]}")
+
+
+def test_one_call_step_compaction_with_long_paths(monkeypatch):
+    """Accepted paths long enough to need several batches of row moves, on
+    both the split-merge and the single-split launch shapes."""
+    rng = np.random.default_rng(12)
+    for prefix, split_keys in ((300, None), (5000, None), (300, "100000")):
+        if split_keys:
+            monkeypatch.setenv("ST_ATTN_SPLIT_KEYS", split_keys)
+        B = 3
+        trees = [tree_chain(40), tree_random_attach(rng, 60, 20), tree_chain(25)]
+        wl = build_workload("long", rng, dtype="bf16", Hq=4, Hkv=2, D=128, V=64,
+                            prefix_lens=[prefix] * B, trees=trees, max_depth=39,
+                            token_rule="plant_leaf_path", logit_sigma=1.0)
+        a, b = to_device(wl), to_device(wl)
+        stp.verification_step(a, fused=False)
+        stp.verification_step(b, fused=True)
+        torch.cuda.synchronize()
+        res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.V, wl.max_depth)
+        assert np.array_equal(b.buf["accept_len"].cpu().numpy(), res["accept_len"])
+        assert int(res["accept_len"].max()) >= 20
+        kn, vn, src, new_len, st = oracle.kv_compact(wl.k_cache, wl.v_cache, wl.prefix_len,
+                                                     res["accept_len"], res["accept_nodes"],
+                                                     wl.max_depth + 1)
+        assert np.array_equal(b.k_cache.cpu().view(torch.int16).numpy().view(np.uint16), kn)
+        assert np.array_equal(b.v_cache.cpu().view(torch.int16).numpy().view(np.uint16), vn)
+        assert torch.equal(a.k_cache, b.k_cache) and torch.equal(a.buf["out"], b.buf["out"])
+        assert status_of(b) == 0

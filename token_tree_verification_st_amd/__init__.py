@@ -21,6 +21,8 @@ from .binding import (  # noqa: F401
     st_tree_attention,
     st_tree_attention_workspace,
     st_tree_mask,
+    st_verification_step,
+    st_verification_step_workspace,
     st_verify_greedy,
     st_verify_greedy_workspace,
     st_verify_stochastic,

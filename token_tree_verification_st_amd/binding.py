@@ -36,6 +36,23 @@ class StTree(ctypes.Structure):
     ]
 
 
+class StStep(ctypes.Structure):
+    """Mirror of st_step (include/st.h), field for field."""
+    _fields_ = [
+        ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("S_max", ctypes.c_int32), ("prefix_len", ctypes.c_void_p), ("max_prefix", ctypes.c_int32),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("V", ctypes.c_int32), ("tokens", ctypes.c_void_p), ("logits", ctypes.c_void_p),
+        ("draft_logits", ctypes.c_void_p), ("temperature", ctypes.c_float),
+        ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64),
+        ("accept_len", ctypes.c_void_p), ("accept_nodes", ctypes.c_void_p),
+        ("out_tokens", ctypes.c_void_p), ("near_ties", ctypes.c_void_p),
+        ("src_slot", ctypes.c_void_p), ("new_len", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 _c = ctypes
 
@@ -58,6 +75,8 @@ def _declare(lib):
                                      P, P, P, S, P, P]),
         "st_kv_compact": (I, [I, I, I, I, P, P, I, P, P, P, I, P, P, P, P]),
         "st_status_str": (_c.c_char_p, [I]),
+        "st_verification_step_workspace": (S, [TP, _c.POINTER(StStep)]),
+        "st_verification_step": (I, [TP, _c.POINTER(StStep), P, S, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -162,7 +181,8 @@ def st_tree_attention_workspace(tree: Tree, Hq: int, Hkv: int, D: int, dtype: to
 
 def st_tree_attention(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix: int, mask, out,
                       lse=None, workspace=None, scale: Optional[float] = None, status=None):
-    """q [T][Hq][D]; caches [B][Hkv][S_max][D]; out like q; lse fp32 [T][Hq] or None."""
+    """q [T][Hq][D]; caches [B][Hkv][S_max][D]; out like q; lse fp32 [T][Hq] or None;
+    mask [T*W] int64 from st_tree_mask, or None to derive the masks from the tree."""
     T, Hq, D = q.shape
     B, Hkv, S_max, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or T != tree.T or B != tree.B:
@@ -172,7 +192,8 @@ def st_tree_attention(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix: i
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
     _dev(prefix_len, "prefix_len", torch.int32, B)
-    _dev(mask, "mask", torch.int64, tree.T * tree.W)
+    if mask is not None:
+        _dev(mask, "mask", torch.int64, tree.T * tree.W)
     if lse is not None:
         _dev(lse, "lse", torch.float32, T * Hq)
     need = st_tree_attention_workspace(tree, Hq, Hkv, D, q.dtype, max_prefix)
@@ -248,6 +269,66 @@ def st_kv_compact(k_cache, v_cache, prefix_len, accept_len, accept_nodes, src_sl
         B, Hkv, D, _dtype_code(k_cache), _ptr(k_cache), _ptr(v_cache), S_max, _ptr(prefix_len),
         _ptr(accept_len), _ptr(accept_nodes), max_path, _ptr(src_slot), _ptr(new_len),
         _ptr(status), _stream()), "st_kv_compact")
+
+
+def _step_struct(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix: int, out, lse,
+                 tokens, logits, draft_logits, temperature: float, seed: int, offset: int,
+                 accept_len, accept_nodes, out_tokens, near_ties, src_slot, new_len,
+                 scale: Optional[float]) -> StStep:
+    T, Hq, D = q.shape
+    B, Hkv, S_max, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or T != tree.T or B != tree.B:
+        raise ValueError("shape mismatch between q, caches and tree")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
+        _dev(t, name, q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _dev(prefix_len, "prefix_len", torch.int32, B)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, T * Hq)
+    V = logits.shape[-1]
+    _dev(tokens, "tokens", torch.int32, T)
+    _dev(logits, "logits", torch.float32, T * V)
+    if draft_logits is not None:
+        _dev(draft_logits, "draft_logits", torch.float32, T * V)
+    _path_outputs(tree, accept_len, accept_nodes, out_tokens)
+    _dev(src_slot, "src_slot", torch.int32, B * (tree.max_depth + 1))
+    _dev(new_len, "new_len", torch.int32, B)
+    if near_ties is not None:
+        _dev(near_ties, "near_ties", torch.int32, B)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    return StStep(Hq, Hkv, D, _dtype_code(q), scale, q.data_ptr(), k_cache.data_ptr(),
+                  v_cache.data_ptr(), S_max, prefix_len.data_ptr(), max_prefix, out.data_ptr(),
+                  0 if lse is None else lse.data_ptr(), V, tokens.data_ptr(), logits.data_ptr(),
+                  0 if draft_logits is None else draft_logits.data_ptr(), float(temperature),
+                  int(seed), int(offset), accept_len.data_ptr(), accept_nodes.data_ptr(),
+                  out_tokens.data_ptr(), 0 if near_ties is None else near_ties.data_ptr(),
+                  src_slot.data_ptr(), new_len.data_ptr())
+
+
+def st_verification_step_workspace(tree: Tree, step: StStep) -> int:
+    return load_library().st_verification_step_workspace(tree.ref, ctypes.byref(step))
+
+
+def st_verification_step(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix: int, out, lse,
+                         tokens, logits, accept_len, accept_nodes, out_tokens, src_slot, new_len,
+                         workspace, draft_logits=None, temperature: float = 1.0, seed: int = 0,
+                         offset: int = 0, near_ties=None, scale: Optional[float] = None,
+                         status=None):
+    """Acceptance, attention and compaction of one layer in one call (greedy
+    when draft_logits is None, else stochastic).  The caches are compacted in
+    place."""
+    step = _step_struct(tree, q, k_cache, v_cache, prefix_len, max_prefix, out, lse, tokens,
+                        logits, draft_logits, temperature, seed, offset, accept_len, accept_nodes,
+                        out_tokens, near_ties, src_slot, new_len, scale)
+    need = st_verification_step_workspace(tree, step)
+    if need == 0:
+        raise ValueError("st_verification_step: invalid arguments")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check(load_library().st_verification_step(
+        tree.ref, ctypes.byref(step), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(status), _stream()), "st_verification_step")
 
 
 def st_status_str(code: int) -> str:

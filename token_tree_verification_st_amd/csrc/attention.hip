@@ -26,7 +26,7 @@
 //
 // fp32 path (VALU).  The same decomposition with 16 rows per workgroup and
 // plain fp32 dot products; it serves fp32 inputs, which need 1e-5 accuracy.
-#include "st_internal.h"
+#include "step_internal.h"
 
 #include <math.h>
 #include <stdlib.h>
@@ -43,6 +43,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 struct AttnArgs {
   const int32_t* node_off;
+  const int32_t* parent;     // used when mask is null: masks are derived in the kernel
   const int32_t* prefix_len;
   const uint64_t* mask;
   const void* q;
@@ -105,6 +106,28 @@ __device__ inline bool tree_bit(uint64_t w0, uint64_t w1, uint64_t w2, uint64_t 
   const int wi = j >> 6;
   const uint64_t w = wi == 0 ? w0 : wi == 1 ? w1 : wi == 2 ? w2 : w3;
   return (w >> (j & 63)) & 1ull;
+}
+
+// Ancestor bitmask of request-local node `node` (the node itself and every
+// node on its root path) from the request's parent array in LDS.  Each step
+// moves to a smaller index, so the walk ends; it returns false when it meets a
+// parent outside [0, j) or a root whose parent is not -1.
+__device__ inline bool ancestor_words(const int* sPar, int node, uint64_t& w0, uint64_t& w1,
+                                      uint64_t& w2, uint64_t& w3) {
+  w0 = w1 = w2 = w3 = 0ull;
+  int j = node;
+  while (true) {
+    const uint64_t bit = 1ull << (j & 63);
+    const int wi = j >> 6;
+    w0 |= wi == 0 ? bit : 0ull;
+    w1 |= wi == 1 ? bit : 0ull;
+    w2 |= wi == 2 ? bit : 0ull;
+    w3 |= wi == 3 ? bit : 0ull;
+    const int p = sPar[j];
+    if (j == 0) return p == -1;
+    if (p < 0 || p >= j) return false;
+    j = p;
+  }
 }
 
 // ---------------------------------------------------------------- bf16 MFMA, shared pieces
@@ -362,7 +385,7 @@ attn_stream_kernel(AttnArgs a) {
   constexpr int MWORDS = ROWS * 4;
   constexpr int MPT = (MWORDS + 255) / 256;           // mask words per thread
   static_assert(DPC * (NSTAGE - 1) <= 63, "in-flight loads exceed the vmcnt range");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[BODY + MWORDS * 8];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[BODY + MWORDS * 8 + ST_MAX_NODES * 4];
   uint64_t* sMask = (uint64_t*)(lds + BODY);
 
   Item it;
@@ -395,14 +418,26 @@ attn_stream_kernel(AttnArgs a) {
   const int niter = (nch + KWV - 1) / KWV;       // the same for every wavefront
   uint16_t* ring = (uint16_t*)lds + kg * NSTAGE * STAGE;
 
-  // Ancestor-mask words of the workgroup's rows (clamped, unconditional loads)
+  // Ancestor masks are needed only when the key range reaches tree keys: read
+  // the workgroup's rows of `mask`, or (mask == null) the request's parent
+  // array, from which they are derived below.  Clamped, unconditional loads.
+  const bool need_mask = k1 > rq.P;
+  const bool derive = a.mask == nullptr;
   uint64_t mword[MPT];
+  int par = -1;
 #pragma unroll
-  for (int i = 0; i < MPT; ++i) {
-    const int idx = min(tid + 256 * i, MWORDS - 1), row = row0 + idx / 4, w = idx % 4;
-    const int node = min(row, rows_b - 1) / a.G;
-    mword[i] = a.mask[(size_t)(rq.lo + node) * a.W + min(w, a.W - 1)];
-    mword[i] = (row < rows_b && w < a.W) ? mword[i] : 0ull;
+  for (int i = 0; i < MPT; ++i) mword[i] = 0ull;
+  if (need_mask) {
+    if (derive) {
+      par = a.parent[rq.lo + min(tid, rq.n - 1)];
+    } else {
+#pragma unroll
+      for (int i = 0; i < MPT; ++i) {
+        const int idx = min(tid + 256 * i, MWORDS - 1), row = row0 + idx / 4, w = idx % 4;
+        const int node = min(row, rows_b - 1) / a.G;
+        mword[i] = a.mask[(size_t)(rq.lo + node) * a.W + min(w, a.W - 1)];
+      }
+    }
   }
   // Q^T fragments of this wavefront's rows (rows past the end repeat the last)
   bf16x8 qf[RBW][NKS];
@@ -422,9 +457,29 @@ attn_stream_kernel(AttnArgs a) {
       chunk_dma<D, RWV>(ring + s * STAGE, ring + s * STAGE + kCK * D, kgp, vgp,
                         k0 + (s * KWV + kg) * kCK, klast, rw, lane);
   wait_chunks<NSTAGE - 1, DPC>(min(NSTAGE - 1, nmine));  // the q and mask loads are older
+  if (need_mask) {
+    if (derive) {
+      int* sPar = (int*)(sMask + MWORDS);
+      if (tid < rq.n) sPar[tid] = par;
+      lds_barrier();
+      if (tid < ROWS) {
+        const int row = row0 + tid;
+        uint64_t w0 = 0ull, w1 = 0ull, w2 = 0ull, w3 = 0ull;
+        if (row < rows_b && !ancestor_words(sPar, row / a.G, w0, w1, w2, w3))
+          st::set_status(a.status, ST_STATUS_BAD_PARENT);
+        sMask[tid * 4 + 0] = w0;
+        sMask[tid * 4 + 1] = w1;
+        sMask[tid * 4 + 2] = w2;
+        sMask[tid * 4 + 3] = w3;
+      }
+    } else {
 #pragma unroll
-  for (int i = 0; i < MPT; ++i)
-    if (tid + 256 * i < MWORDS) sMask[tid + 256 * i] = mword[i];
+      for (int i = 0; i < MPT; ++i) {
+        const int idx = tid + 256 * i, row = row0 + idx / 4, w = idx % 4;
+        if (idx < MWORDS) sMask[idx] = (row < rows_b && w < a.W) ? mword[i] : 0ull;
+      }
+    }
+  }
   lds_barrier();
 
   f32x4 acc[RBW][NDB];
@@ -579,12 +634,33 @@ attn_valu_kernel(AttnArgs a) {
   const Tin* qp = (const Tin*)a.q + (size_t)grow * D;
   for (int d = c; d < D; d += 16) sQ[r][d] = row_ok ? load_val(qp + d) : 0.f;
   uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
-  if (row_ok) {
-    const uint64_t* mr = a.mask + (size_t)(rq.lo + node) * a.W;
-    mw0 = mr[0];
-    if (a.W > 1) mw1 = mr[1];
-    if (a.W > 2) mw2 = mr[2];
-    if (a.W > 3) mw3 = mr[3];
+  if (a.mask) {
+    if (row_ok) {
+      const uint64_t* mr = a.mask + (size_t)(rq.lo + node) * a.W;
+      mw0 = mr[0];
+      if (a.W > 1) mw1 = mr[1];
+      if (a.W > 2) mw2 = mr[2];
+      if (a.W > 3) mw3 = mr[3];
+    }
+  } else {  // derive the row's ancestor mask from the request's parent array
+    __shared__ int sPar[ST_MAX_NODES];
+    __shared__ uint64_t sRow[R][4];
+    for (int i = tid; i < rq.n; i += 256) sPar[i] = a.parent[rq.lo + i];
+    __syncthreads();
+    if (c == 0) {
+      uint64_t w0 = 0ull, w1 = 0ull, w2 = 0ull, w3 = 0ull;
+      if (row_ok && !ancestor_words(sPar, node, w0, w1, w2, w3))
+        st::set_status(a.status, ST_STATUS_BAD_PARENT);
+      sRow[r][0] = w0;
+      sRow[r][1] = w1;
+      sRow[r][2] = w2;
+      sRow[r][3] = w3;
+    }
+    __syncthreads();
+    mw0 = sRow[r][0];
+    mw1 = sRow[r][1];
+    mw2 = sRow[r][2];
+    mw3 = sRow[r][3];
   }
   const size_t head_off = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
   const Tin* kg = (const Tin*)a.k + head_off;
@@ -673,14 +749,14 @@ attn_valu_kernel(AttnArgs a) {
 // ---------------------------------------------------------------- combine
 
 // Merge the splits of every row: the partial (m, l) pairs and 4 dims of the
-// partial outputs of up to 8 splits are all loaded before any is used.
+// partial outputs of up to 8 splits are all loaded before any is used.  Block
+// `blk` covers 256 / (D/4) consecutive rows.
 template <typename Tout, int D>
-__global__ void __launch_bounds__(256)
-attn_combine_kernel(AttnArgs a) {
+__device__ inline void combine_block(const AttnArgs& a, int blk) {
   constexpr int LPR = D / 4;        // lanes per row, 4 dims each
   constexpr int RPB = 256 / LPR;    // rows per block
   constexpr int CHUNK = 8;
-  const int grow = blockIdx.x * RPB + threadIdx.x / LPR;
+  const int grow = blk * RPB + threadIdx.x / LPR;
   const int d = 4 * (threadIdx.x % LPR);
   const int TH = a.T * a.Hq;
   if (grow >= TH) return;
@@ -726,6 +802,27 @@ attn_combine_kernel(AttnArgs a) {
   if (a.lse && d == 0) a.lse[grow] = (M + log2f(L)) * kLn2;
 }
 
+template <typename Tout, int D>
+__global__ void __launch_bounds__(256)
+attn_combine_kernel(AttnArgs a) {
+  combine_block<Tout, D>(a, blockIdx.x);
+}
+
+// The merge of the splits followed, in the same launch, by the compaction of
+// the accepted paths (blocks n_combine.. : one per request and cache head).
+// The attention kernel has finished reading the tree slots when this starts.
+template <typename Tout, int D>
+__global__ void __launch_bounds__(256)
+attn_combine_compact_kernel(AttnArgs a, st::CompactArgs c, int n_combine) {
+  const int blk = blockIdx.x;
+  if (blk < n_combine) {
+    combine_block<Tout, D>(a, blk);
+  } else {
+    const int k = blk - n_combine;
+    st::kv_compact_block(c, k / (2 * c.Hkv), k % (2 * c.Hkv));
+  }
+}
+
 // ---------------------------------------------------------------- planning
 
 struct Plan {
@@ -757,9 +854,14 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
   } else {
     // Row groups: enough to hold every row of a kv head, so K and V are read
     // once per key range (at most 4); row blocks per wave: as many as the
-    // rows need (a tree of 6 nodes uses one 16-row block, not four).
+    // rows need (a tree of 6 nodes uses one 16-row block, not four).  Up to
+    // 64 rows, when the batch must be split over keys anyway to fill the
+    // chip, two 32-row workgroups per kv head (the second reads K and V from
+    // the L2 the first filled) halve the splits to merge and give each
+    // wavefront twice the chunks, which evens out its chunk count.
     p.rwv = rows_max <= 64 ? 1 : rows_max <= 128 ? 2 : 4;
     p.rbw = rows_max <= 16 ? 1 : rows_max <= 32 ? 2 : 4;
+    if (rows_max <= 64 && (long)t->B * Hkv * 2 <= 256) p.rbw = 2;
     const int forced = env_int("ST_ATTN_SHAPE", -1);  // 0..4: (1,1) (1,2) (1,4) (2,4) (4,4)
     if (forced >= 0 && forced <= 4) {
       p.rwv = forced <= 2 ? 1 : forced == 3 ? 2 : 4;
@@ -804,16 +906,16 @@ extern "C" size_t st_tree_attention_workspace(const st_tree* tree, int Hq, int H
   return p.ws_bytes;
 }
 
-extern "C" int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype,
-                                 float scale, const void* q, const void* k_cache,
-                                 const void* v_cache, int S_max, const int32_t* prefix_len,
-                                 int max_prefix, const uint64_t* mask, void* out, float* lse,
-                                 void* workspace, size_t ws_bytes, int32_t* status,
-                                 void* stream) {
+int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype,
+                            float scale, const void* q, const void* k_cache, const void* v_cache,
+                            int S_max, const int32_t* prefix_len, int max_prefix,
+                            const uint64_t* mask, void* out, float* lse, void* workspace,
+                            size_t ws_bytes, int32_t* status, void* stream,
+                            const st::CompactArgs* compact) {
   Plan p;
   int rc = make_plan(tree, Hq, Hkv, D, dtype, max_prefix, p);
   if (rc) return rc;
-  if (!q || !k_cache || !v_cache || !prefix_len || !mask || !out || S_max < 1 ||
+  if (!q || !k_cache || !v_cache || !prefix_len || !out || S_max < 1 ||
       !(scale > 0.f) || !isfinite(scale))
     return ST_E_INVALID;
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) % 16)
@@ -821,6 +923,7 @@ extern "C" int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st
   if (p.ws_bytes && (!workspace || ws_bytes < p.ws_bytes)) return ST_E_WORKSPACE;
   AttnArgs a;
   a.node_off = tree->node_off;
+  a.parent = tree->parent;
   a.prefix_len = prefix_len;
   a.mask = mask;
   a.q = q;
@@ -870,10 +973,12 @@ extern "C" int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st
     else hipLaunchKernelGGL((attn_valu_kernel<float, 64>), grid, block, 0, s, a);
   }
   if ((rc = st::check_launch())) return rc;
-  if (p.NS > 1) {
-    const int TH = tree->total_nodes * Hq;
-    const int rpb = 256 / (D / 4);
-    const dim3 cg((TH + rpb - 1) / rpb);
+  const int TH = tree->total_nodes * Hq;
+  const int rpb = 256 / (D / 4);
+  const int n_combine = p.NS > 1 ? (TH + rpb - 1) / rpb : 0;
+  if (!compact) {
+    if (n_combine == 0) return ST_OK;
+    const dim3 cg(n_combine);
     if (p.stream) {
       if (D == 128) hipLaunchKernelGGL((attn_combine_kernel<uint16_t, 128>), cg, block, 0, s, a);
       else hipLaunchKernelGGL((attn_combine_kernel<uint16_t, 64>), cg, block, 0, s, a);
@@ -881,7 +986,31 @@ extern "C" int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st
       if (D == 128) hipLaunchKernelGGL((attn_combine_kernel<float, 128>), cg, block, 0, s, a);
       else hipLaunchKernelGGL((attn_combine_kernel<float, 64>), cg, block, 0, s, a);
     }
-    rc = st::check_launch();
+    return st::check_launch();
   }
-  return rc;
+  const dim3 cg(n_combine + compact->B * 2 * compact->Hkv);
+  const st::CompactArgs& c = *compact;
+  if (p.stream) {
+    if (D == 128)
+      hipLaunchKernelGGL((attn_combine_compact_kernel<uint16_t, 128>), cg, block, 0, s, a, c, n_combine);
+    else
+      hipLaunchKernelGGL((attn_combine_compact_kernel<uint16_t, 64>), cg, block, 0, s, a, c, n_combine);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL((attn_combine_compact_kernel<float, 128>), cg, block, 0, s, a, c, n_combine);
+    else
+      hipLaunchKernelGGL((attn_combine_compact_kernel<float, 64>), cg, block, 0, s, a, c, n_combine);
+  }
+  return st::check_launch();
+}
+
+extern "C" int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype,
+                                 float scale, const void* q, const void* k_cache,
+                                 const void* v_cache, int S_max, const int32_t* prefix_len,
+                                 int max_prefix, const uint64_t* mask, void* out, float* lse,
+                                 void* workspace, size_t ws_bytes, int32_t* status,
+                                 void* stream) {
+  return st::tree_attention_impl(tree, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, S_max,
+                                 prefix_len, max_prefix, mask, out, lse, workspace, ws_bytes,
+                                 status, stream, nullptr);
 }

@@ -1,0 +1,66 @@
+// Device body of the accepted-path KV compaction (the depth-first KV-cache
+// update of the SpecInfer news article, "Token 樹驗證器"): slot P + j of every
+// kv head takes what slot P + path[j] held before, for j = 0..L.  Shared by
+// st_kv_compact and by the combine launch of st_verification_step.
+//
+// The copy is in place.  A path strictly increases (path[j] >= j), so the
+// source of a later move is never the destination of an earlier one.  One
+// 256-thread workgroup moves the rows of one (request, cache, head): a batch
+// of moves first reads all of its sources, then (after a barrier) writes all
+// of its destinations, so within a batch no source is overwritten before it
+// is read, and later batches read only slots no earlier move wrote.
+#pragma once
+#include "st_internal.h"
+
+namespace st {
+
+struct CompactArgs {
+  int B, Hkv, S_max, chunks;  // chunks: 16-byte pieces per cache row (<= 256)
+  uint4* kc;
+  uint4* vc;
+  const int32_t* prefix_len;
+  const int32_t* accept_len;
+  const int32_t* accept_nodes;
+  int max_path;
+  int32_t* src_slot;
+  int32_t* new_len;
+  int32_t* status;
+};
+
+// One workgroup (blockDim.x == 256): request b, cache row set y (< Hkv: keys
+// of head y, else values of head y - Hkv).
+__device__ inline void kv_compact_block(const CompactArgs& c, int b, int y) {
+  const int P = c.prefix_len[b], L = c.accept_len[b];
+  const int32_t* path = c.accept_nodes + (size_t)b * c.max_path;
+  int bad = 0;
+  if (L < 0 || L + 1 > c.max_path || P < 0) {
+    bad = ST_STATUS_PATH_OVERFLOW;
+  } else {
+    for (int j = 0; j <= L; ++j) {
+      const int n = path[j];
+      if (n < 0 || (long)P + n >= c.S_max || (j > 0 && n <= path[j - 1])) bad = ST_STATUS_BAD_PARENT;
+    }
+  }
+  if (y == 0 && threadIdx.x == 0) {
+    for (int j = 0; j < c.max_path; ++j)
+      c.src_slot[(size_t)b * c.max_path + j] = (!bad && j <= L) ? P + path[j] : -1;
+    c.new_len[b] = bad ? P : P + L + 1;
+    st::set_status(c.status, bad);
+  }
+  if (bad) return;
+  const int head = y % c.Hkv;
+  uint4* rows = (y < c.Hkv ? c.kc : c.vc) + ((size_t)b * c.Hkv + head) * (size_t)c.S_max * c.chunks;
+  const int per_pass = 256 / c.chunks;
+  const int col = threadIdx.x % c.chunks, jr = threadIdx.x / c.chunks;
+  for (int j0 = 0; j0 <= L; j0 += per_pass) {
+    const int j = j0 + jr;
+    const bool move = jr < per_pass && j <= L && path[min(j, L)] != j;
+    uint4 v;
+    if (move) v = rows[(size_t)(P + path[j]) * c.chunks + col];
+    __syncthreads();
+    if (move) rows[(size_t)(P + j) * c.chunks + col] = v;
+    __syncthreads();
+  }
+}
+
+}  // namespace st

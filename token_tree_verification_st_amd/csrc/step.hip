@@ -1,0 +1,64 @@
+// st_verification_step: acceptance, attention with in-kernel ancestor masks,
+// then the split merge and the KV compaction in one launch.
+#include "step_internal.h"
+
+#include <math.h>
+
+namespace {
+
+size_t verify_ws(const st_tree* t, const st_step* s) {
+  return s->draft_logits ? st_verify_stochastic_workspace(t, s->V)
+                         : st_verify_greedy_workspace(t, s->V);
+}
+
+bool step_fields_ok(const st_step* s) {
+  return s && s->q && s->k_cache && s->v_cache && s->prefix_len && s->out && s->tokens &&
+         s->logits && s->accept_len && s->accept_nodes && s->out_tokens && s->src_slot &&
+         s->new_len && s->V >= 1 && s->S_max >= 1 && s->max_prefix >= 0 &&
+         s->scale > 0.f && isfinite(s->scale) &&
+         (!s->draft_logits || (s->temperature > 0.f && isfinite(s->temperature)));
+}
+
+}  // namespace
+
+extern "C" size_t st_verification_step_workspace(const st_tree* tree, const st_step* s) {
+  if (st::check_tree_host(tree) || !step_fields_ok(s)) return 0;
+  const size_t a = st_tree_attention_workspace(tree, s->Hq, s->Hkv, s->D, s->dtype, s->max_prefix);
+  return st::align_up(verify_ws(tree, s), 256) + a;
+}
+
+extern "C" int st_verification_step(const st_tree* tree, const st_step* s, void* workspace,
+                                    size_t ws_bytes, int32_t* status, void* stream) {
+  int rc = st::check_tree_host(tree);
+  if (rc) return rc;
+  if (!step_fields_ok(s)) return ST_E_INVALID;
+  // every check that the three launches would make, before enqueueing any
+  if (s->Hq < 1 || s->Hkv < 1 || s->Hq % s->Hkv || (s->D != 64 && s->D != 128))
+    return ST_E_UNSUPPORTED;
+  if (s->dtype != ST_F32 && s->dtype != ST_BF16) return ST_E_INVALID;
+  if (((uintptr_t)s->q | (uintptr_t)s->k_cache | (uintptr_t)s->v_cache | (uintptr_t)s->out) % 16)
+    return ST_E_INVALID;
+  const size_t vws = verify_ws(tree, s);
+  const size_t off = st::align_up(vws, 256);
+  const size_t aws = st_tree_attention_workspace(tree, s->Hq, s->Hkv, s->D, s->dtype, s->max_prefix);
+  if ((vws || aws) && (!workspace || ws_bytes < off + aws)) return ST_E_WORKSPACE;
+  st::CompactArgs c;
+  const int max_path = tree->max_depth + 1;
+  rc = st::fill_compact_args(tree->B, s->Hkv, s->D, s->dtype, s->k_cache, s->v_cache, s->S_max,
+                             s->prefix_len, s->accept_len, s->accept_nodes, max_path,
+                             s->src_slot, s->new_len, status, c);
+  if (rc) return rc;
+
+  if (s->draft_logits)
+    rc = st_verify_stochastic(tree, s->V, s->tokens, s->logits, s->draft_logits, s->temperature,
+                              s->seed, s->offset, s->accept_len, s->accept_nodes, s->out_tokens,
+                              s->near_ties, workspace, vws, status, stream);
+  else
+    rc = st_verify_greedy(tree, s->V, s->tokens, s->logits, s->accept_len, s->accept_nodes,
+                          s->out_tokens, workspace, vws, status, stream);
+  if (rc) return rc;
+  return st::tree_attention_impl(tree, s->Hq, s->Hkv, s->D, s->dtype, s->scale, s->q,
+                                 s->k_cache, s->v_cache, s->S_max, s->prefix_len, s->max_prefix,
+                                 nullptr, s->out, s->lse, (char*)workspace + off, aws, status,
+                                 stream, &c);
+}

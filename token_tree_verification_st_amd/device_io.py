@@ -84,6 +84,9 @@ def alloc_outputs(dw: DeviceWorkload, device="cuda"):
     if dw.V > 0:
         ws = max(st_verify_greedy_workspace(tree, dw.V), st_verify_stochastic_workspace(tree, dw.V))
         b["verify_ws"] = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        # the one-call step: acceptance workspace (256-aligned), then attention's
+        b["step_ws"] = torch.empty((ws + 255) // 256 * 256 + b["attn_ws"].numel(),
+                                   dtype=torch.uint8, device=device)
     b["src_slot"] = torch.zeros(dw.B, mp, dtype=torch.int32, device=device)
     b["new_len"] = torch.zeros(dw.B, dtype=torch.int32, device=device)
     b["status"] = torch.zeros(1, dtype=torch.int32, device=device)

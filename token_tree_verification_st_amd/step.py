@@ -1,11 +1,13 @@
-"""One verification step of one attention layer, as a sequence of C-ABI calls
-on the current stream: ancestor mask -> tree attention -> acceptance (greedy or
-stochastic) -> KV compaction.  Every call only enqueues kernels."""
+"""One verification step of one attention layer on the current stream:
+acceptance (greedy or stochastic), tree attention and KV compaction, either as
+the one-call st_verification_step (ancestor masks derived inside attention,
+compaction in the launch that merges the attention splits) or as the sequence
+of separate entry points, mask first.  Every call only enqueues kernels."""
 
 from __future__ import annotations
 
-from .binding import (st_kv_compact, st_tree_attention, st_tree_mask, st_verify_greedy,
-                      st_verify_stochastic)
+from .binding import (st_kv_compact, st_tree_attention, st_tree_mask, st_verification_step,
+                      st_verify_greedy, st_verify_stochastic)
 from .device_io import DeviceWorkload
 
 
@@ -14,11 +16,12 @@ def run_mask(dw: DeviceWorkload):
     st_tree_mask(dw.tree, b["mask"], b["depth"], b["status"])
 
 
-def run_attention(dw: DeviceWorkload, scale=None):
+def run_attention(dw: DeviceWorkload, scale=None, derive_mask: bool = False):
+    """derive_mask: pass no mask, so the kernel derives it from the tree."""
     b = dw.buf
     st_tree_attention(dw.tree, dw.q, dw.k_cache, dw.v_cache, dw.prefix_len, dw.max_prefix,
-                      b["mask"], b["out"], b["lse"], b["attn_ws"], scale=scale,
-                      status=b["status"])
+                      None if derive_mask else b["mask"], b["out"], b["lse"], b["attn_ws"],
+                      scale=scale, status=b["status"])
 
 
 def run_verify(dw: DeviceWorkload, stochastic: bool):
@@ -38,10 +41,24 @@ def run_compact(dw: DeviceWorkload):
                   b["src_slot"], b["new_len"], b["status"])
 
 
+def run_step(dw: DeviceWorkload, stochastic: bool):
+    """The whole step in one C-ABI call."""
+    b = dw.buf
+    st_verification_step(dw.tree, dw.q, dw.k_cache, dw.v_cache, dw.prefix_len, dw.max_prefix,
+                         b["out"], b["lse"], dw.tokens, dw.logits, b["accept_len"],
+                         b["accept_nodes"], b["out_tokens"], b["src_slot"], b["new_len"],
+                         b["step_ws"], draft_logits=dw.draft_logits if stochastic else None,
+                         temperature=dw.temperature, seed=dw.rng_seed, offset=dw.rng_offset,
+                         near_ties=b["near_ties"] if stochastic else None, status=b["status"])
+
+
 def verification_step(dw: DeviceWorkload, stochastic: bool = False, verify: bool = True,
-                      compact: bool = True):
-    """mask -> attention -> acceptance -> compaction (acceptance and compaction
-    need logits)."""
+                      compact: bool = True, fused: bool = True):
+    """One step: the one-call path when it applies (logits present, acceptance
+    and compaction wanted), else mask -> attention -> acceptance -> compaction."""
+    if fused and verify and compact and dw.V > 0:
+        run_step(dw, stochastic)
+        return
     run_mask(dw)
     run_attention(dw)
     if verify and dw.V > 0:
