@@ -374,49 +374,97 @@ template <int D, int NSTAGE, int RWV, int RBW>
 __global__ void __launch_bounds__(256, 1)
 attn_stream_kernel(AttnArgs a) {
   constexpr int KWV = 4 / RWV;
+  constexpr bool PRIVATE = RWV == 1;                  // every wavefront owns its ring
+  constexpr bool QLDS = RWV == 1;                     // Q staged in LDS once for all key groups
   constexpr int NKS = D / 32, NDB = D / 16, CH = D / 8;
   constexpr int WROWS = 16 * RBW, ROWS = WROWS * RWV;
   constexpr int STAGE = 2 * kCK * D;                  // bf16 elements: K then V
   constexpr int DPC = 2 * (kCK * CH / 64) / RWV;      // direct loads per chunk and wavefront
+  constexpr int PRIME = PRIVATE ? NSTAGE : NSTAGE - 1; // chunks in flight when the loop starts
   constexpr int RING_BYTES = KWV * NSTAGE * STAGE * 2;
   constexpr int SLOT = (NDB * 4 + 2) * 64;            // floats: one row block of one wave
   constexpr int MERGE_BYTES = KWV > 1 ? RWV * RBW * KWV * SLOT * 4 : 0;
   constexpr int BODY = RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES;
+  constexpr int QBYTES = QLDS ? ROWS * D * 2 : 0;
   constexpr int MWORDS = ROWS * 4;
   constexpr int MPT = (MWORDS + 255) / 256;           // mask words per thread
-  static_assert(DPC * (NSTAGE - 1) <= 63, "in-flight loads exceed the vmcnt range");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[BODY + MWORDS * 8 + ST_MAX_NODES * 4];
-  uint64_t* sMask = (uint64_t*)(lds + BODY);
+  static_assert(DPC * PRIME <= 63, "in-flight loads exceed the vmcnt range");
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t lds[BODY + QBYTES + MWORDS * 8 + ST_MAX_NODES * 4];
+  uint16_t* sQ = (uint16_t*)(lds + BODY);
+  uint64_t* sMask = (uint64_t*)(lds + BODY + QBYTES);
+  int* sPar = (int*)(sMask + MWORDS);
 
   Item it;
   if (!decode_item(a, it)) return;
-  const ReqInfo rq = request_info(a, it.b);
-  if (!rq.ok) {
-    if (threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
-      st::set_status(a.status, ST_STATUS_BAD_PREFIX);
-    return;
-  }
-  const int rows_b = rq.n * a.G;
-  const int row0 = it.rblk * ROWS;
-  if (row0 >= rows_b) return;
-  const int k0 = it.split * a.KS;
-  if (k0 >= rq.key_end) return;
-  const int k1 = min(k0 + a.KS, rq.key_end);
-  const int klast = k1 - 1;
-
   // the wavefront index is uniform: keep it (and all that derives from it) scalar
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rw = wave % RWV, kg = wave / RWV;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int wrow0 = row0 + rw * WROWS;
+  const int k0 = it.split * a.KS;
   const size_t head_off = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
   const uint16_t* kgp = (const uint16_t*)a.k + head_off;
   const uint16_t* vgp = (const uint16_t*)a.v + head_off;
+  uint16_t* ring = (uint16_t*)lds + kg * NSTAGE * STAGE;
+
+  // Start streaming before the request's sizes are known: the first chunk of
+  // this key group, with rows clamped to the split's nominal end and to the
+  // head's S_max slots (always inside the cache).  It is checked below.
+  const int klast_spec = min(k0 + a.KS, a.S_max) - 1;
+  const int ck0 = k0 + kg * kCK;
+  const bool spec = ck0 <= klast_spec;
+  if (spec) chunk_dma<D, RWV>(ring, ring + kCK * D, kgp, vgp, ck0, klast_spec, rw, lane);
+
+  const ReqInfo rq = request_info(a, it.b);
+  const int rows_b = rq.n * a.G;
+  const int row0 = it.rblk * ROWS;
+  if (!rq.ok || row0 >= rows_b || k0 >= rq.key_end) {
+    ST_WAIT_VMCNT(0);  // no direct load may land in LDS after the workgroup has left
+    if (!rq.ok && threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
+      st::set_status(a.status, ST_STATUS_BAD_PREFIX);
+    return;
+  }
+  const int k1 = min(k0 + a.KS, rq.key_end);
+  const int klast = k1 - 1;
+  const int wrow0 = row0 + rw * WROWS;
   const int nch = (k1 - k0 + kCK - 1) / kCK;
   const int nmine = (nch - kg + KWV - 1) / KWV;  // chunks kg, kg + KWV, ...
   const int niter = (nch + KWV - 1) / KWV;       // the same for every wavefront
-  uint16_t* ring = (uint16_t*)lds + kg * NSTAGE * STAGE;
+  const int want = min(PRIME, nmine);
+  // The first chunk was right if it exists and ends inside the range (its rows
+  // were then not clamped); otherwise drain it and, if it exists, reload it.
+  if (spec != (want > 0) || (spec && ck0 + kCK - 1 > klast)) {
+    ST_WAIT_VMCNT(0);
+    if (want > 0) chunk_dma<D, RWV>(ring, ring + kCK * D, kgp, vgp, ck0, klast, rw, lane);
+  }
+
+  // Q of the workgroup's rows (rows past the end repeat the last): staged in
+  // LDS once when several key groups share the rows, else loaded directly.
+  bf16x8 qf[RBW][NKS];
+  if constexpr (QLDS) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int RPI = 64 / CH, QI = ROWS * CH / 64;
+    for (int i = wave; i < QI; i += 4) {
+      const int row = i * RPI + lane / CH, pos = lane % CH;
+      const int rr = min(row0 + row, rows_b - 1);
+      const uint16_t* src = (const uint16_t*)a.q +
+                            ((size_t)(rq.lo + rr / a.G) * a.Hq + it.g * a.G + rr % a.G) * D +
+                            8 * (pos ^ kswz<D>(row));
+      __builtin_amdgcn_global_load_lds(src, ST_LDS_PTR(sQ + i * 512), 16, 0, 0);
+    }
+#endif
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      const int row = min(wrow0 + rb * 16 + r16, rows_b - 1);
+      const int node = row / a.G, hq = it.g * a.G + row % a.G;
+      const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(rq.lo + node) * a.Hq + hq) * D;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[rb][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * ks + 8 * grp));
+    }
+  }
 
   // Ancestor masks are needed only when the key range reaches tree keys: read
   // the workgroup's rows of `mask`, or (mask == null) the request's parent
@@ -439,27 +487,15 @@ attn_stream_kernel(AttnArgs a) {
       }
     }
   }
-  // Q^T fragments of this wavefront's rows (rows past the end repeat the last)
-  bf16x8 qf[RBW][NKS];
+  // the rest of the ring
 #pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) {
-    const int row = min(wrow0 + rb * 16 + r16, rows_b - 1);
-    const int node = row / a.G, hq = it.g * a.G + row % a.G;
-    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(rq.lo + node) * a.Hq + hq) * D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[rb][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * ks + 8 * grp));
-  }
-  // prime the ring
-#pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
+  for (int s = 1; s < PRIME; ++s)
     if (s < nmine)
       chunk_dma<D, RWV>(ring + s * STAGE, ring + s * STAGE + kCK * D, kgp, vgp,
                         k0 + (s * KWV + kg) * kCK, klast, rw, lane);
-  wait_chunks<NSTAGE - 1, DPC>(min(NSTAGE - 1, nmine));  // the q and mask loads are older
+  wait_chunks<PRIME - 1, DPC>(want - 1);  // Q, masks and the first chunk are older
   if (need_mask) {
     if (derive) {
-      int* sPar = (int*)(sMask + MWORDS);
       if (tid < rq.n) sPar[tid] = par;
       lds_barrier();
       if (tid < ROWS) {
@@ -480,7 +516,17 @@ attn_stream_kernel(AttnArgs a) {
       }
     }
   }
-  lds_barrier();
+  lds_barrier();  // Q (when staged) and the masks are in LDS
+  if constexpr (QLDS) {
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      const int r = rb * 16 + r16;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[rb][ks] = __builtin_bit_cast(
+            bf16x8, *(const u32x4*)(sQ + r * D + 8 * ((4 * ks + grp) ^ kswz<D>(r))));
+    }
+  }
 
   f32x4 acc[RBW][NDB];
   float m[RBW], l[RBW];
@@ -492,26 +538,49 @@ attn_stream_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const uint64_t* sMw = sMask + rw * WROWS * 4;
-  int stage = 0, refill = NSTAGE - 1;
-  for (int r = 0; r < niter; ++r) {
-    // chunk r is the oldest outstanding; up to NSTAGE - 2 newer ones stay in flight
-    wait_chunks<NSTAGE - 2, DPC>(min(NSTAGE - 2, nmine - r - 1));
-    if constexpr (RWV > 1) lds_barrier();  // every row group is done with chunk r - 1
-    __builtin_amdgcn_sched_barrier(0);
-    if (r + NSTAGE - 1 < nmine) {
-      uint16_t* sb = ring + refill * STAGE;
-      chunk_dma<D, RWV>(sb, sb + kCK * D, kgp, vgp, k0 + ((r + NSTAGE - 1) * KWV + kg) * kCK,
-                        klast, rw, lane);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (r < nmine) {
+  if constexpr (PRIVATE) {
+    // A ring of one's own: compute chunk r, then refill its stage with chunk
+    // r + NSTAGE; no other wavefront reads it, so no barrier is needed.
+    int stage = 0;
+    for (int r = 0; r < nmine; ++r) {
+      wait_chunks<NSTAGE - 1, DPC>(min(NSTAGE - 1, nmine - r - 1));
+      __builtin_amdgcn_sched_barrier(0);
       const uint16_t* sK = ring + stage * STAGE;
       chunk_compute<D, RBW>(sK, sK + kCK * D, sMw, k0 + (r * KWV + kg) * kCK, rq.P, k1,
                             a.scale_log2, r16, grp, qf, acc, m, l);
+      __builtin_amdgcn_sched_barrier(0);
+      if (r + NSTAGE < nmine) {
+        uint16_t* sb = ring + stage * STAGE;
+        chunk_dma<D, RWV>(sb, sb + kCK * D, kgp, vgp, k0 + ((r + NSTAGE) * KWV + kg) * kCK,
+                          klast, rw, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      stage = stage + 1 == NSTAGE ? 0 : stage + 1;
     }
-    __builtin_amdgcn_sched_barrier(0);
-    stage = stage + 1 == NSTAGE ? 0 : stage + 1;
-    refill = refill + 1 == NSTAGE ? 0 : refill + 1;
+  } else {
+    // A ring shared by the row groups of a key group: at the top of round r
+    // (after the barrier, so every row group is done with chunk r - 1) refill
+    // the stage chunk r - 1 used with chunk r + NSTAGE - 1.
+    int stage = 0, refill = NSTAGE - 1;
+    for (int r = 0; r < niter; ++r) {
+      wait_chunks<NSTAGE - 2, DPC>(min(NSTAGE - 2, nmine - r - 1));
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (r + NSTAGE - 1 < nmine) {
+        uint16_t* sb = ring + refill * STAGE;
+        chunk_dma<D, RWV>(sb, sb + kCK * D, kgp, vgp, k0 + ((r + NSTAGE - 1) * KWV + kg) * kCK,
+                          klast, rw, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (r < nmine) {
+        const uint16_t* sK = ring + stage * STAGE;
+        chunk_compute<D, RBW>(sK, sK + kCK * D, sMw, k0 + (r * KWV + kg) * kCK, rq.P, k1,
+                              a.scale_log2, r16, grp, qf, acc, m, l);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      stage = stage + 1 == NSTAGE ? 0 : stage + 1;
+      refill = refill + 1 == NSTAGE ? 0 : refill + 1;
+    }
   }
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {

@@ -1,7 +1,8 @@
 // Device body of the accepted-path KV compaction (the depth-first KV-cache
 // update of the SpecInfer news article, "Token 樹驗證器"): slot P + j of every
 // kv head takes what slot P + path[j] held before, for j = 0..L.  Shared by
-// st_kv_compact and by the combine launch of st_verification_step.
+// st_kv_compact and by the last launch of st_verification_step, where each
+// compaction workgroup can also run the greedy walk that yields the path.
 //
 // The copy is in place.  A path strictly increases (path[j] >= j), so the
 // source of a later move is never the destination of an earlier one.  One
@@ -10,7 +11,7 @@
 // of its destinations, so within a batch no source is overwritten before it
 // is read, and later batches read only slots no earlier move wrote.
 #pragma once
-#include "st_internal.h"
+#include "greedy_walk_dev.h"
 
 namespace st {
 
@@ -25,13 +26,16 @@ struct CompactArgs {
   int32_t* src_slot;
   int32_t* new_len;
   int32_t* status;
+  bool walk;            // take the path from a greedy walk run in the workgroup
+  GreedyWalkArgs g;     // ... with these inputs (the step's argmax partials)
 };
 
-// One workgroup (blockDim.x == 256): request b, cache row set y (< Hkv: keys
-// of head y, else values of head y - Hkv).
-__device__ inline void kv_compact_block(const CompactArgs& c, int b, int y) {
-  const int P = c.prefix_len[b], L = c.accept_len[b];
-  const int32_t* path = c.accept_nodes + (size_t)b * c.max_path;
+// Moves of one workgroup (blockDim.x == 256): request b, cache row set y
+// (< Hkv: keys of head y, else values of head y - Hkv), path[0..L] of the
+// accepted path (global or LDS).  Row set 0 also stores src_slot / new_len.
+__device__ inline void kv_compact_rows(const CompactArgs& c, int b, int y, int L,
+                                       const int* path) {
+  const int P = c.prefix_len[b];
   int bad = 0;
   if (L < 0 || L + 1 > c.max_path || P < 0) {
     bad = ST_STATUS_PATH_OVERFLOW;
@@ -61,6 +65,24 @@ __device__ inline void kv_compact_block(const CompactArgs& c, int b, int y) {
     if (move) rows[(size_t)(P + j) * c.chunks + col] = v;
     __syncthreads();
   }
+}
+
+// One compaction workgroup: the path comes from accept_len / accept_nodes,
+// or (c.walk) from the greedy walk that the first wavefront runs here; row
+// set 0's workgroup also stores the walk's outputs.
+__device__ inline void kv_compact_block(const CompactArgs& c, int b, int y) {
+  if (!c.walk) {
+    kv_compact_rows(c, b, y, c.accept_len[b], c.accept_nodes + (size_t)b * c.max_path);
+    return;
+  }
+  __shared__ GreedyWalkLds s;
+  __shared__ int sL;
+  if (threadIdx.x < ST_WAVE) {
+    const int L = greedy_walk_wave(c.g, b, s, y == 0);
+    if (threadIdx.x == 0) sL = L;
+  }
+  __syncthreads();
+  kv_compact_rows(c, b, y, sL, s.path);
 }
 
 }  // namespace st

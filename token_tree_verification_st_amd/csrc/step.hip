@@ -1,5 +1,6 @@
 // st_verification_step: acceptance, attention with in-kernel ancestor masks,
-// then the split merge and the KV compaction in one launch.
+// then the split merge and the KV compaction in one launch (for greedy
+// acceptance the tree walk runs inside the compaction workgroups).
 #include "step_internal.h"
 
 #include <math.h>
@@ -49,13 +50,20 @@ extern "C" int st_verification_step(const st_tree* tree, const st_step* s, void*
                              s->src_slot, s->new_len, status, c);
   if (rc) return rc;
 
-  if (s->draft_logits)
+  // Greedy: only the vocab argmax goes first; each compaction workgroup of the
+  // last launch walks its request's tree itself (a few microseconds of
+  // latency-bound work that then needs no launch of its own).  Stochastic:
+  // both acceptance kernels go first.
+  if (s->draft_logits) {
     rc = st_verify_stochastic(tree, s->V, s->tokens, s->logits, s->draft_logits, s->temperature,
                               s->seed, s->offset, s->accept_len, s->accept_nodes, s->out_tokens,
                               s->near_ties, workspace, vws, status, stream);
-  else
-    rc = st_verify_greedy(tree, s->V, s->tokens, s->logits, s->accept_len, s->accept_nodes,
-                          s->out_tokens, workspace, vws, status, stream);
+  } else {
+    rc = st::greedy_argmax_only(tree, s->V, s->tokens, s->logits, s->accept_len,
+                                s->accept_nodes, s->out_tokens, workspace, vws, status, stream,
+                                c.g);
+    c.walk = true;
+  }
   if (rc) return rc;
   return st::tree_attention_impl(tree, s->Hq, s->Hkv, s->D, s->dtype, s->scale, s->q,
                                  s->k_cache, s->v_cache, s->S_max, s->prefix_len, s->max_prefix,

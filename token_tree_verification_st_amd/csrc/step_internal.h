@@ -5,6 +5,14 @@
 
 namespace st {
 
+// st_verify_greedy without its walk: checks the arguments, launches the
+// vocab argmax and fills the walk's inputs, for the walk to run in the
+// compaction workgroups of the last launch (verify.hip).
+int greedy_argmax_only(const st_tree* tree, int V, const int32_t* tokens, const float* logits,
+                       int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                       void* workspace, size_t ws_bytes, int32_t* status, void* stream,
+                       GreedyWalkArgs& walk);
+
 // Checks the arguments of st_kv_compact and fills CompactArgs (compact.hip).
 int fill_compact_args(int B, int Hkv, int D, st_dtype dtype, void* k_cache, void* v_cache,
                       int S_max, const int32_t* prefix_len, const int32_t* accept_len,

@@ -18,7 +18,7 @@
 // spending one vocab reduction per rejection.  A second kernel walks each
 // request's tree through those per-node verdicts and draws the replacement
 // token at the stop node by inverse CDF.
-#include "st_internal.h"
+#include "step_internal.h"
 
 #include <float.h>
 #include <limits.h>
@@ -60,24 +60,15 @@ struct SumOp {
   __device__ T operator()(T a, T b) const { return a + b; }
 };
 
-// (value, index) argmax with the lowest index on equal values; NaN never wins.
-__device__ inline void argmax_merge(float& v, int& i, float v2, int i2) {
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
-}
+using st::argmax_merge;
+using st::ArgmaxPart;
+using st::kMaxPath;
 
 // ---------------------------------------------------------------- greedy
 
 constexpr int kArgmaxBlock = 256;
 constexpr int kArgmaxPerThread = 32;                          // logits per thread
 constexpr int kArgmaxSlice = kArgmaxBlock * kArgmaxPerThread;  // vocab entries per workgroup
-
-struct ArgmaxPart {
-  float v;
-  int i;
-};
 
 // Workgroup (t, slice) reduces logits[t][slice*8192 .. +8192) to its maximum
 // and lowest index; all of a thread's loads are issued before any is used.
@@ -171,79 +162,18 @@ __device__ inline void write_path_outputs(int b, int L, int max_depth, const int
                                           const int32_t* tokens, int lo, int last_token,
                                           int32_t* accept_len, int32_t* accept_nodes,
                                           int32_t* out_tokens) {
-  const int mp = max_depth + 1;
-  for (int j = threadIdx.x; j <= mp; j += blockDim.x) {
-    if (j < mp) accept_nodes[(size_t)b * mp + j] = j <= L ? path[j] : -1;
-    int tok = -1;
-    if (j < L) tok = tokens[lo + path[j + 1]];
-    else if (j == L) tok = last_token;
-    out_tokens[(size_t)b * (mp + 1) + j] = tok;
-  }
-  if (threadIdx.x == 0) accept_len[b] = L;
+  st::write_path_outputs(threadIdx.x, blockDim.x, b, L, max_depth, path, tokens, lo, last_token,
+                         accept_len, accept_nodes, out_tokens);
 }
 
-constexpr int kMaxPath = ST_MAX_NODES;
 
 // One wavefront per request: the request's parents, tokens and merged argmax
 // are staged in LDS, then the walk moves from node to node with the lowest
 // matching child found by a ballot over the wavefront.
 __global__ void __launch_bounds__(ST_WAVE)
-greedy_walk_kernel(const int32_t* __restrict__ node_off, const int32_t* __restrict__ parent,
-                   const int32_t* __restrict__ tokens, const ArgmaxPart* __restrict__ part,
-                   int nslices, int T, int V, int max_nodes, int max_depth,
-                   int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
-                   int32_t* status) {
-  __shared__ int path[kMaxPath + 1];
-  __shared__ int sp[ST_MAX_NODES], stok[ST_MAX_NODES], sa[ST_MAX_NODES];
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const int lo = node_off[b], hi = node_off[b + 1], n = hi - lo;
-  if (lo < 0 || hi > T || n < 1 || n > max_nodes) {
-    if (lane == 0) st::set_status(status, ST_STATUS_BAD_PARENT);
-    return;
-  }
-  int bits = 0;
-  for (int i = lane; i < n; i += ST_WAVE) {
-    const int p = parent[lo + i], tok = tokens[lo + i];
-    sp[i] = p;
-    stok[i] = tok;
-    if (i == 0 ? (p != -1) : (p < 0 || p >= i)) bits |= ST_STATUS_BAD_PARENT;
-    if (i > 0 && (tok < 0 || tok >= V)) bits |= ST_STATUS_BAD_TOKEN;
-    const ArgmaxPart* pp = part + (size_t)(lo + i) * nslices;
-    float bv = pp[0].v;
-    int bi = pp[0].i;
-    for (int k = 1; k < nslices; ++k) argmax_merge(bv, bi, pp[k].v, pp[k].i);
-    sa[i] = (bi == INT_MAX) ? 0 : bi;
-  }
-  for (int o = 32; o > 0; o >>= 1) bits |= __shfl_xor(bits, o, ST_WAVE);
-  if (lane == 0) st::set_status(status, bits);
-  __syncthreads();
-
-  int u = 0, L = 0;
-  bool overflow = false;
-  if (lane == 0) path[0] = 0;
-  while (true) {
-    const int a = sa[u];
-    int found = -1;
-    // children of u have larger indices; the lowest matching index wins
-    for (int c0 = u + 1; c0 < n && found < 0; c0 += ST_WAVE) {
-      const int c = c0 + lane;
-      const bool hit = c < n && sp[c] == u && stok[c] == a;
-      const uint64_t m = __ballot(hit);
-      if (m) found = c0 + __ffsll((unsigned long long)m) - 1;
-    }
-    if (found < 0) break;
-    if (L == max_depth) {
-      overflow = true;
-      break;
-    }
-    ++L;
-    if (lane == 0) path[L] = found;
-    u = found;
-  }
-  __syncthreads();
-  if (overflow && lane == 0) st::set_status(status, ST_STATUS_PATH_OVERFLOW);
-  write_path_outputs(b, L, max_depth, path, tokens, lo, overflow ? -1 : sa[u], accept_len,
-                     accept_nodes, out_tokens);
+greedy_walk_kernel(st::GreedyWalkArgs g) {
+  __shared__ st::GreedyWalkLds s;
+  st::greedy_walk_wave(g, blockIdx.x, s, true);
 }
 
 // ---------------------------------------------------------------- Philox4x64-10
@@ -544,10 +474,10 @@ extern "C" size_t st_verify_greedy_workspace(const st_tree* tree, int V) {
   return st::align_up((size_t)tree->total_nodes * argmax_slices(V) * sizeof(ArgmaxPart), 256);
 }
 
-extern "C" int st_verify_greedy(const st_tree* tree, int V, const int32_t* tokens,
-                                const float* logits, int32_t* accept_len, int32_t* accept_nodes,
-                                int32_t* out_tokens, void* workspace, size_t ws_bytes,
-                                int32_t* status, void* stream) {
+int st::greedy_argmax_only(const st_tree* tree, int V, const int32_t* tokens,
+                           const float* logits, int32_t* accept_len, int32_t* accept_nodes,
+                           int32_t* out_tokens, void* workspace, size_t ws_bytes,
+                           int32_t* status, void* stream, st::GreedyWalkArgs& g) {
   int rc = st::check_tree_host(tree);
   if (rc) return rc;
   if (V < 1 || !tokens || !logits || !accept_len || !accept_nodes || !out_tokens || !workspace)
@@ -556,13 +486,23 @@ extern "C" int st_verify_greedy(const st_tree* tree, int V, const int32_t* token
   if (ws_bytes < st_verify_greedy_workspace(tree, V)) return ST_E_WORKSPACE;
   ArgmaxPart* part = (ArgmaxPart*)workspace;
   const int ns = argmax_slices(V);
-  hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(row_argmax_kernel, dim3(tree->total_nodes, ns), dim3(kArgmaxBlock), 0, s,
-                     logits, V, part, status);
-  if ((rc = st::check_launch())) return rc;
-  hipLaunchKernelGGL(greedy_walk_kernel, dim3(tree->B), dim3(ST_WAVE), 0, s, tree->node_off,
-                     tree->parent, tokens, part, ns, tree->total_nodes, V, tree->max_nodes,
-                     tree->max_depth, accept_len, accept_nodes, out_tokens, status);
+  hipLaunchKernelGGL(row_argmax_kernel, dim3(tree->total_nodes, ns), dim3(kArgmaxBlock), 0,
+                     (hipStream_t)stream, logits, V, part, status);
+  g = st::GreedyWalkArgs{tree->node_off, tree->parent, tokens, part, ns,
+                         tree->total_nodes, V, tree->max_nodes, tree->max_depth,
+                         accept_len, accept_nodes, out_tokens, status};
+  return st::check_launch();
+}
+
+extern "C" int st_verify_greedy(const st_tree* tree, int V, const int32_t* tokens,
+                                const float* logits, int32_t* accept_len, int32_t* accept_nodes,
+                                int32_t* out_tokens, void* workspace, size_t ws_bytes,
+                                int32_t* status, void* stream) {
+  st::GreedyWalkArgs g;
+  const int rc = st::greedy_argmax_only(tree, V, tokens, logits, accept_len, accept_nodes,
+                                        out_tokens, workspace, ws_bytes, status, stream, g);
+  if (rc) return rc;
+  hipLaunchKernelGGL(greedy_walk_kernel, dim3(tree->B), dim3(ST_WAVE), 0, (hipStream_t)stream, g);
   return st::check_launch();
 }
 
