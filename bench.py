@@ -40,7 +40,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of a graph")
     ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per attention launch")
+                    help="traffic summary (default profiles/attention_<workload>_traffic.md); "
+                         "used only if it was taken from the current attention sources")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -168,16 +171,23 @@ def main():
     for c in calls:
         _, ms = timed_replay(capture(fns[c]))
         per_call[c] = ms / K * 1e3  # us per launch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     st_words = [int(r.buf["status"].item()) for r in reps]
     assert not any(st_words), f"device status {st_words}"
 
     attn_bytes = algorithmic_attention_bytes(wl)
     attn_us = per_call["attention"]
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    from token_tree_verification_st_amd.profiling import read_traffic
+    traffic = read_traffic(args.traffic or os.path.join(
+        ROOT, "profiles", f"attention_{wl.name}_traffic.md"))
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "st_tree_attention", "algorithmic_bytes": attn_bytes,

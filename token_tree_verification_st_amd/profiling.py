@@ -1,0 +1,127 @@
+"""Summaries of rocprofv3 output for profiles/ (host-side text processing).
+
+    python -m token_tree_verification_st_amd.profiling stats   STATS_CSV OUT.md TITLE COMMAND
+    python -m token_tree_verification_st_amd.profiling traffic FETCH_CSV WRITE_CSV COPY_BYTES \\
+        WORKLOAD OUT.md COMMAND_FETCH COMMAND_WRITE
+
+`traffic` reads two --pmc runs of the same bench command (FETCH_SIZE, then
+WRITE_SIZE, KiB per dispatch).  Each counter is scaled by what it reads for
+the plain device copy of COPY_BYTES that `bench.py --copy-calibration` runs in
+the same process, and the per-call HBM bytes of st_tree_attention (streaming
+kernel + split merge) are written with the hash of the attention sources, so
+bench.py can tell whether the figure still describes the built kernel.
+"""
+
+from __future__ import annotations
+
+import csv
+import hashlib
+import os
+import re
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ATTENTION_SOURCES = ("csrc/attention.hip", "csrc/st_internal.h", "csrc/step_internal.h",
+                     "csrc/kv_compact_dev.h", "csrc/greedy_walk_dev.h", "build.py")
+ATTENTION_KERNELS = ("attn_stream_kernel", "attn_valu_kernel", "attn_combine_kernel<")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def attention_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ATTENTION_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "")
+    n = re.sub(r"^void ", "", n)
+    return n.split("(")[0]
+
+
+def stats_md(stats_csv: str, title: str, command: str) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = [f"# {title}", "", "Command (run from /tmp with TMPDIR=/tmp; $R = repository root):", "",
+           "```", command, "```", "",
+           "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    return "\n".join(out) + "\n"
+
+
+def _per_dispatch(counter_csv: str, counter: str):
+    """Per kernel name: (mean counter value in KiB over its dispatches, number
+    of dispatches, largest single value)."""
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(counter_csv)):
+        if r["Counter_Name"] == counter:
+            vals[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v), max(v)) for k, v in vals.items()}
+
+
+def traffic(fetch_csv: str, write_csv: str, copy_bytes: int):
+    f = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    w = _per_dispatch(write_csv, "WRITE_SIZE")
+    if COPY_KERNEL not in f or COPY_KERNEL not in w:
+        raise SystemExit("the calibration copy is missing from the counter runs")
+    # the calibration copy is the largest copy dispatch of the run
+    f_scale = copy_bytes / (f[COPY_KERNEL][2] * 1024.0)
+    w_scale = copy_bytes / (w[COPY_KERNEL][2] * 1024.0)
+    per_kernel = {}
+    for k in sorted(set(f) | set(w)):
+        if any(k.startswith(p.rstrip("<")) for p in ATTENTION_KERNELS) and \
+                ("combine_compact" not in k):
+            fb = f.get(k, (0.0, 0, 0.0))[0] * 1024.0 * f_scale
+            wb = w.get(k, (0.0, 0, 0.0))[0] * 1024.0 * w_scale
+            per_kernel[k] = (fb, wb, f.get(k, (0, 0, 0))[1])
+    return f_scale, w_scale, per_kernel
+
+
+def traffic_md(fetch_csv, write_csv, copy_bytes, workload, cmd_f, cmd_w):
+    f_scale, w_scale, per_kernel = traffic(fetch_csv, write_csv, copy_bytes)
+    total = sum(fb + wb for fb, wb, _ in per_kernel.values())
+    out = [f"# st_tree_attention HBM traffic, workload {workload}", "",
+           "Commands (run from /tmp with TMPDIR=/tmp; $R = repository root):", "",
+           "```", cmd_f, cmd_w, "```", "",
+           f"Calibration: a device copy of {copy_bytes} bytes in the same process reads "
+           f"FETCH_SIZE x {f_scale:.3f} and WRITE_SIZE x {w_scale:.3f} of its true bytes.", "",
+           "| kernel | dispatches | fetch bytes | write bytes |", "|---|---|---|---|"]
+    for k, (fb, wb, n) in per_kernel.items():
+        out.append(f"| {k} | {n} | {fb:.0f} | {wb:.0f} |")
+    out += ["", "Machine-readable (read by bench.py):", "",
+            f"source_sha256: {attention_source_hash()}",
+            f"bytes_per_launch: {total:.0f}", ""]
+    return "\n".join(out)
+
+
+def read_traffic(path: str):
+    """bytes_per_launch from a traffic summary, or None when the summary is
+    missing or was taken from different attention sources."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"^source_sha256: (\w+)", text, re.M)
+    b = re.search(r"^bytes_per_launch: (\d+)", text, re.M)
+    if not h or not b or h.group(1) != attention_source_hash():
+        return None
+    return int(b.group(1))
+
+
+def main(argv):
+    if argv[0] == "stats":
+        stats_csv, out, title, command = argv[1:5]
+        open(out, "w").write(stats_md(stats_csv, title, command))
+    elif argv[0] == "traffic":
+        fcsv, wcsv, copy_bytes, workload, out, cmd_f, cmd_w = argv[1:8]
+        open(out, "w").write(traffic_md(fcsv, wcsv, int(copy_bytes), workload, cmd_f, cmd_w))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
