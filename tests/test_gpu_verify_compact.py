@@ -283,3 +283,29 @@ def test_one_call_step_compaction_with_long_paths(monkeypatch):
         assert np.array_equal(b.v_cache.cpu().view(torch.int16).numpy().view(np.uint16), vn)
         assert torch.equal(a.k_cache, b.k_cache) and torch.equal(a.buf["out"], b.buf["out"])
         assert status_of(b) == 0
+
+
+def test_one_call_step_argmax_in_attention_with_idle_workgroups():
+    """Greedy bf16 step whose argmax slices are reduced by the attention
+    workgroups, including those whose split lies past a short request's keys
+    and that leave early: acceptance equals the oracle and the separate calls."""
+    rng = np.random.default_rng(21)
+    trees = [tree_random_attach(rng, 30, 6), tree_chain(5), tree_random_attach(rng, 40, 8)]
+    wl = build_workload("amfuse", rng, dtype="bf16", Hq=4, Hkv=2, D=128, V=5000,
+                        prefix_lens=[3000, 7, 1200], trees=trees, max_depth=8,
+                        token_rule="plant_leaf_path", logit_sigma=2.0)
+    a, b = to_device(wl), to_device(wl)
+    stp.verification_step(a, fused=False)
+    stp.verification_step(b, fused=True)
+    torch.cuda.synchronize()
+    res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.V, wl.max_depth)
+    _assert_paths_equal(res, device_paths(b))
+    for k in ("accept_len", "accept_nodes", "out_tokens", "src_slot", "new_len", "status"):
+        assert torch.equal(a.buf[k], b.buf[k]), k
+    assert torch.equal(a.k_cache, b.k_cache) and torch.equal(a.buf["out"], b.buf["out"])
+    # a non-finite logit is still reported from inside the attention launch
+    wl.logits[17, 123] = np.inf
+    c = to_device(wl)
+    stp.verification_step(c, fused=True)
+    torch.cuda.synchronize()
+    assert status_of(c) & 4

@@ -54,6 +54,7 @@ struct AttnArgs {
   float2* ws_ml;   // [NS][T*Hq] (m in log2 units, l)
   float* ws_acc;   // [NS][T*Hq][D]
   int32_t* status;
+  st::ArgmaxJob am;  // vocab argmax slices reduced in the prologue (am.logits null: none)
   int B, T, Hq, Hkv, G, S_max, W, max_nodes, max_prefix;
   int KS;          // keys per split (multiple of 16)
   int NS;          // splits of the longest request
@@ -65,7 +66,7 @@ struct AttnArgs {
 };
 
 struct Item {
-  int b, g, split, rblk;
+  int w, b, g, split, rblk;
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8).  Item w
@@ -75,6 +76,7 @@ __device__ inline bool decode_item(const AttnArgs& a, Item& it) {
   const int bid = blockIdx.x;
   int w = (bid & 7) * a.per_xcd + (bid >> 3);
   if (w >= a.items) return false;
+  it.w = w;
   it.rblk = w % a.n_rblk;
   w /= a.n_rblk;
   it.split = w % a.NS;
@@ -84,22 +86,44 @@ __device__ inline bool decode_item(const AttnArgs& a, Item& it) {
   return true;
 }
 
+// The argmax slice of workgroup w (units never exceed the workgroups; V is a
+// multiple of 4): loads issued at the start of the kernel, reduced once the
+// prologue's own loads have been waited for.
+__device__ inline void argmax_unit_finish(const AttnArgs& a, int w, const st::ArgmaxRegs& r,
+                                          int* scratch) {
+  const st::ArgmaxJob& j = a.am;
+  st::argmax_slice_finish<true>(r, j.V, w / j.nslices, w % j.nslices, j.nslices, j.part,
+                                j.status, scratch);
+}
+
 struct ReqInfo {
   int lo, n, P, key_end, nsplit;
   bool ok;
 };
 
-__device__ inline ReqInfo request_info(const AttnArgs& a, int b) {
+// The request's sizes.  The three loads are independent of each other and
+// the checks use no branches, so all three are in flight together.
+struct ReqWords {
+  int lo, hi, P;
+};
+__device__ inline ReqWords request_load(const AttnArgs& a, int b) {
+  return ReqWords{a.node_off[b], a.node_off[b + 1], a.prefix_len[b]};
+}
+
+__device__ inline ReqInfo request_finish(const AttnArgs& a, ReqWords w) {
   ReqInfo r;
-  r.lo = a.node_off[b];
-  const int hi = a.node_off[b + 1];
-  r.n = hi - r.lo;
-  r.P = a.prefix_len[b];
-  r.ok = r.lo >= 0 && hi <= a.T && r.n >= 1 && r.n <= a.max_nodes && r.P >= 0 &&
-         r.P <= a.max_prefix && r.P + r.n <= a.S_max;
-  r.key_end = r.P + r.n;
+  r.lo = w.lo;
+  r.n = w.hi - w.lo;
+  r.P = w.P;
+  r.ok = (w.lo >= 0) & (w.hi <= a.T) & (r.n >= 1) & (r.n <= a.max_nodes) & (w.P >= 0) &
+         (w.P <= a.max_prefix) & (w.P + r.n <= a.S_max);
+  r.key_end = w.P + r.n;
   r.nsplit = (r.key_end + a.KS - 1) / a.KS;
   return r;
+}
+
+__device__ inline ReqInfo request_info(const AttnArgs& a, int b) {
+  return request_finish(a, request_load(a, b));
 }
 
 __device__ inline bool tree_bit(uint64_t w0, uint64_t w1, uint64_t w2, uint64_t w3, int j) {
@@ -407,22 +431,21 @@ attn_stream_kernel(AttnArgs a) {
   const uint16_t* kgp = (const uint16_t*)a.k + head_off;
   const uint16_t* vgp = (const uint16_t*)a.v + head_off;
   uint16_t* ring = (uint16_t*)lds + kg * NSTAGE * STAGE;
-
-  // Start streaming before the request's sizes are known: the first chunk of
-  // this key group, with rows clamped to the split's nominal end and to the
-  // head's S_max slots (always inside the cache).  It is checked below.
-  const int klast_spec = min(k0 + a.KS, a.S_max) - 1;
-  const int ck0 = k0 + kg * kCK;
-  const bool spec = ck0 <= klast_spec;
-  if (spec) chunk_dma<D, RWV>(ring, ring + kCK * D, kgp, vgp, ck0, klast_spec, rw, lane);
+  // (the argmax reduction borrows the parent-array words of LDS before the
+  // masks are built; a second LDS object would cost the ring's prefetch: the
+  // compiler then waits for every direct load before each LDS read)
+  int* am_scratch = sPar;
+  const bool am = a.am.logits != nullptr && it.w < a.am.units;
+  st::ArgmaxRegs amr;
+  if (am) st::argmax_slice_load<true>(a.am.logits, a.am.V, it.w / a.am.nslices, it.w % a.am.nslices, amr);
 
   const ReqInfo rq = request_info(a, it.b);
   const int rows_b = rq.n * a.G;
   const int row0 = it.rblk * ROWS;
   if (!rq.ok || row0 >= rows_b || k0 >= rq.key_end) {
-    ST_WAIT_VMCNT(0);  // no direct load may land in LDS after the workgroup has left
     if (!rq.ok && threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
       st::set_status(a.status, ST_STATUS_BAD_PREFIX);
+    if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
     return;
   }
   const int k1 = min(k0 + a.KS, rq.key_end);
@@ -432,12 +455,8 @@ attn_stream_kernel(AttnArgs a) {
   const int nmine = (nch - kg + KWV - 1) / KWV;  // chunks kg, kg + KWV, ...
   const int niter = (nch + KWV - 1) / KWV;       // the same for every wavefront
   const int want = min(PRIME, nmine);
-  // The first chunk was right if it exists and ends inside the range (its rows
-  // were then not clamped); otherwise drain it and, if it exists, reload it.
-  if (spec != (want > 0) || (spec && ck0 + kCK - 1 > klast)) {
-    ST_WAIT_VMCNT(0);
-    if (want > 0) chunk_dma<D, RWV>(ring, ring + kCK * D, kgp, vgp, ck0, klast, rw, lane);
-  }
+  // the first chunk goes first, then Q and the masks, then the rest of the ring
+  if (nmine > 0) chunk_dma<D, RWV>(ring, ring + kCK * D, kgp, vgp, k0 + kg * kCK, klast, rw, lane);
 
   // Q of the workgroup's rows (rows past the end repeat the last): staged in
   // LDS once when several key groups share the rows, else loaded directly.
@@ -487,13 +506,13 @@ attn_stream_kernel(AttnArgs a) {
       }
     }
   }
-  // the rest of the ring
 #pragma unroll
   for (int s = 1; s < PRIME; ++s)
     if (s < nmine)
       chunk_dma<D, RWV>(ring + s * STAGE, ring + s * STAGE + kCK * D, kgp, vgp,
                         k0 + (s * KWV + kg) * kCK, klast, rw, lane);
-  wait_chunks<PRIME - 1, DPC>(want - 1);  // Q, masks and the first chunk are older
+  wait_chunks<PRIME - 1, DPC>(want - 1);  // the first chunk, Q and the masks are older
+  if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
   if (need_mask) {
     if (derive) {
       if (tid < rq.n) sPar[tid] = par;
@@ -968,6 +987,13 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
 
 }  // namespace
 
+int st::attention_workgroups(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype,
+                             int max_prefix) {
+  Plan p;
+  if (make_plan(tree, Hq, Hkv, D, dtype, max_prefix, p)) return 0;
+  return p.items;
+}
+
 extern "C" size_t st_tree_attention_workspace(const st_tree* tree, int Hq, int Hkv, int D,
                                               st_dtype dtype, int max_prefix) {
   Plan p;
@@ -980,7 +1006,7 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
                             int S_max, const int32_t* prefix_len, int max_prefix,
                             const uint64_t* mask, void* out, float* lse, void* workspace,
                             size_t ws_bytes, int32_t* status, void* stream,
-                            const st::CompactArgs* compact) {
+                            const st::CompactArgs* compact, const st::ArgmaxJob* argmax) {
   Plan p;
   int rc = make_plan(tree, Hq, Hkv, D, dtype, max_prefix, p);
   if (rc) return rc;
@@ -1019,6 +1045,8 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
   a.items = p.items;
   a.per_xcd = p.per_xcd;
   a.scale_log2 = scale * kLog2e;
+  a.am = st::ArgmaxJob{nullptr, nullptr, 0, 0, 0, nullptr};
+  if (argmax && p.stream) a.am = *argmax;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(8 * p.per_xcd), block(256);
   if (p.stream) {
@@ -1081,5 +1109,5 @@ extern "C" int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st
                                  void* stream) {
   return st::tree_attention_impl(tree, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, S_max,
                                  prefix_len, max_prefix, mask, out, lse, workspace, ws_bytes,
-                                 status, stream, nullptr);
+                                 status, stream, nullptr, nullptr);
 }

@@ -22,6 +22,99 @@ __device__ inline void argmax_merge(float& v, int& i, float v2, int i2) {
 
 constexpr int kMaxPath = ST_MAX_NODES;
 
+// ---------------------------------------------------------------- vocab argmax
+
+// A workgroup of kArgmaxBlock threads reduces one 8192-entry slice of one
+// logits row to its maximum and lowest index.  Loading and reducing are split
+// so that a caller can keep the loads in flight while it does other work.
+constexpr int kArgmaxBlock = 256;
+constexpr int kArgmaxPerThread = 32;                          // logits per thread
+constexpr int kArgmaxSlice = kArgmaxBlock * kArgmaxPerThread;  // vocab entries per slice
+
+typedef float am_f32x4 __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline int argmax_slices(int V) { return (V + kArgmaxSlice - 1) / kArgmaxSlice; }
+
+struct ArgmaxRegs {
+  am_f32x4 x[kArgmaxPerThread / 4];
+};
+
+// Every load of this thread's 32 entries of slice `slice` of row t, issued up
+// front (16-byte non-temporal loads when VEC: V is a multiple of 4).
+template <bool VEC>
+__device__ inline void argmax_slice_load(const float* logits, int V, int t, int slice,
+                                         ArgmaxRegs& r) {
+  const float* row = logits + (size_t)t * V;
+  const int base = slice * kArgmaxSlice;
+  const int tid = threadIdx.x;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int k = 0; k < kArgmaxPerThread / 4; ++k) {
+      const int v = base + 4 * (tid + k * kArgmaxBlock);
+      r.x[k] = v < V ? __builtin_nontemporal_load((const am_f32x4*)(row + v))
+                     : am_f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kArgmaxPerThread; ++k) {
+      const int v = base + tid + k * kArgmaxBlock;
+      r.x[k / 4][k % 4] = v < V ? row[v] : -INFINITY;
+    }
+  }
+}
+
+// Reduce the loaded entries over the workgroup (all kArgmaxBlock threads call
+// it) and store the slice's (max, lowest index); a NaN or infinite logit sets
+// ST_STATUS_NONFINITE.  `scratch` is 2 * (kArgmaxBlock / 64) + 1 words of LDS.
+template <bool VEC>
+__device__ inline void argmax_slice_finish(const ArgmaxRegs& r, int V, int t, int slice,
+                                           int nslices, ArgmaxPart* part, int32_t* status,
+                                           int* scratch) {
+  const int base = slice * kArgmaxSlice;
+  const int tid = threadIdx.x;
+  float best = -INFINITY;
+  int bidx = INT_MAX;
+  bool finite = true;
+#pragma unroll
+  for (int k = 0; k < kArgmaxPerThread / 4; ++k) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = VEC ? base + 4 * (tid + k * kArgmaxBlock) + j
+                        : base + tid + (4 * k + j) * kArgmaxBlock;
+      if (v < V) {
+        const float x = r.x[k][j];
+        finite = finite && isfinite(x);
+        argmax_merge(best, bidx, x, v);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(best, o, ST_WAVE);
+    const int i2 = __shfl_xor(bidx, o, ST_WAVE);
+    argmax_merge(best, bidx, v2, i2);
+  }
+  constexpr int NW = kArgmaxBlock / ST_WAVE;
+  float* sv = (float*)scratch;
+  int* si = scratch + NW;
+  int* sf = scratch + 2 * NW;
+  if (tid == 0) *sf = 1;
+  __syncthreads();
+  const int w = tid / ST_WAVE;
+  if (tid % ST_WAVE == 0) {
+    sv[w] = best;
+    si[w] = bidx;
+  }
+  if (!finite) *sf = 0;
+  __syncthreads();
+  if (tid == 0) {
+    for (int k = 1; k < NW; ++k) argmax_merge(best, bidx, sv[k], si[k]);
+    part[(size_t)t * nslices + slice] = ArgmaxPart{best, bidx};
+    if (!*sf) set_status(status, ST_STATUS_NONFINITE);
+  }
+  __syncthreads();  // the scratch words may be reused right after
+}
+
 // accept_nodes / out_tokens / accept_len of request b, written by threads
 // tid = 0..nthreads-1.
 __device__ inline void write_path_outputs(int tid, int nthreads, int b, int L, int max_depth,

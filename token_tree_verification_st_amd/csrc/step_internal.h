@@ -5,13 +5,23 @@
 
 namespace st {
 
-// st_verify_greedy without its walk: checks the arguments, launches the
-// vocab argmax and fills the walk's inputs, for the walk to run in the
-// compaction workgroups of the last launch (verify.hip).
-int greedy_argmax_only(const st_tree* tree, int V, const int32_t* tokens, const float* logits,
-                       int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
-                       void* workspace, size_t ws_bytes, int32_t* status, void* stream,
-                       GreedyWalkArgs& walk);
+// st_verify_greedy in parts (verify.hip): check the arguments and fill the
+// walk's inputs (the argmax partials go to the start of `workspace`), launch
+// the vocab argmax.  The one-call step runs the argmax inside the attention
+// launch instead when it can, and the walk in its compaction workgroups.
+int greedy_prepare(const st_tree* tree, int V, const int32_t* tokens, const float* logits,
+                   int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                   void* workspace, size_t ws_bytes, int32_t* status, GreedyWalkArgs& walk);
+int greedy_argmax_launch(const GreedyWalkArgs& walk, const float* logits, void* stream);
+
+// Vocab argmax slices handed to the attention launch: its workgroups load them
+// while their first K/V chunk is in flight and reduce them before their loop.
+struct ArgmaxJob {
+  const float* logits;
+  ArgmaxPart* part;
+  int V, nslices, units;  // units = rows * nslices
+  int32_t* status;
+};
 
 // Checks the arguments of st_kv_compact and fills CompactArgs (compact.hip).
 int fill_compact_args(int B, int Hkv, int D, st_dtype dtype, void* k_cache, void* v_cache,
@@ -21,12 +31,19 @@ int fill_compact_args(int B, int Hkv, int D, st_dtype dtype, void* k_cache, void
 
 // st_tree_attention; with `compact` set, the launch that merges the splits
 // also moves the accepted paths' KV rows (after the attention kernel has read
-// them), or a compaction launch follows when there is nothing to merge
+// them), or a compaction launch follows when there is nothing to merge; with
+// `argmax` set, the streaming kernel's workgroups also reduce those argmax
+// slices (the fp32 kernel does not: the slices are then launched first)
 // (attention.hip).
 int tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype, float scale,
                         const void* q, const void* k_cache, const void* v_cache, int S_max,
                         const int32_t* prefix_len, int max_prefix, const uint64_t* mask,
                         void* out, float* lse, void* workspace, size_t ws_bytes, int32_t* status,
-                        void* stream, const CompactArgs* compact);
+                        void* stream, const CompactArgs* compact,
+                        const ArgmaxJob* argmax = nullptr);
+
+// Work items (workgroups with work) of the attention plan for these sizes.
+int attention_workgroups(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype,
+                         int max_prefix);
 
 }  // namespace st

@@ -66,80 +66,22 @@ using st::kMaxPath;
 
 // ---------------------------------------------------------------- greedy
 
-constexpr int kArgmaxBlock = 256;
-constexpr int kArgmaxPerThread = 32;                          // logits per thread
-constexpr int kArgmaxSlice = kArgmaxBlock * kArgmaxPerThread;  // vocab entries per workgroup
+using st::kArgmaxBlock;
+using st::kArgmaxSlice;
 
 // Workgroup (t, slice) reduces logits[t][slice*8192 .. +8192) to its maximum
 // and lowest index; all of a thread's loads are issued before any is used.
 __global__ void __launch_bounds__(kArgmaxBlock)
 row_argmax_kernel(const float* __restrict__ logits, int V, ArgmaxPart* __restrict__ part,
                   int32_t* status) {
-  const int t = blockIdx.x, slice = blockIdx.y, nslices = gridDim.y;
-  const float* row = logits + (size_t)t * V;
-  const int base = slice * kArgmaxSlice;
-  float best = -INFINITY;
-  int bidx = INT_MAX;
-  bool finite = true;
+  __shared__ int scratch[2 * (kArgmaxBlock / ST_WAVE) + 1];
+  st::ArgmaxRegs r;
   if ((V & 3) == 0) {
-    constexpr int N4 = kArgmaxPerThread / 4;
-    f32x4 x[N4];
-#pragma unroll
-    for (int k = 0; k < N4; ++k) {
-      const int v = base + 4 * (threadIdx.x + k * kArgmaxBlock);
-      x[k] = v < V ? __builtin_nontemporal_load((const f32x4*)(row + v))
-                   : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    }
-#pragma unroll
-    for (int k = 0; k < N4; ++k) {
-      const int v = base + 4 * (threadIdx.x + k * kArgmaxBlock);
-      if (v < V) {
-        finite = finite && isfinite(x[k].x) && isfinite(x[k].y) && isfinite(x[k].z) &&
-                 isfinite(x[k].w);
-        argmax_merge(best, bidx, x[k].x, v);
-        argmax_merge(best, bidx, x[k].y, v + 1);
-        argmax_merge(best, bidx, x[k].z, v + 2);
-        argmax_merge(best, bidx, x[k].w, v + 3);
-      }
-    }
+    st::argmax_slice_load<true>(logits, V, blockIdx.x, blockIdx.y, r);
+    st::argmax_slice_finish<true>(r, V, blockIdx.x, blockIdx.y, gridDim.y, part, status, scratch);
   } else {
-    float x[kArgmaxPerThread];
-#pragma unroll
-    for (int k = 0; k < kArgmaxPerThread; ++k) {
-      const int v = base + threadIdx.x + k * kArgmaxBlock;
-      x[k] = v < V ? row[v] : -INFINITY;
-    }
-#pragma unroll
-    for (int k = 0; k < kArgmaxPerThread; ++k) {
-      const int v = base + threadIdx.x + k * kArgmaxBlock;
-      if (v < V) {
-        finite = finite && isfinite(x[k]);
-        argmax_merge(best, bidx, x[k], v);
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(best, o, ST_WAVE);
-    const int i2 = __shfl_xor(bidx, o, ST_WAVE);
-    argmax_merge(best, bidx, v2, i2);
-  }
-  __shared__ float sv[kArgmaxBlock / ST_WAVE];
-  __shared__ int si[kArgmaxBlock / ST_WAVE];
-  __shared__ int sf;
-  if (threadIdx.x == 0) sf = 1;
-  __syncthreads();
-  const int w = threadIdx.x / ST_WAVE;
-  if (threadIdx.x % ST_WAVE == 0) {
-    sv[w] = best;
-    si[w] = bidx;
-  }
-  if (!finite) sf = 0;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int k = 1; k < kArgmaxBlock / ST_WAVE; ++k) argmax_merge(best, bidx, sv[k], si[k]);
-    part[(size_t)t * nslices + slice] = ArgmaxPart{best, bidx};
-    if (!sf) st::set_status(status, ST_STATUS_NONFINITE);
+    st::argmax_slice_load<false>(logits, V, blockIdx.x, blockIdx.y, r);
+    st::argmax_slice_finish<false>(r, V, blockIdx.x, blockIdx.y, gridDim.y, part, status, scratch);
   }
 }
 
@@ -467,30 +409,32 @@ stoch_walk_kernel(const int32_t* __restrict__ node_off, const int32_t* __restric
 
 // ---------------------------------------------------------------- entry points
 
-static int argmax_slices(int V) { return (V + kArgmaxSlice - 1) / kArgmaxSlice; }
+using st::argmax_slices;
 
 extern "C" size_t st_verify_greedy_workspace(const st_tree* tree, int V) {
   if (st::check_tree_host(tree) || V < 1) return 0;
   return st::align_up((size_t)tree->total_nodes * argmax_slices(V) * sizeof(ArgmaxPart), 256);
 }
 
-int st::greedy_argmax_only(const st_tree* tree, int V, const int32_t* tokens,
-                           const float* logits, int32_t* accept_len, int32_t* accept_nodes,
-                           int32_t* out_tokens, void* workspace, size_t ws_bytes,
-                           int32_t* status, void* stream, st::GreedyWalkArgs& g) {
+int st::greedy_prepare(const st_tree* tree, int V, const int32_t* tokens, const float* logits,
+                       int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                       void* workspace, size_t ws_bytes, int32_t* status,
+                       st::GreedyWalkArgs& g) {
   int rc = st::check_tree_host(tree);
   if (rc) return rc;
   if (V < 1 || !tokens || !logits || !accept_len || !accept_nodes || !out_tokens || !workspace)
     return ST_E_INVALID;
   if (tree->max_depth + 1 > kMaxPath) return ST_E_UNSUPPORTED;
   if (ws_bytes < st_verify_greedy_workspace(tree, V)) return ST_E_WORKSPACE;
-  ArgmaxPart* part = (ArgmaxPart*)workspace;
-  const int ns = argmax_slices(V);
-  hipLaunchKernelGGL(row_argmax_kernel, dim3(tree->total_nodes, ns), dim3(kArgmaxBlock), 0,
-                     (hipStream_t)stream, logits, V, part, status);
-  g = st::GreedyWalkArgs{tree->node_off, tree->parent, tokens, part, ns,
-                         tree->total_nodes, V, tree->max_nodes, tree->max_depth,
-                         accept_len, accept_nodes, out_tokens, status};
+  g = st::GreedyWalkArgs{tree->node_off, tree->parent, tokens, (ArgmaxPart*)workspace,
+                         argmax_slices(V), tree->total_nodes, V, tree->max_nodes,
+                         tree->max_depth, accept_len, accept_nodes, out_tokens, status};
+  return ST_OK;
+}
+
+int st::greedy_argmax_launch(const st::GreedyWalkArgs& g, const float* logits, void* stream) {
+  hipLaunchKernelGGL(row_argmax_kernel, dim3(g.T, g.nslices), dim3(kArgmaxBlock), 0,
+                     (hipStream_t)stream, logits, g.V, (ArgmaxPart*)g.part, g.status);
   return st::check_launch();
 }
 
@@ -499,9 +443,9 @@ extern "C" int st_verify_greedy(const st_tree* tree, int V, const int32_t* token
                                 int32_t* out_tokens, void* workspace, size_t ws_bytes,
                                 int32_t* status, void* stream) {
   st::GreedyWalkArgs g;
-  const int rc = st::greedy_argmax_only(tree, V, tokens, logits, accept_len, accept_nodes,
-                                        out_tokens, workspace, ws_bytes, status, stream, g);
-  if (rc) return rc;
+  int rc = st::greedy_prepare(tree, V, tokens, logits, accept_len, accept_nodes, out_tokens,
+                              workspace, ws_bytes, status, g);
+  if (rc || (rc = st::greedy_argmax_launch(g, logits, stream))) return rc;
   hipLaunchKernelGGL(greedy_walk_kernel, dim3(tree->B), dim3(ST_WAVE), 0, (hipStream_t)stream, g);
   return st::check_launch();
 }
