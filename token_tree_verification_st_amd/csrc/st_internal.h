@@ -26,6 +26,21 @@ inline int mask_words(int max_nodes) { return (max_nodes + 63) / 64; }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Compute units of the current device, queried once per device.
+inline int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 // ---------------------------------------------------------------- device side
 
 __device__ inline void set_status(int32_t* status, int bits) {

@@ -11,13 +11,13 @@
 // rejection).  The residual after k rejected children of node u has a closed
 // form: r_k = max(0, p_u - c_k q_u) / D_k with c_0 = 0, D_0 = 1,
 // c_{k+1} = c_k + D_k and D_{k+1} = sum_v max(0, p_u - c_{k+1} q_u)
-// (unchanged when that sum is 0).  It does not depend on which tokens were
-// rejected, so every node can test its own children as soon as its logits are
-// loaded: one workgroup per node keeps both logit rows in registers, computes
-// max / sum-exp, then tests its children in order until the first acceptance,
-// spending one vocab reduction per rejection.  A second kernel walks each
-// request's tree through those per-node verdicts and draws the replacement
-// token at the stop node by inverse CDF.
+// (unchanged when that sum is 0).  A first kernel reduces every logit row to
+// its softmax statistics (max, sum of exponentials), one workgroup per row;
+// with those, testing the first child of any node needs two logits only.  A
+// second kernel walks each request's tree with one workgroup: the children's
+// tests read precomputed values, and only the nodes where the walk rejects a
+// child or stops have their two rows read again, for the residual masses and
+// the inverse-CDF draw of the replacement token.
 #include "step_internal.h"
 
 #include <float.h>
@@ -35,30 +35,110 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kTieEps = 1e-6;
 
 // ---------------------------------------------------------------- reductions
+//
+// Wavefront reductions and scans in VALU: DPP moves within 16-lane rows, and
+// gfx950's permlane swaps between rows.  Every exchange is an involution and
+// both partners add in the same operand order, so all lanes of a reduction
+// end with the same bits.
 
-template <int BLOCK, typename T, typename Op>
-__device__ inline T block_reduce(T v, T* lds, Op op) {
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {  // 0 where the source lane is absent
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// (own, partner) for the partners l ^ 16 and l ^ 32, in either order
+template <bool X32>
+__device__ __forceinline__ void swap_rows(double v, double& x0, double& x1) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+  const auto l = X32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                     : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h = X32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                     : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  x0 = __longlong_as_double((long long)(((uint64_t)h[0] << 32) | l[0]));
+  x1 = __longlong_as_double((long long)(((uint64_t)h[1] << 32) | l[1]));
+}
+template <bool X32>
+__device__ __forceinline__ void swap_rows(float v, float& x0, float& x1) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = X32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x0 = __uint_as_float(r[0]);
+  x1 = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
+  double x0, x1;
+  swap_rows<false>(v, x0, x1);
+  v = x0 + x1;
+  swap_rows<true>(v, x0, x1);
+  return x0 + x1;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  float x0, x1;
+  swap_rows<false>(v, x0, x1);
+  v = fmaxf(x0, x1);
+  swap_rows<true>(v, x0, x1);
+  return fmaxf(x0, x1);
+}
+
+// Inclusive scan over the lanes of a wavefront.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  v += dpp_f64<0x111>(v);       // row_shr:1
+  v += dpp_f64<0x112>(v);       // row_shr:2
+  v += dpp_f64<0x114>(v);       // row_shr:4
+  v += dpp_f64<0x118>(v);       // row_shr:8
+  v += dpp_f64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+// The value of lane l - 1 (0 in lane 0).
+__device__ __forceinline__ double wave_shr1(double v) { return dpp_f64<0x138>(v); }
+
+// Workgroup-wide reductions: wavefront results through LDS, combined in
+// wavefront order by every thread.
+template <int BLOCK>
+__device__ inline double block_sum(double v, double* lds) {
   constexpr int NW = BLOCK / ST_WAVE;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o, ST_WAVE));
+  v = wave_sum(v);
   const int w = threadIdx.x / ST_WAVE, lane = threadIdx.x % ST_WAVE;
   __syncthreads();
   if (lane == 0) lds[w] = v;
   __syncthreads();
-  T r = lds[0];
+  double r = lds[0];
 #pragma unroll
-  for (int i = 1; i < NW; ++i) r = op(r, lds[i]);
+  for (int i = 1; i < NW; ++i) r += lds[i];
   return r;
 }
-
-struct MaxOp {
-  template <typename T>
-  __device__ T operator()(T a, T b) const { return a > b ? a : b; }
-};
-struct SumOp {
-  template <typename T>
-  __device__ T operator()(T a, T b) const { return a + b; }
-};
+template <int BLOCK>
+__device__ inline float block_max(float v, float* lds) {
+  constexpr int NW = BLOCK / ST_WAVE;
+  v = wave_max(v);
+  const int w = threadIdx.x / ST_WAVE, lane = threadIdx.x % ST_WAVE;
+  __syncthreads();
+  if (lane == 0) lds[w] = v;
+  __syncthreads();
+  float r = lds[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, lds[i]);
+  return r;
+}
 
 using st::argmax_merge;
 using st::ArgmaxPart;
@@ -151,258 +231,486 @@ __device__ inline void node_uniforms(uint64_t seed, uint64_t offset, int req, in
 
 // ---------------------------------------------------------------- stochastic
 
-struct NodeVerdict {
-  double c, D;      // residual after the tested children: max(0, p - c q) / D
-  double Zt, Zd;    // sums of exp2((l - M) * log2e / T), target and draft
-  float Mt, Md;     // row maxima
-  int accepted;     // first accepted child (local index), -1 if none
-  int ties;         // near ties among this node's tests
+// Softmax statistics of one logit row at temperature T: M = max logit and
+// Z = sum over v of exp2((l_v - M) * log2e / T), each term rounded to fp32,
+// groups of four consecutive terms summed in fp32 and the groups in fp64.
+// Rows 2t and 2t+1 are node t's target and draft rows.
+struct RowStat {
+  float M;
+  int pad;
+  double Z;
 };
 
-constexpr int kStochBlock = 512;
-constexpr int kStochNpt = 64;  // logits per thread and row: V <= 32768
+// What the walk needs from a node: its first accepted child (local index, -1
+// if none), the near ties among its tests and, when no child is accepted, the
+// replacement token drawn there and whether that draw was a near tie.
+struct NodeVerdict {
+  int accepted, ties, token, token_tie;
+};
 
-__global__ void __launch_bounds__(kStochBlock)
-stoch_node_kernel(const int32_t* __restrict__ node_off, const int32_t* __restrict__ parent,
-                  const int32_t* __restrict__ tokens, const float* __restrict__ tl,
-                  const float* __restrict__ dl, int B, int T, int V, float temperature,
-                  uint64_t seed, uint64_t offset, NodeVerdict* __restrict__ out,
-                  int32_t* status) {
-  __shared__ double red_d[kStochBlock / ST_WAVE];
-  __shared__ float red_f[kStochBlock / ST_WAVE];
-  __shared__ uint64_t kids[ST_MAX_NODES / 64];
-  __shared__ int s_dec;
-  const int t = blockIdx.x, tid = threadIdx.x;
-  const int b = st::request_of(node_off, B, t);
-  const int lo = node_off[b], n = node_off[b + 1] - lo, i = t - lo;
-  const float* rt = tl + (size_t)t * V;
-  const float* rd = dl + (size_t)t * V;
+struct StochArgs {
+  const int32_t* node_off;
+  const int32_t* parent;
+  const int32_t* tokens;
+  const float* tl;
+  const float* dl;
+  RowStat* stat;
+  NodeVerdict* verdict;
+  int B, T, V, max_nodes, max_depth;
+  float temperature;
+  uint64_t seed, offset;
+  int32_t* accept_len;
+  int32_t* accept_nodes;
+  int32_t* out_tokens;
+  int32_t* near_ties;
+  int32_t* status;
+};
 
-  float xt[kStochNpt], xd[kStochNpt];
-  bool finite = true;
-  float mt = -INFINITY, md = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kStochNpt; ++k) {
-    const int v = k * kStochBlock + tid;
-    xt[k] = v < V ? __builtin_nontemporal_load(rt + v) : -INFINITY;
-    xd[k] = v < V ? __builtin_nontemporal_load(rd + v) : -INFINITY;
-  }
-#pragma unroll
-  for (int k = 0; k < kStochNpt; ++k) {
-    if (k * kStochBlock + tid < V) finite = finite && isfinite(xt[k]) && isfinite(xd[k]);
-    mt = fmaxf(mt, xt[k]);
-    md = fmaxf(md, xd[k]);
-  }
-  if (!finite) st::set_status(status, ST_STATUS_NONFINITE);
-  mt = block_reduce<kStochBlock>(mt, red_f, MaxOp());
-  md = block_reduce<kStochBlock>(md, red_f, MaxOp());
-  const float s = kLog2e / temperature;
-  double zt = 0.0, zd = 0.0;
-#pragma unroll
-  for (int k = 0; k < kStochNpt; ++k) {
-    xt[k] = exp2f((xt[k] - mt) * s);  // padding: exp2(-inf) = 0
-    xd[k] = exp2f((xd[k] - md) * s);
-    zt += xt[k];
-    zd += xd[k];
-  }
-  zt = block_reduce<kStochBlock>(zt, red_d, SumOp());
-  zd = block_reduce<kStochBlock>(zd, red_d, SumOp());
-  const double a = 1.0 / zt, bq = 1.0 / zd;
+constexpr int kStochBlock = 1024;
+constexpr int kStochWaves = kStochBlock / ST_WAVE;
+constexpr int kStochMaxV = 32768;
+constexpr int kStochNpt = kStochMaxV / kStochBlock;  // row entries per thread
 
-  // children of local node i, as a bitmask over local indices
-  if (tid < ST_MAX_NODES / 64) kids[tid] = 0;
+// A row is spread over the workgroup wavefront by wavefront: wavefront w holds
+// the kStochNpt*64 consecutive logits from w*kStochNpt*64, as tiles of
+// 64*EPT.  With VEC (V % 4 == 0, 16-byte aligned rows) entries 4k..4k+3 of a
+// lane are four consecutive logits of tile k (one coalesced 16-byte load per
+// lane), else entry k is one logit of tile k.
+template <bool VEC>
+__device__ inline int row_index(int e, int tid) {
+  const int w = tid / ST_WAVE, lane = tid % ST_WAVE;
+  return w * (kStochNpt * ST_WAVE) +
+         (VEC ? (e >> 2) * (4 * ST_WAVE) + lane * 4 + (e & 3) : e * ST_WAVE + lane);
+}
+
+// Loads a thread's row entries.  Every load is issued, unconditionally, before
+// any is used, so the wait for one buffer does not also wait for loads issued
+// after it: entries past the row end (all entries when `on` is false) read the
+// row's first logit instead, which leaves the row maximum unchanged; sums mask
+// them out with row_index(e) < V, applied to computed terms only.
+template <bool VEC>
+__device__ inline void load_row(const float* __restrict__ src, int V, bool on,
+                                float (&x)[kStochNpt]) {
+  const int tid = threadIdx.x;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int k = 0; k < kStochNpt / 4; ++k) {
+      const int v = row_index<true>(4 * k, tid);
+      const f32x4 q =
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (on && v < V ? v : 0)));
+      x[4 * k] = q.x;
+      x[4 * k + 1] = q.y;
+      x[4 * k + 2] = q.z;
+      x[4 * k + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kStochNpt; ++e) {
+      const int v = row_index<false>(e, tid);
+      x[e] = __builtin_nontemporal_load(src + (on && v < V ? v : 0));
+    }
+  }
+}
+
+// 2^x by the hardware instruction: results below 2^-126 flush to 0, which no
+// sum here can see (every sum has a term equal to 1) and which only reaches
+// the acceptance tests at sizes far inside their near-tie band.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp2((l - M) * s), times `scale`, for the entries inside the row, else 0.
+template <bool VEC>
+__device__ inline void row_probs(float (&x)[kStochNpt], int V, float M, float s, float scale) {
+#pragma unroll
+  for (int e = 0; e < kStochNpt; ++e) {
+    const float p = exp2_fast((x[e] - M) * s) * scale;
+    x[e] = row_index<VEC>(e, threadIdx.x) < V ? p : 0.f;
+  }
+}
+
+// The residual weight max(0, p_v - c q_v) of one row entry from its
+// probabilities P = p_v and Q = q_v, both rounded to fp32: a fused
+// multiply-add and a max in fp32.
+__device__ __forceinline__ float resid(float P, float Q, float c) {
+  return fmaxf(0.f, fmaf(-c, Q, P));
+}
+// Sum of the residual weights of entries [k*EPT, k*EPT+EPT) of a thread: fp32
+// within the (at most 4) entries, fp64 from there on.
+template <int EPT>
+__device__ __forceinline__ double resid_group(const float (&P)[kStochNpt],
+                                              const float (&Q)[kStochNpt], float c, int k) {
+  float s = resid(P[k * EPT], Q[k * EPT], c);
+#pragma unroll
+  for (int j = 1; j < EPT; ++j) s += resid(P[k * EPT + j], Q[k * EPT + j], c);
+  return (double)s;
+}
+// A thread's share of sum_v max(0, p_v - c q_v).
+template <bool VEC>
+__device__ __forceinline__ double resid_sum(const float (&P)[kStochNpt],
+                                            const float (&Q)[kStochNpt], float c) {
+  constexpr int EPT = VEC ? 4 : 1;
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < kStochNpt / EPT; ++k) s += resid_group<EPT>(P, Q, c, k);
+  return s;
+}
+
+struct DrawLds {
+  double wsum[kStochWaves];
+  int pick, tie;
+};
+
+// Inverse-CDF draw from the residual w_v = max(0, p_v - c q_v) in ascending
+// vocab order: the smallest v whose running sum exceeds u * sum(w).  Every
+// wavefront reduces its slice of the row; the prefix over the slices (summed
+// in wavefront order by every thread) names the slice that crosses the
+// threshold, and that wavefront alone locates the tile, then the entry.  The
+// threshold test at every level compares running sums that begin where the
+// previous level's left off.  Returns sum(w); pick and tie are set when it is
+// positive.
+template <bool VEC>
+__device__ inline double draw_residual(const float (&P)[kStochNpt], const float (&Q)[kStochNpt],
+                                       float c, double u, DrawLds& s, int& pick, int& tie) {
+  constexpr int EPT = VEC ? 4 : 1, NT = kStochNpt / EPT;
+  const int tid = threadIdx.x, lane = tid % ST_WAVE;
+  const int w = __builtin_amdgcn_readfirstlane(tid / ST_WAVE);
+  const double mine = wave_sum(resid_sum<VEC>(P, Q, c));
+  if (lane == 0) s.wsum[w] = mine;
+  if (tid == 0) {
+    s.pick = 0;
+    s.tie = 0;
+  }
   __syncthreads();
-  const bool sane = n >= 1 && n <= ST_MAX_NODES && lo + n <= T;
-  if (sane && tid < n && tid > i && parent[lo + tid] == i)
-    atomicOr((unsigned long long*)&kids[tid >> 6], 1ull << (tid & 63));
-  __syncthreads();
-
-  double c = 0.0, D = 1.0;
-  int ties = 0, accepted = -1;
-  for (int w = 0; w < ST_MAX_NODES / 64 && accepted < 0; ++w) {
-    uint64_t m = kids[w];
-    while (m && accepted < 0) {
-      const int child = w * 64 + __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      if (tid == 0) {
-        const int x = tokens[lo + child];
-        int dec = 0;
-        if (x >= 0 && x < V) {
-          double ua, us;
-          node_uniforms(seed, offset, b, child, ua, us);
-          const double px = (double)exp2f((rt[x] - mt) * s) * a;
-          const double qx = (double)exp2f((rd[x] - md) * s) * bq;
-          const double r = fmax(0.0, px - c * qx) / D;
-          const double lhs = ua * qx;
-          ties += fabs(r - lhs) < kTieEps;
-          dec = lhs < r;
-        }
-        s_dec = dec;
-      }
-      __syncthreads();
-      const int dec = s_dec;
-      __syncthreads();
-      if (dec) {
-        accepted = child;
-        break;
-      }
-      const double cn = c + D;
-      const double cq = cn * bq;
+  double total = 0.0;
+  for (int i = 0; i < kStochWaves; ++i) total += s.wsum[i];
+  const double thr = u * total;
+  // the slice: running sums over the wavefronts' slices, in the same order
+  double base = 0.0, run0 = 0.0;
+  int ws = -1;
+  for (int i = 0; i < kStochWaves; ++i) {
+    const double next = run0 + s.wsum[i];
+    if (ws < 0 && next > thr) {
+      ws = i;
+      base = run0;
+    }
+    run0 = next;
+  }
+  if (ws < 0) {  // total == 0
+    pick = 0;
+    tie = 0;
+    return total;
+  }
+  if (w == ws) {
+    // recomputed from P and Q rather than kept from above (registers)
+    float cw = c;
+    asm volatile("" : "+v"(cw));
+    // the tile: running sums over the wavefront's tiles from `base`
+    double run = base, tbase = base;
+    int kt = -1, klast = -1;
+    double lbase = base;
+    for (int k = 0; k < NT; ++k) {
       double part = 0.0;
 #pragma unroll
-      for (int k = 0; k < kStochNpt; ++k) {
-        // keep the fp64 widening inside the loop (hoisting it would need 256
-        // more registers)
-        float et = xt[k], ed = xd[k];
-        asm volatile("" : "+v"(et), "+v"(ed));
-        part += fmax(0.0, (double)et * a - (double)ed * cq);
+      for (int kk = 0; kk < NT; ++kk)
+        if (kk == k) part = resid_group<EPT>(P, Q, cw, kk);
+      const double tsum = wave_sum(part);
+      const double next = run + tsum;
+      if (kt < 0 && next > thr) {
+        kt = k;
+        tbase = run;
       }
-      const double Dn = block_reduce<kStochBlock>(part, red_d, SumOp());
+      if (tsum > 0.0) {
+        klast = k;
+        lbase = run;
+      }
+      run = next;
+    }
+    if (kt < 0) {  // rounding: no tile crosses; take the last positive one
+      kt = klast;
+      tbase = lbase;
+    }
+    // the entry: a scan over the lanes of tile kt
+    float wt[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) wt[j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < NT; ++k)
+      if (k == kt) {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) wt[j] = resid(P[k * EPT + j], Q[k * EPT + j], cw);
+      }
+    double sub = 0.0;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) sub += (double)wt[j];
+    double run2 = tbase + wave_shr1(wave_incl_scan(sub));
+    double lo_edge = 0.0, hi_edge = 0.0, last_lo = 0.0, last_hi = 0.0;
+    int found = -1, last = -1;
+    // within a lane the weights are added one by one in fp64
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const double x = (double)wt[j];
+      const double before = run2;
+      run2 += x;
+      if (x > 0.0) {
+        last = j;
+        last_lo = before;
+        last_hi = run2;
+        if (found < 0 && run2 > thr) {
+          found = j;
+          lo_edge = before;
+          hi_edge = run2;
+        }
+      }
+    }
+    const uint64_t fm = __ballot(found >= 0);
+    // no entry-level crossing (rounding): the last positive entry of the tile
+    const uint64_t lm = __ballot(last >= 0);
+    const int who = fm ? __ffsll((unsigned long long)fm) - 1
+                       : lm ? 63 - __clzll((long long)lm) : -1;
+    if (lane == who) {
+      const int j = fm ? found : last;
+      const double ce_lo = fm ? lo_edge : last_lo, ce_hi = fm ? hi_edge : last_hi;
+      const int v = row_index<VEC>(kt * EPT + j, tid);
+      s.pick = v;
+      s.tie = fabs(ce_hi - thr) < kTieEps * total || (v > 0 && fabs(ce_lo - thr) < kTieEps * total);
+    }
+  }
+  __syncthreads();
+  pick = s.pick;
+  tie = s.tie;
+  return total;
+}
+
+// Row statistics, persistent: workgroup g reduces rows g, g + G, g + 2G, ...
+// (G = gridDim.x), with the next row's loads in flight while the current row
+// is reduced (two register buffers, used alternately).
+template <bool VEC>
+__device__ inline void finish_row(const StochArgs& g, const float (&x)[kStochNpt], int r,
+                                  float* red_f, double* red_d) {
+  float m = -INFINITY;
+  bool finite = true;
+#pragma unroll
+  for (int e = 0; e < kStochNpt; ++e) {
+    finite &= (bool)isfinite(x[e]);
+    m = fmaxf(m, x[e]);
+  }
+  if (!finite) st::set_status(g.status, ST_STATUS_NONFINITE);
+  m = block_max<kStochBlock>(m, red_f);
+  const float sc = kLog2e / g.temperature;
+  // fp32 within a group of (at most 4) consecutive entries, fp64 from there on
+  constexpr int EPT = VEC ? 4 : 1;
+  double z = 0.0;
+#pragma unroll
+  for (int k = 0; k < kStochNpt / EPT; ++k) {
+    float zk = exp2_fast((x[k * EPT] - m) * sc);
+#pragma unroll
+    for (int j = 1; j < EPT; ++j) zk += exp2_fast((x[k * EPT + j] - m) * sc);
+    z += (double)(row_index<VEC>(k * EPT, threadIdx.x) < g.V ? zk : 0.f);
+  }
+  z = block_sum<kStochBlock>(z, red_d);
+  if (threadIdx.x == 0) {
+    RowStat rs;
+    rs.M = m;
+    rs.pad = 0;
+    rs.Z = z;
+    g.stat[r] = rs;
+  }
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kStochBlock)
+row_stat_kernel(StochArgs g) {
+  __shared__ float red_f[kStochWaves];
+  __shared__ double red_d[kStochWaves];
+  const int R = 2 * g.T, G = gridDim.x;
+  // Past the last row a buffer is refilled from row 0 (read by every
+  // workgroup, so from cache) and never used: the loads stay unconditional.
+  auto row = [&](int r) { return r < R ? ((r & 1) ? g.dl : g.tl) + (size_t)(r >> 1) * g.V : g.tl; };
+  float xa[kStochNpt], xb[kStochNpt];
+  int r = blockIdx.x;
+  load_row<VEC>(row(r), g.V, true, xa);
+  while (true) {
+    load_row<VEC>(row(r + G), g.V, true, xb);
+    finish_row<VEC>(g, xa, r, red_f, red_d);
+    r += G;
+    if (r >= R) break;
+    load_row<VEC>(row(r + G), g.V, true, xa);
+    finish_row<VEC>(g, xb, r, red_f, red_d);
+    r += G;
+    if (r >= R) break;
+  }
+}
+
+struct NodeLds {
+  int place[4];  // b, lo, n, ok
+  uint64_t kid_mask[ST_MAX_NODES / 64];
+  int kids[ST_MAX_NODES];  // children, ascending
+  double px[ST_MAX_NODES], qx[ST_MAX_NODES], ua[ST_MAX_NODES];  // per child
+  int ok[ST_MAX_NODES];                                           // token in range
+  double red[kStochWaves];
+  double u_draw;
+  DrawLds draw;
+};
+
+// One workgroup per node u decides what the walk would do on reaching u: test
+// u's children in ascending order, child c with token x accepted iff
+// u_acc(c) q_u[x] < r[x] with r starting at p_u, and draw the replacement
+// token from r when no child is accepted.  The first test needs only the row
+// statistics; u's rows are read (into registers, as fp32 probabilities) once
+// a child is rejected, for the residual masses of the later tests and the
+// draw.  A leaf reads its target row only, to draw from p_u.
+template <bool VEC>
+__global__ void __launch_bounds__(kStochBlock)
+stoch_node_kernel(StochArgs g) {
+  __shared__ NodeLds s;
+  const int tid = threadIdx.x, t = blockIdx.x;
+  if (tid < ST_WAVE) {  // node t's request: the number of request starts at or before t, less one
+    int cnt = 0;
+    for (int b0 = 0; b0 < g.B; b0 += ST_WAVE) {
+      const int b = b0 + tid;
+      cnt += __popcll(__ballot(b < g.B && g.node_off[b] <= t));
+    }
+    const int b = cnt > 0 ? cnt - 1 : 0;
+    const int lo = g.node_off[b], hi = g.node_off[b + 1];
+    if (tid == 0) {
+      s.place[0] = b;
+      s.place[1] = lo;
+      s.place[2] = hi - lo;
+      s.place[3] = (lo >= 0) & (hi <= g.T) & (hi - lo >= 1) & (hi - lo <= g.max_nodes) &
+                   (t >= lo) & (t < hi);
+    }
+  }
+  if (tid < ST_MAX_NODES / 64) s.kid_mask[tid] = 0;
+  __syncthreads();
+  if (!s.place[3]) return;  // the walk flags the request
+  const int b = s.place[0], lo = s.place[1], n = s.place[2], i = t - lo;
+  if (tid < n && tid > i && g.parent[lo + tid] == i)
+    atomicOr((unsigned long long*)&s.kid_mask[tid >> 6], 1ull << (tid & 63));
+  if (tid == kStochBlock - 1) {
+    double ua, us;
+    node_uniforms(g.seed, g.offset, b, i, ua, us);
+    s.u_draw = us;
+  }
+  const RowStat rt = g.stat[2 * t];
+  const double a = 1.0 / rt.Z;
+  const float sc = kLog2e / g.temperature, af = (float)a;
+  __syncthreads();
+  int nk = 0;
+#pragma unroll
+  for (int w = 0; w < ST_MAX_NODES / 64; ++w) nk += __popcll(s.kid_mask[w]);
+
+  if (nk == 0) {  // a leaf: the walk stops here with r = p_u
+    float P[kStochNpt];
+    load_row<VEC>(g.tl + (size_t)t * g.V, g.V, true, P);
+    row_probs<VEC>(P, g.V, rt.M, sc, af);
+    int token, tie;
+    draw_residual<VEC>(P, P, 0.f, s.u_draw, s.draw, token, tie);
+    if (tid == 0) g.verdict[t] = NodeVerdict{-1, 0, token, tie};
+    return;
+  }
+
+  const RowStat rd = g.stat[2 * t + 1];
+  const double bq = 1.0 / rd.Z;
+  if (tid < n && ((s.kid_mask[tid >> 6] >> (tid & 63)) & 1)) {
+    int rank = __popcll(s.kid_mask[tid >> 6] & ((1ull << (tid & 63)) - 1));
+    for (int w = 0; w < (tid >> 6); ++w) rank += __popcll(s.kid_mask[w]);
+    s.kids[rank] = tid;
+    const int x = g.tokens[lo + tid];
+    const bool ok = x >= 0 && x < g.V;
+    s.ok[rank] = ok;
+    if (ok) {
+      const size_t at = (size_t)t * g.V + x;
+      s.px[rank] = (double)exp2_fast((g.tl[at] - rt.M) * sc) * a;
+      s.qx[rank] = (double)exp2_fast((g.dl[at] - rd.M) * sc) * bq;
+      double ua, us;
+      node_uniforms(g.seed, g.offset, b, tid, ua, us);
+      s.ua[rank] = ua;
+    }
+  }
+  __syncthreads();
+
+  int ties = 0, accepted = -1;
+  double c = 0.0, D = 1.0;
+  // child k's test against r = max(0, p - c q) / D
+  auto test = [&](int k) {
+    if (!s.ok[k]) return false;
+    const double qv = s.qx[k];
+    const double r = fmax(0.0, s.px[k] - c * qv) / D;
+    const double lhs = s.ua[k] * qv;
+    ties += fabs(r - lhs) < kTieEps;
+    return lhs < r;
+  };
+  int token = -1, tie = 0;
+  if (test(0)) {
+    accepted = s.kids[0];
+  } else {
+    float P[kStochNpt], Q[kStochNpt];
+    load_row<VEC>(g.tl + (size_t)t * g.V, g.V, true, P);
+    load_row<VEC>(g.dl + (size_t)t * g.V, g.V, true, Q);
+    row_probs<VEC>(P, g.V, rt.M, sc, af);
+    row_probs<VEC>(Q, g.V, rd.M, sc, (float)bq);
+    // after each rejection r <- max(0, r - q) renormalised, i.e. c <- c + D
+    for (int k = 1; k < nk && accepted < 0; ++k) {
+      const double cn = c + D;
+      const double Dn = block_sum<kStochBlock>(resid_sum<VEC>(P, Q, (float)cn), s.red);
       if (Dn > 0.0) {
         c = cn;
         D = Dn;
       }
+      if (test(k)) accepted = s.kids[k];
+    }
+    if (accepted < 0) {  // every child rejected: draw from the final residual
+      const double total = draw_residual<VEC>(P, Q, (float)(c + D), s.u_draw, s.draw, token, tie);
+      if (!(total > 0.0)) {  // the last rejection left no mass: r unchanged
+        __syncthreads();
+        draw_residual<VEC>(P, Q, (float)c, s.u_draw, s.draw, token, tie);
+      }
     }
   }
-  if (tid == 0) {
-    NodeVerdict nv;
-    nv.c = c;
-    nv.D = D;
-    nv.Zt = zt;
-    nv.Zd = zd;
-    nv.Mt = mt;
-    nv.Md = md;
-    nv.accepted = accepted;
-    nv.ties = ties;
-    out[t] = nv;
-  }
+  if (tid == 0) g.verdict[t] = NodeVerdict{accepted, ties, token, tie};
 }
 
-// Exclusive scan of one double per thread across the block.
-template <int BLOCK>
-__device__ inline double block_exclusive_scan(double v, double* lds, double& total) {
-  constexpr int NW = BLOCK / ST_WAVE;
-  const int lane = threadIdx.x % ST_WAVE, w = threadIdx.x / ST_WAVE;
-  double incl = v;
-#pragma unroll
-  for (int o = 1; o < ST_WAVE; o <<= 1) {
-    const double y = __shfl_up(incl, o, ST_WAVE);
-    if (lane >= o) incl += y;
-  }
-  __syncthreads();
-  if (lane == ST_WAVE - 1) lds[w] = incl;
-  __syncthreads();
-  double before = 0.0;
-  total = 0.0;
-  for (int k = 0; k < NW; ++k) {
-    if (k < w) before += lds[k];
-    total += lds[k];
-  }
-  return before + incl - v;
-}
-
-__global__ void __launch_bounds__(kStochBlock)
-stoch_walk_kernel(const int32_t* __restrict__ node_off, const int32_t* __restrict__ parent,
-                  const int32_t* __restrict__ tokens, const float* __restrict__ tl,
-                  const float* __restrict__ dl, const NodeVerdict* __restrict__ verdict, int T,
-                  int V, int max_nodes, int max_depth, float temperature, uint64_t seed,
-                  uint64_t offset, int32_t* accept_len, int32_t* accept_nodes,
-                  int32_t* out_tokens, int32_t* near_ties, int32_t* status) {
+// One wavefront per request follows the verdicts from the root: step to the
+// accepted child while there is one (at most max_depth steps), then emit the
+// token drawn at the stop node.
+__global__ void __launch_bounds__(ST_WAVE)
+stoch_walk_kernel(StochArgs g) {
   __shared__ int path[kMaxPath + 1];
-  __shared__ int s_u, s_L, s_over, s_ties;
-  __shared__ double red[kStochBlock / ST_WAVE];
-  __shared__ int s_pick, s_last;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int lo = node_off[b], hi = node_off[b + 1], n = hi - lo;
-  if (lo < 0 || hi > T || n < 1 || n > max_nodes) {
-    if (tid == 0) st::set_status(status, ST_STATUS_BAD_PARENT);
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int lo = g.node_off[b], hi = g.node_off[b + 1], n = hi - lo;
+  if (lo < 0 || hi > g.T || n < 1 || n > g.max_nodes) {
+    if (lane == 0) st::set_status(g.status, ST_STATUS_BAD_PARENT);
     return;
   }
-  const int bits = check_request(parent, tokens, lo, n, V);
-  if (bits) st::set_status(status, bits);
-
-  if (tid == 0) {
-    int u = 0, L = 0, ties = 0, over = 0;
+  const int bits = check_request(g.parent, g.tokens, lo, n, g.V);
+  if (bits) st::set_status(g.status, bits);
+  int L = 0, ties = 0, last = -1;
+  bool over = false;
+  if (lane == 0) {
+    int u = 0;
     path[0] = 0;
     while (true) {
-      const NodeVerdict nv = verdict[lo + u];
-      ties += nv.ties;
-      const int c = nv.accepted;
-      if (c <= u || c >= n) break;  // -1: no child accepted
-      if (L == max_depth) {
-        over = 1;
+      const NodeVerdict v = g.verdict[lo + u];
+      ties += v.ties;
+      if (v.accepted <= u || v.accepted >= n) {  // -1: stop here
+        last = v.token;
+        ties += v.token_tie;
         break;
       }
-      path[++L] = c;
-      u = c;
-    }
-    s_u = u;
-    s_L = L;
-    s_over = over;
-    s_ties = ties;
-    s_pick = INT_MAX;
-    s_last = -1;
-  }
-  __syncthreads();
-  const int u = s_u, L = s_L;
-  int last_token = -1, ties = s_ties;
-  if (!s_over) {
-    // replacement token: inverse CDF of r = max(0, p_u - c q_u) / D at u
-    const NodeVerdict nv = verdict[lo + u];
-    const float s = kLog2e / temperature;
-    const double a = 1.0 / nv.Zt, cq = nv.c / nv.Zd;
-    const float* rt = tl + (size_t)(lo + u) * V;
-    const float* rd = dl + (size_t)(lo + u) * V;
-    const int chunk = (V + kStochBlock - 1) / kStochBlock;
-    const int v0 = tid * chunk, v1 = min(V, v0 + chunk);
-    double local = 0.0;
-    int last_pos = -1;
-    for (int v = v0; v < v1; ++v) {
-      const double w = fmax(0.0, (double)exp2f((rt[v] - nv.Mt) * s) * a -
-                                     (double)exp2f((rd[v] - nv.Md) * s) * cq);
-      local += w;
-      if (w > 0.0) last_pos = v;
-    }
-    double total;
-    const double excl = block_exclusive_scan<kStochBlock>(local, red, total);
-    double ua, us;
-    node_uniforms(seed, offset, b, u, ua, us);
-    const double thr = us * total;
-    if (last_pos >= 0) atomicMax(&s_last, last_pos);
-    int pick = -1;
-    double c_hi = 0.0, c_lo = 0.0;
-    if (excl <= thr && excl + local > thr) {
-      // same summation order as `local`, so the last running sum equals it
-      double run = 0.0;
-      for (int v = v0; v < v1; ++v) {
-        const double w = fmax(0.0, (double)exp2f((rt[v] - nv.Mt) * s) * a -
-                                       (double)exp2f((rd[v] - nv.Md) * s) * cq);
-        c_lo = excl + run;
-        run += w;
-        if (excl + run > thr) {
-          pick = v;
-          c_hi = excl + run;
-          break;
-        }
+      if (L == g.max_depth) {
+        over = true;
+        break;
       }
-      if (pick >= 0) atomicMin(&s_pick, pick);
+      path[++L] = v.accepted;
+      u = v.accepted;
     }
-    __syncthreads();
-    const int chosen = s_pick != INT_MAX ? s_pick : s_last;
-    if (pick >= 0 && pick == chosen) {
-      const bool tie = fabs(c_hi - thr) < kTieEps * total ||
-                       (pick > 0 && fabs(c_lo - thr) < kTieEps * total);
-      s_ties = s_ties + (int)tie;
-    }
-    __syncthreads();
-    ties = s_ties;
-    last_token = chosen < 0 ? 0 : chosen;
-  } else if (tid == 0) {
-    st::set_status(status, ST_STATUS_PATH_OVERFLOW);
+    if (over) st::set_status(g.status, ST_STATUS_PATH_OVERFLOW);
+    if (g.near_ties) g.near_ties[b] = ties;
   }
-  write_path_outputs(b, L, max_depth, path, tokens, lo, last_token, accept_len, accept_nodes,
-                     out_tokens);
-  if (tid == 0 && near_ties) near_ties[b] = ties;
+  L = __shfl(L, 0, ST_WAVE);
+  last = __shfl(last, 0, ST_WAVE);
+  st::wave_lds_sync();
+  write_path_outputs(b, L, g.max_depth, path, g.tokens, lo, last, g.accept_len, g.accept_nodes,
+                     g.out_tokens);
 }
 
 }  // namespace
@@ -453,7 +761,8 @@ extern "C" int st_verify_greedy(const st_tree* tree, int V, const int32_t* token
 extern "C" size_t st_verify_stochastic_workspace(const st_tree* tree, int V) {
   (void)V;
   if (st::check_tree_host(tree)) return 0;
-  return st::align_up((size_t)tree->total_nodes * sizeof(NodeVerdict), 256);
+  return st::align_up((size_t)tree->total_nodes * (2 * sizeof(RowStat) + sizeof(NodeVerdict)),
+                      256);
 }
 
 extern "C" int st_verify_stochastic(const st_tree* tree, int V, const int32_t* tokens,
@@ -467,17 +776,25 @@ extern "C" int st_verify_stochastic(const st_tree* tree, int V, const int32_t* t
   if (V < 1 || !tokens || !target_logits || !draft_logits || !accept_len || !accept_nodes ||
       !out_tokens || !workspace || !(temperature > 0.0f))
     return ST_E_INVALID;
-  if (V > kStochBlock * kStochNpt || tree->max_depth + 1 > kMaxPath) return ST_E_UNSUPPORTED;
+  if (V > kStochMaxV || tree->max_depth + 1 > kMaxPath) return ST_E_UNSUPPORTED;
   if (ws_bytes < st_verify_stochastic_workspace(tree, V)) return ST_E_WORKSPACE;
-  NodeVerdict* nv = (NodeVerdict*)workspace;
+  const int T = tree->total_nodes;
+  RowStat* stat = (RowStat*)workspace;
+  const StochArgs g{tree->node_off, tree->parent, tokens, target_logits, draft_logits, stat,
+                    (NodeVerdict*)(stat + 2 * T), tree->B, T, V, tree->max_nodes,
+                    tree->max_depth, temperature, seed, offset, accept_len, accept_nodes,
+                    out_tokens, near_ties, status};
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(stoch_node_kernel, dim3(tree->total_nodes), dim3(kStochBlock), 0, s,
-                     tree->node_off, tree->parent, tokens, target_logits, draft_logits, tree->B,
-                     tree->total_nodes, V, temperature, seed, offset, nv, status);
+  // one persistent statistics workgroup per compute unit
+  const int stat_wg = 2 * T < st::device_cus() ? 2 * T : st::device_cus();
+  if ((V & 3) == 0) {
+    hipLaunchKernelGGL(row_stat_kernel<true>, dim3(stat_wg), dim3(kStochBlock), 0, s, g);
+    hipLaunchKernelGGL(stoch_node_kernel<true>, dim3(T), dim3(kStochBlock), 0, s, g);
+  } else {
+    hipLaunchKernelGGL(row_stat_kernel<false>, dim3(stat_wg), dim3(kStochBlock), 0, s, g);
+    hipLaunchKernelGGL(stoch_node_kernel<false>, dim3(T), dim3(kStochBlock), 0, s, g);
+  }
   if ((rc = st::check_launch())) return rc;
-  hipLaunchKernelGGL(stoch_walk_kernel, dim3(tree->B), dim3(kStochBlock), 0, s, tree->node_off,
-                     tree->parent, tokens, target_logits, draft_logits, nv, tree->total_nodes, V,
-                     tree->max_nodes, tree->max_depth, temperature, seed, offset, accept_len,
-                     accept_nodes, out_tokens, near_ties, status);
+  hipLaunchKernelGGL(stoch_walk_kernel, dim3(tree->B), dim3(ST_WAVE), 0, s, g);
   return st::check_launch();
 }
