@@ -111,33 +111,64 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
 // The value of lane l - 1 (0 in lane 0).
 __device__ __forceinline__ double wave_shr1(double v) { return dpp_f64<0x138>(v); }
 
-// Workgroup-wide reductions: wavefront results through LDS, combined in
-// wavefront order by every thread.
-template <int BLOCK>
-__device__ inline double block_sum(double v, double* lds) {
-  constexpr int NW = BLOCK / ST_WAVE;
-  v = wave_sum(v);
-  const int w = threadIdx.x / ST_WAVE, lane = threadIdx.x % ST_WAVE;
-  __syncthreads();
-  if (lane == 0) lds[w] = v;
-  __syncthreads();
-  double r = lds[0];
+// Workgroup-wide reductions: wavefront results through LDS (2 * NW slots), then
+// combined pairwise in a fixed order by every thread.  Consecutive calls on
+// one slot array must alternate `set` (0, 1): a wavefront may then write its
+// next result while others still read the previous set, and one barrier per
+// call suffices.
+template <int NW, typename T, typename Op>
+__device__ __forceinline__ T tree_fold(const T* x, Op op) {
+  T v[NW];
 #pragma unroll
-  for (int i = 1; i < NW; ++i) r += lds[i];
-  return r;
+  for (int i = 0; i < NW; ++i) v[i] = x[i];
+#pragma unroll
+  for (int h = NW / 2; h >= 1; h /= 2)
+#pragma unroll
+    for (int i = 0; i < h; ++i) v[i] = op(v[2 * i], v[2 * i + 1]);
+  return v[0];
 }
 template <int BLOCK>
-__device__ inline float block_max(float v, float* lds) {
+__device__ inline double block_sum(double v, double* lds, int set) {
+  constexpr int NW = BLOCK / ST_WAVE;
+  v = wave_sum(v);
+  if (threadIdx.x % ST_WAVE == 0) lds[set * NW + threadIdx.x / ST_WAVE] = v;
+  __syncthreads();
+  return tree_fold<NW>(lds + set * NW, [](double a, double b) { return a + b; });
+}
+// Two reductions sharing one barrier: (x, y) -> (max x, max y) and sums.
+template <int BLOCK>
+__device__ inline void block_max2(float& x, float& y, float* lds) {
+  constexpr int NW = BLOCK / ST_WAVE;
+  x = wave_max(x);
+  y = wave_max(y);
+  if (threadIdx.x % ST_WAVE == 0) {
+    lds[threadIdx.x / ST_WAVE] = x;
+    lds[NW + threadIdx.x / ST_WAVE] = y;
+  }
+  __syncthreads();
+  x = tree_fold<NW>(lds, [](float a, float b) { return fmaxf(a, b); });
+  y = tree_fold<NW>(lds + NW, [](float a, float b) { return fmaxf(a, b); });
+}
+template <int BLOCK>
+__device__ inline void block_sum2(double& x, double& y, double* lds) {
+  constexpr int NW = BLOCK / ST_WAVE;
+  x = wave_sum(x);
+  y = wave_sum(y);
+  if (threadIdx.x % ST_WAVE == 0) {
+    lds[threadIdx.x / ST_WAVE] = x;
+    lds[NW + threadIdx.x / ST_WAVE] = y;
+  }
+  __syncthreads();
+  x = tree_fold<NW>(lds, [](double a, double b) { return a + b; });
+  y = tree_fold<NW>(lds + NW, [](double a, double b) { return a + b; });
+}
+template <int BLOCK>
+__device__ inline float block_max(float v, float* lds, int set) {
   constexpr int NW = BLOCK / ST_WAVE;
   v = wave_max(v);
-  const int w = threadIdx.x / ST_WAVE, lane = threadIdx.x % ST_WAVE;
+  if (threadIdx.x % ST_WAVE == 0) lds[set * NW + threadIdx.x / ST_WAVE] = v;
   __syncthreads();
-  if (lane == 0) lds[w] = v;
-  __syncthreads();
-  float r = lds[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) r = fmaxf(r, lds[i]);
-  return r;
+  return tree_fold<NW>(lds + set * NW, [](float a, float b) { return fmaxf(a, b); });
 }
 
 using st::argmax_merge;
@@ -231,16 +262,6 @@ __device__ inline void node_uniforms(uint64_t seed, uint64_t offset, int req, in
 
 // ---------------------------------------------------------------- stochastic
 
-// Softmax statistics of one logit row at temperature T: M = max logit and
-// Z = sum over v of exp2((l_v - M) * log2e / T), each term rounded to fp32,
-// groups of four consecutive terms summed in fp32 and the groups in fp64.
-// Rows 2t and 2t+1 are node t's target and draft rows.
-struct RowStat {
-  float M;
-  int pad;
-  double Z;
-};
-
 // What the walk needs from a node: its first accepted child (local index, -1
 // if none), the near ties among its tests and, when no child is accepted, the
 // replacement token drawn there and whether that draw was a near tie.
@@ -254,7 +275,6 @@ struct StochArgs {
   const int32_t* tokens;
   const float* tl;
   const float* dl;
-  RowStat* stat;
   NodeVerdict* verdict;
   int B, T, V, max_nodes, max_depth;
   float temperature;
@@ -266,21 +286,30 @@ struct StochArgs {
   int32_t* status;
 };
 
-constexpr int kStochBlock = 1024;
-constexpr int kStochWaves = kStochBlock / ST_WAVE;
 constexpr int kStochMaxV = 32768;
-constexpr int kStochNpt = kStochMaxV / kStochBlock;  // row entries per thread
+constexpr int kNodeBlock = 1024;  // 32 entries of each row per thread
+constexpr int kMaxWaves = kNodeBlock / ST_WAVE;
 
-// A row is spread over the workgroup wavefront by wavefront: wavefront w holds
-// the kStochNpt*64 consecutive logits from w*kStochNpt*64, as tiles of
-// 64*EPT.  With VEC (V % 4 == 0, 16-byte aligned rows) entries 4k..4k+3 of a
-// lane are four consecutive logits of tile k (one coalesced 16-byte load per
-// lane), else entry k is one logit of tile k.
-template <bool VEC>
+// A row is spread over a workgroup of kStochMaxV / NPT threads, NPT entries
+// per thread, wavefront by wavefront: wavefront w holds the NPT*64
+// consecutive logits from w*NPT*64, as tiles of 64*EPT.  With VEC (V % 4 == 0,
+// 16-byte aligned rows) entries 4k..4k+3 of a lane are four consecutive
+// logits of tile k (one coalesced 16-byte load per lane), else entry k is one
+// logit of tile k.
+template <bool VEC, int NPT>
 __device__ inline int row_index(int e, int tid) {
   const int w = tid / ST_WAVE, lane = tid % ST_WAVE;
-  return w * (kStochNpt * ST_WAVE) +
+  return w * (NPT * ST_WAVE) +
          (VEC ? (e >> 2) * (4 * ST_WAVE) + lane * 4 + (e & 3) : e * ST_WAVE + lane);
+}
+
+// How many of this thread's entry groups (EPT entries each) lie inside a row
+// of V logits: in the layout above they are a prefix of the thread's groups.
+template <bool VEC, int NPT>
+__device__ inline int groups_inside(int V, int tid) {
+  constexpr int EPT = VEC ? 4 : 1, STRIDE = EPT * ST_WAVE;
+  const int first = row_index<VEC, NPT>(0, tid);
+  return V > first ? min(NPT / EPT, (V - first + STRIDE - 1) / STRIDE) : 0;
 }
 
 // Loads a thread's row entries.  Every load is issued, unconditionally, before
@@ -288,14 +317,13 @@ __device__ inline int row_index(int e, int tid) {
 // after it: entries past the row end (all entries when `on` is false) read the
 // row's first logit instead, which leaves the row maximum unchanged; sums mask
 // them out with row_index(e) < V, applied to computed terms only.
-template <bool VEC>
-__device__ inline void load_row(const float* __restrict__ src, int V, bool on,
-                                float (&x)[kStochNpt]) {
+template <bool VEC, int NPT>
+__device__ inline void load_row(const float* __restrict__ src, int V, bool on, float (&x)[NPT]) {
   const int tid = threadIdx.x;
   if constexpr (VEC) {
 #pragma unroll
-    for (int k = 0; k < kStochNpt / 4; ++k) {
-      const int v = row_index<true>(4 * k, tid);
+    for (int k = 0; k < NPT / 4; ++k) {
+      const int v = row_index<true, NPT>(4 * k, tid);
       const f32x4 q =
           __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (on && v < V ? v : 0)));
       x[4 * k] = q.x;
@@ -305,8 +333,8 @@ __device__ inline void load_row(const float* __restrict__ src, int V, bool on,
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < kStochNpt; ++e) {
-      const int v = row_index<false>(e, tid);
+    for (int e = 0; e < NPT; ++e) {
+      const int v = row_index<false, NPT>(e, tid);
       x[e] = __builtin_nontemporal_load(src + (on && v < V ? v : 0));
     }
   }
@@ -317,60 +345,112 @@ __device__ inline void load_row(const float* __restrict__ src, int V, bool on,
 // the acceptance tests at sizes far inside their near-tie band.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// exp2((l - M) * s), times `scale`, for the entries inside the row, else 0.
-template <bool VEC>
-__device__ inline void row_probs(float (&x)[kStochNpt], int V, float M, float s, float scale) {
-#pragma unroll
-  for (int e = 0; e < kStochNpt; ++e) {
-    const float p = exp2_fast((x[e] - M) * s) * scale;
-    x[e] = row_index<VEC>(e, threadIdx.x) < V ? p : 0.f;
-  }
-}
-
-// The residual weight max(0, p_v - c q_v) of one row entry from its
-// probabilities P = p_v and Q = q_v, both rounded to fp32: a fused
-// multiply-add and a max in fp32.
+// The residual weight of one row entry, up to a common factor, from the
+// rounded exponentials P = Z_t p_v and Q = Z_d q_v:
+//   max(0, p_v - c q_v) = max(0, P - c' Q) / Z_t  with  c' = c Z_t / Z_d,
+// a fused multiply-add and a max in fp32.
 __device__ __forceinline__ float resid(float P, float Q, float c) {
   return fmaxf(0.f, fmaf(-c, Q, P));
 }
 // Sum of the residual weights of entries [k*EPT, k*EPT+EPT) of a thread: fp32
 // within the (at most 4) entries, fp64 from there on.
-template <int EPT>
-__device__ __forceinline__ double resid_group(const float (&P)[kStochNpt],
-                                              const float (&Q)[kStochNpt], float c, int k) {
+template <int EPT, int NPT>
+__device__ __forceinline__ double resid_group(const float (&P)[NPT], const float (&Q)[NPT],
+                                              float c, int k) {
   float s = resid(P[k * EPT], Q[k * EPT], c);
 #pragma unroll
   for (int j = 1; j < EPT; ++j) s += resid(P[k * EPT + j], Q[k * EPT + j], c);
   return (double)s;
 }
 // A thread's share of sum_v max(0, p_v - c q_v).
-template <bool VEC>
-__device__ __forceinline__ double resid_sum(const float (&P)[kStochNpt],
-                                            const float (&Q)[kStochNpt], float c) {
+template <bool VEC, int NPT>
+__device__ __forceinline__ double resid_sum(const float (&P)[NPT], const float (&Q)[NPT],
+                                            float c) {
   constexpr int EPT = VEC ? 4 : 1;
   double s = 0.0;
 #pragma unroll
-  for (int k = 0; k < kStochNpt / EPT; ++k) s += resid_group<EPT>(P, Q, c, k);
+  for (int k = 0; k < NPT / EPT; ++k) s += resid_group<EPT>(P, Q, c, k);
   return s;
 }
 
+// v plus the partner lane's v at exchange stage S: the lanes l ^ 32, l ^ 16,
+// l ^ 8 (a row rotation by 8), l ^ 7 (mirror inside 8 lanes), l ^ 2, l ^ 1.
+// Both partners add the same two operands, so they end with the same bits.
+template <int S>
+__device__ __forceinline__ double xsum(double v) {
+  if constexpr (S <= 1) {
+    double x0, x1;
+    swap_rows<S == 0>(v, x0, x1);
+    return x0 + x1;
+  } else if constexpr (S == 2) {
+    return v + dpp_f64<0x128>(v);  // row_ror:8
+  } else if constexpr (S == 3) {
+    return v + dpp_f64<0x141>(v);  // row_half_mirror
+  } else if constexpr (S == 4) {
+    return v + dpp_f64<0x4E>(v);  // quad_perm [2,3,0,1]
+  } else {
+    return v + dpp_f64<0xB1>(v);  // quad_perm [1,0,3,2]
+  }
+}
+// One halving exchange: every one of the M values is summed with the
+// partner's, and a lane keeps the half selected by the stage's lane bit
+// (bit 5 - S, which the two partners hold with opposite values).
+template <int S, int M>
+__device__ __forceinline__ void halve(double (&cur)[16], int lane) {
+  const bool upper = lane & (32 >> S);
+#pragma unroll
+  for (int j = 0; j < M / 2; ++j) {
+    const double lo = xsum<S>(cur[j]), hi = xsum<S>(cur[j + M / 2]);
+    cur[j] = upper ? hi : lo;
+  }
+}
+// The wavefront sums of N (8 or 16) per-lane values, all at once: log2(N)
+// halving exchanges leave each lane with the partial sum of one value (value
+// k in lanes k * 64 / N ...), and the remaining exchanges complete it.
+template <int N>
+__device__ inline void wave_sum_n(const double (&t)[N], double (&S)[N]) {
+  static_assert(N == 8 || N == 16, "8 or 16 values");
+  const int lane = threadIdx.x % ST_WAVE;
+  double cur[16];
+#pragma unroll
+  for (int j = 0; j < N; ++j) cur[j] = t[j];
+  halve<0, N>(cur, lane);
+  halve<1, N / 2>(cur, lane);
+  halve<2, N / 4>(cur, lane);
+  if constexpr (N == 16)
+    halve<3, 2>(cur, lane);
+  else
+    cur[0] = xsum<3>(cur[0]);
+  cur[0] = xsum<4>(cur[0]);
+  cur[0] = xsum<5>(cur[0]);
+  const uint64_t bits = (uint64_t)__double_as_longlong(cur[0]);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int src = k * (ST_WAVE / N);
+    const uint32_t lo32 = __builtin_amdgcn_readlane((int)(uint32_t)bits, src);
+    const uint32_t hi32 = __builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), src);
+    S[k] = __longlong_as_double((long long)(((uint64_t)hi32 << 32) | lo32));
+  }
+}
+
 struct DrawLds {
-  double wsum[kStochWaves];
+  double wsum[kMaxWaves];
   int pick, tie;
 };
 
-// Inverse-CDF draw from the residual w_v = max(0, p_v - c q_v) in ascending
-// vocab order: the smallest v whose running sum exceeds u * sum(w).  Every
+// Inverse-CDF draw from the residual w_v = max(0, P_v - c Q_v) in ascending
+// vocab order (any positive multiple of it draws the same token): the
+// smallest v whose running sum exceeds u * sum(w).  Every
 // wavefront reduces its slice of the row; the prefix over the slices (summed
 // in wavefront order by every thread) names the slice that crosses the
 // threshold, and that wavefront alone locates the tile, then the entry.  The
 // threshold test at every level compares running sums that begin where the
 // previous level's left off.  Returns sum(w); pick and tie are set when it is
 // positive.
-template <bool VEC>
-__device__ inline double draw_residual(const float (&P)[kStochNpt], const float (&Q)[kStochNpt],
-                                       float c, double u, DrawLds& s, int& pick, int& tie) {
-  constexpr int EPT = VEC ? 4 : 1, NT = kStochNpt / EPT;
+template <bool VEC, int NPT>
+__device__ inline double draw_residual(const float (&P)[NPT], const float (&Q)[NPT], float c,
+                                       double u, DrawLds& s, int& pick, int& tie) {
+  constexpr int EPT = VEC ? 4 : 1, NT = NPT / EPT, NW = kStochMaxV / NPT / ST_WAVE;
   const int tid = threadIdx.x, lane = tid % ST_WAVE;
   const int w = __builtin_amdgcn_readfirstlane(tid / ST_WAVE);
   const double mine = wave_sum(resid_sum<VEC>(P, Q, c));
@@ -381,12 +461,12 @@ __device__ inline double draw_residual(const float (&P)[kStochNpt], const float 
   }
   __syncthreads();
   double total = 0.0;
-  for (int i = 0; i < kStochWaves; ++i) total += s.wsum[i];
+  for (int i = 0; i < NW; ++i) total += s.wsum[i];
   const double thr = u * total;
   // the slice: running sums over the wavefronts' slices, in the same order
   double base = 0.0, run0 = 0.0;
   int ws = -1;
-  for (int i = 0; i < kStochWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const double next = run0 + s.wsum[i];
     if (ws < 0 && next > thr) {
       ws = i;
@@ -407,12 +487,7 @@ __device__ inline double draw_residual(const float (&P)[kStochNpt], const float 
     double run = base, tbase = base;
     int kt = -1, klast = -1;
     double lbase = base;
-    for (int k = 0; k < NT; ++k) {
-      double part = 0.0;
-#pragma unroll
-      for (int kk = 0; kk < NT; ++kk)
-        if (kk == k) part = resid_group<EPT>(P, Q, cw, kk);
-      const double tsum = wave_sum(part);
+    auto visit = [&](int k, double tsum) {
       const double next = run + tsum;
       if (kt < 0 && next > thr) {
         kt = k;
@@ -423,21 +498,45 @@ __device__ inline double draw_residual(const float (&P)[kStochNpt], const float 
         lbase = run;
       }
       run = next;
+    };
+    if constexpr (NT == 8 || NT == 16) {
+      double t[NT], S[NT];
+#pragma unroll
+      for (int k = 0; k < NT; ++k) t[k] = resid_group<EPT>(P, Q, cw, k);
+      wave_sum_n<NT>(t, S);
+#pragma unroll
+      for (int k = 0; k < NT; ++k) visit(k, S[k]);
+    } else {
+      for (int k = 0; k < NT; ++k) {
+        double part = 0.0;
+#pragma unroll
+        for (int kk = 0; kk < NT; ++kk)
+          if (kk == k) part = resid_group<EPT>(P, Q, cw, kk);
+        visit(k, wave_sum(part));
+      }
     }
     if (kt < 0) {  // rounding: no tile crosses; take the last positive one
       kt = klast;
       tbase = lbase;
     }
     // the entry: a scan over the lanes of tile kt
-    float wt[EPT];
+    float sp[EPT], sq[EPT], wt[EPT];
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) wt[j] = 0.f;
+    for (int j = 0; j < EPT; ++j) {
+      sp[j] = P[j];
+      sq[j] = Q[j];
+    }
 #pragma unroll
-    for (int k = 0; k < NT; ++k)
-      if (k == kt) {
+    for (int k = 1; k < NT; ++k) {
+      const bool sel = k == kt;
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) wt[j] = resid(P[k * EPT + j], Q[k * EPT + j], cw);
+      for (int j = 0; j < EPT; ++j) {
+        sp[j] = sel ? P[k * EPT + j] : sp[j];
+        sq[j] = sel ? Q[k * EPT + j] : sq[j];
       }
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) wt[j] = resid(sp[j], sq[j], cw);
     double sub = 0.0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) sub += (double)wt[j];
@@ -469,7 +568,7 @@ __device__ inline double draw_residual(const float (&P)[kStochNpt], const float 
     if (lane == who) {
       const int j = fm ? found : last;
       const double ce_lo = fm ? lo_edge : last_lo, ce_hi = fm ? hi_edge : last_hi;
-      const int v = row_index<VEC>(kt * EPT + j, tid);
+      const int v = row_index<VEC, NPT>(kt * EPT + j, tid);
       s.pick = v;
       s.tie = fabs(ce_hi - thr) < kTieEps * total || (v > 0 && fabs(ce_lo - thr) < kTieEps * total);
     }
@@ -480,147 +579,128 @@ __device__ inline double draw_residual(const float (&P)[kStochNpt], const float 
   return total;
 }
 
-// Row statistics, persistent: workgroup g reduces rows g, g + G, g + 2G, ...
-// (G = gridDim.x), with the next row's loads in flight while the current row
-// is reduced (two register buffers, used alternately).
-template <bool VEC>
-__device__ inline void finish_row(const StochArgs& g, const float (&x)[kStochNpt], int r,
-                                  float* red_f, double* red_d) {
-  float m = -INFINITY;
-  bool finite = true;
-#pragma unroll
-  for (int e = 0; e < kStochNpt; ++e) {
-    finite &= (bool)isfinite(x[e]);
-    m = fmaxf(m, x[e]);
-  }
-  if (!finite) st::set_status(g.status, ST_STATUS_NONFINITE);
-  m = block_max<kStochBlock>(m, red_f);
-  const float sc = kLog2e / g.temperature;
-  // fp32 within a group of (at most 4) consecutive entries, fp64 from there on
-  constexpr int EPT = VEC ? 4 : 1;
-  double z = 0.0;
-#pragma unroll
-  for (int k = 0; k < kStochNpt / EPT; ++k) {
-    float zk = exp2_fast((x[k * EPT] - m) * sc);
-#pragma unroll
-    for (int j = 1; j < EPT; ++j) zk += exp2_fast((x[k * EPT + j] - m) * sc);
-    z += (double)(row_index<VEC>(k * EPT, threadIdx.x) < g.V ? zk : 0.f);
-  }
-  z = block_sum<kStochBlock>(z, red_d);
-  if (threadIdx.x == 0) {
-    RowStat rs;
-    rs.M = m;
-    rs.pad = 0;
-    rs.Z = z;
-    g.stat[r] = rs;
-  }
-}
-
-template <bool VEC>
-__global__ void __launch_bounds__(kStochBlock)
-row_stat_kernel(StochArgs g) {
-  __shared__ float red_f[kStochWaves];
-  __shared__ double red_d[kStochWaves];
-  const int R = 2 * g.T, G = gridDim.x;
-  // Past the last row a buffer is refilled from row 0 (read by every
-  // workgroup, so from cache) and never used: the loads stay unconditional.
-  auto row = [&](int r) { return r < R ? ((r & 1) ? g.dl : g.tl) + (size_t)(r >> 1) * g.V : g.tl; };
-  float xa[kStochNpt], xb[kStochNpt];
-  int r = blockIdx.x;
-  load_row<VEC>(row(r), g.V, true, xa);
-  while (true) {
-    load_row<VEC>(row(r + G), g.V, true, xb);
-    finish_row<VEC>(g, xa, r, red_f, red_d);
-    r += G;
-    if (r >= R) break;
-    load_row<VEC>(row(r + G), g.V, true, xa);
-    finish_row<VEC>(g, xb, r, red_f, red_d);
-    r += G;
-    if (r >= R) break;
-  }
-}
-
 struct NodeLds {
-  int place[4];  // b, lo, n, ok
   uint64_t kid_mask[ST_MAX_NODES / 64];
   int kids[ST_MAX_NODES];  // children, ascending
   double px[ST_MAX_NODES], qx[ST_MAX_NODES], ua[ST_MAX_NODES];  // per child
   int ok[ST_MAX_NODES];                                           // token in range
-  double red[kStochWaves];
+  float redf[2 * kMaxWaves];
+  double red[2 * kMaxWaves];
   double u_draw;
   DrawLds draw;
 };
 
-// One workgroup per node u decides what the walk would do on reaching u: test
-// u's children in ascending order, child c with token x accepted iff
-// u_acc(c) q_u[x] < r[x] with r starting at p_u, and draw the replacement
-// token from r when no child is accepted.  The first test needs only the row
-// statistics; u's rows are read (into registers, as fp32 probabilities) once
-// a child is rejected, for the residual masses of the later tests and the
-// draw.  A leaf reads its target row only, to draw from p_u.
+// One workgroup per node u, which holds u's two logit rows in registers from
+// start to end: it reduces them to their softmax statistics (max M and
+// Z = sum of exp2((l - M) * log2e / T), terms rounded to fp32, groups of four
+// summed in fp32 and the groups in fp64), then decides what the walk would do
+// on reaching u: test u's children in ascending order, child c with token x
+// accepted iff u_acc(c) q_u[x] < r[x] with r starting at p_u, and draw the
+// replacement token from r when no child is accepted (a leaf draws from p_u).
+// The tree is read before the rows' loads are issued, so that waiting for it
+// never waits for them.
 template <bool VEC>
-__global__ void __launch_bounds__(kStochBlock)
+__global__ void __launch_bounds__(kNodeBlock)
 stoch_node_kernel(StochArgs g) {
+  constexpr int NPT = kStochMaxV / kNodeBlock, EPT = VEC ? 4 : 1;
   __shared__ NodeLds s;
-  const int tid = threadIdx.x, t = blockIdx.x;
-  if (tid < ST_WAVE) {  // node t's request: the number of request starts at or before t, less one
-    int cnt = 0;
-    for (int b0 = 0; b0 < g.B; b0 += ST_WAVE) {
-      const int b = b0 + tid;
-      cnt += __popcll(__ballot(b < g.B && g.node_off[b] <= t));
-    }
-    const int b = cnt > 0 ? cnt - 1 : 0;
-    const int lo = g.node_off[b], hi = g.node_off[b + 1];
-    if (tid == 0) {
-      s.place[0] = b;
-      s.place[1] = lo;
-      s.place[2] = hi - lo;
-      s.place[3] = (lo >= 0) & (hi <= g.T) & (hi - lo >= 1) & (hi - lo <= g.max_nodes) &
-                   (t >= lo) & (t < hi);
-    }
+  const int tid = threadIdx.x, lane = tid % ST_WAVE, t = blockIdx.x;
+  // node t's request: the number of request starts at or before t, less one
+  int cnt = 0;
+  for (int b0 = 0; b0 < g.B; b0 += ST_WAVE) {
+    const int b = b0 + lane;
+    cnt += __popcll(__ballot(b < g.B && g.node_off[b] <= t));
   }
+  const int b = __builtin_amdgcn_readfirstlane(cnt > 0 ? cnt - 1 : 0);
+  const int lo = g.node_off[b], hi = g.node_off[b + 1], n = hi - lo, i = t - lo;
+  if (!((lo >= 0) & (hi <= g.T) & (n >= 1) & (n <= g.max_nodes) & (i >= 0) & (i < n)))
+    return;  // the walk flags the request
+  // this thread's node of the request (clamped, so the loads are unconditional)
+  const int c = tid < n ? tid : 0;
+  const int par = g.parent[lo + c], tok = g.tokens[lo + c];
+  float P[NPT], Q[NPT];
+  load_row<VEC>(g.tl + (size_t)t * g.V, g.V, true, P);
+  load_row<VEC>(g.dl + (size_t)t * g.V, g.V, true, Q);
   if (tid < ST_MAX_NODES / 64) s.kid_mask[tid] = 0;
-  __syncthreads();
-  if (!s.place[3]) return;  // the walk flags the request
-  const int b = s.place[0], lo = s.place[1], n = s.place[2], i = t - lo;
-  if (tid < n && tid > i && g.parent[lo + tid] == i)
-    atomicOr((unsigned long long*)&s.kid_mask[tid >> 6], 1ull << (tid & 63));
-  if (tid == kStochBlock - 1) {
+  if (tid == kNodeBlock - 1) {
     double ua, us;
     node_uniforms(g.seed, g.offset, b, i, ua, us);
     s.u_draw = us;
   }
-  const RowStat rt = g.stat[2 * t];
-  const double a = 1.0 / rt.Z;
-  const float sc = kLog2e / g.temperature, af = (float)a;
+  __syncthreads();
+  const bool kid = tid < n && tid > i && par == i;
+  if (kid) atomicOr((unsigned long long*)&s.kid_mask[tid >> 6], 1ull << (tid & 63));
   __syncthreads();
   int nk = 0;
 #pragma unroll
   for (int w = 0; w < ST_MAX_NODES / 64; ++w) nk += __popcll(s.kid_mask[w]);
+  // each child's token logits (issued now, used after the statistics)
+  int rank = 0;
+  float lt = 0.f, ld = 0.f;
+  const bool ok = kid && tok >= 0 && tok < g.V;
+  if (kid) {
+    rank = __popcll(s.kid_mask[tid >> 6] & ((1ull << (tid & 63)) - 1));
+    for (int w = 0; w < (tid >> 6); ++w) rank += __popcll(s.kid_mask[w]);
+    const size_t at = (size_t)t * g.V + (ok ? tok : 0);
+    lt = g.tl[at];
+    ld = g.dl[at];
+  }
+
+  // statistics of both rows
+  float mt = -INFINITY, md = -INFINITY;
+  bool finite = true;
+#pragma unroll
+  for (int e = 0; e < NPT; ++e) {
+    finite &= (bool)isfinite(P[e]) & (bool)isfinite(Q[e]);
+    mt = fmaxf(mt, P[e]);
+    md = fmaxf(md, Q[e]);
+  }
+  if (!finite) st::set_status(g.status, ST_STATUS_NONFINITE);
+  block_max2<kNodeBlock>(mt, md, s.redf);
+  const float sc = kLog2e / g.temperature;
+  // the rows become their exponentials exp2((l - M) * s) in place, exactly 0
+  // past the row end (the draft row only where it is used: a node with
+  // children); a group's terms are summed in fp32, the groups in fp64
+  const int kin = groups_inside<VEC, NPT>(g.V, tid);
+  double zt = 0.0, zd = 0.0;
+#pragma unroll
+  for (int k = 0; k < NPT / EPT; ++k) {
+    const bool in = k < kin;
+    float st_ = 0.f, sd_ = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const float e = exp2_fast((P[k * EPT + j] - mt) * sc);
+      P[k * EPT + j] = in ? e : 0.f;
+      st_ += P[k * EPT + j];
+    }
+    if (nk) {
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const float e = exp2_fast((Q[k * EPT + j] - md) * sc);
+        Q[k * EPT + j] = in ? e : 0.f;
+        sd_ += Q[k * EPT + j];
+      }
+    }
+    zt += (double)st_;
+    zd += (double)sd_;
+  }
+  block_sum2<kNodeBlock>(zt, zd, s.red);
+  const double a = 1.0 / zt;
 
   if (nk == 0) {  // a leaf: the walk stops here with r = p_u
-    float P[kStochNpt];
-    load_row<VEC>(g.tl + (size_t)t * g.V, g.V, true, P);
-    row_probs<VEC>(P, g.V, rt.M, sc, af);
     int token, tie;
     draw_residual<VEC>(P, P, 0.f, s.u_draw, s.draw, token, tie);
     if (tid == 0) g.verdict[t] = NodeVerdict{-1, 0, token, tie};
     return;
   }
 
-  const RowStat rd = g.stat[2 * t + 1];
-  const double bq = 1.0 / rd.Z;
-  if (tid < n && ((s.kid_mask[tid >> 6] >> (tid & 63)) & 1)) {
-    int rank = __popcll(s.kid_mask[tid >> 6] & ((1ull << (tid & 63)) - 1));
-    for (int w = 0; w < (tid >> 6); ++w) rank += __popcll(s.kid_mask[w]);
+  const double bq = 1.0 / zd, ratio = zt / zd;  // c' = c Z_t / Z_d
+  if (kid) {
     s.kids[rank] = tid;
-    const int x = g.tokens[lo + tid];
-    const bool ok = x >= 0 && x < g.V;
     s.ok[rank] = ok;
     if (ok) {
-      const size_t at = (size_t)t * g.V + x;
-      s.px[rank] = (double)exp2_fast((g.tl[at] - rt.M) * sc) * a;
-      s.qx[rank] = (double)exp2_fast((g.dl[at] - rd.M) * sc) * bq;
+      s.px[rank] = (double)exp2_fast((lt - mt) * sc) * a;
+      s.qx[rank] = (double)exp2_fast((ld - md) * sc) * bq;
       double ua, us;
       node_uniforms(g.seed, g.offset, b, tid, ua, us);
       s.ua[rank] = ua;
@@ -629,12 +709,12 @@ stoch_node_kernel(StochArgs g) {
   __syncthreads();
 
   int ties = 0, accepted = -1;
-  double c = 0.0, D = 1.0;
+  double cc = 0.0, D = 1.0;
   // child k's test against r = max(0, p - c q) / D
   auto test = [&](int k) {
     if (!s.ok[k]) return false;
     const double qv = s.qx[k];
-    const double r = fmax(0.0, s.px[k] - c * qv) / D;
+    const double r = fmax(0.0, s.px[k] - cc * qv) / D;
     const double lhs = s.ua[k] * qv;
     ties += fabs(r - lhs) < kTieEps;
     return lhs < r;
@@ -643,37 +723,35 @@ stoch_node_kernel(StochArgs g) {
   if (test(0)) {
     accepted = s.kids[0];
   } else {
-    float P[kStochNpt], Q[kStochNpt];
-    load_row<VEC>(g.tl + (size_t)t * g.V, g.V, true, P);
-    load_row<VEC>(g.dl + (size_t)t * g.V, g.V, true, Q);
-    row_probs<VEC>(P, g.V, rt.M, sc, af);
-    row_probs<VEC>(Q, g.V, rd.M, sc, (float)bq);
     // after each rejection r <- max(0, r - q) renormalised, i.e. c <- c + D
     for (int k = 1; k < nk && accepted < 0; ++k) {
-      const double cn = c + D;
-      const double Dn = block_sum<kStochBlock>(resid_sum<VEC>(P, Q, (float)cn), s.red);
+      const double cn = cc + D;
+      const double Dn =
+          a * block_sum<kNodeBlock>(resid_sum<VEC>(P, Q, (float)(cn * ratio)), s.red, k & 1);
       if (Dn > 0.0) {
-        c = cn;
+        cc = cn;
         D = Dn;
       }
       if (test(k)) accepted = s.kids[k];
     }
     if (accepted < 0) {  // every child rejected: draw from the final residual
-      const double total = draw_residual<VEC>(P, Q, (float)(c + D), s.u_draw, s.draw, token, tie);
+      const double total =
+          draw_residual<VEC>(P, Q, (float)((cc + D) * ratio), s.u_draw, s.draw, token, tie);
       if (!(total > 0.0)) {  // the last rejection left no mass: r unchanged
         __syncthreads();
-        draw_residual<VEC>(P, Q, (float)c, s.u_draw, s.draw, token, tie);
+        draw_residual<VEC>(P, Q, (float)(cc * ratio), s.u_draw, s.draw, token, tie);
       }
     }
   }
   if (tid == 0) g.verdict[t] = NodeVerdict{accepted, ties, token, tie};
 }
 
-// One wavefront per request follows the verdicts from the root: step to the
-// accepted child while there is one (at most max_depth steps), then emit the
-// token drawn at the stop node.
+// One wavefront per request follows the verdicts from the root (staged in
+// LDS): step to the accepted child while there is one (at most max_depth
+// steps), then emit the token drawn at the stop node.
 __global__ void __launch_bounds__(ST_WAVE)
 stoch_walk_kernel(StochArgs g) {
+  __shared__ NodeVerdict v[ST_MAX_NODES];
   __shared__ int path[kMaxPath + 1];
   const int b = blockIdx.x, lane = threadIdx.x;
   const int lo = g.node_off[b], hi = g.node_off[b + 1], n = hi - lo;
@@ -683,27 +761,30 @@ stoch_walk_kernel(StochArgs g) {
   }
   const int bits = check_request(g.parent, g.tokens, lo, n, g.V);
   if (bits) st::set_status(g.status, bits);
+  for (int i = lane; i < n; i += ST_WAVE) v[i] = g.verdict[lo + i];
+  st::wave_lds_sync();
   int L = 0, ties = 0, last = -1;
-  bool over = false;
   if (lane == 0) {
     int u = 0;
+    bool over = false;
     path[0] = 0;
     while (true) {
-      const NodeVerdict v = g.verdict[lo + u];
-      ties += v.ties;
-      if (v.accepted <= u || v.accepted >= n) {  // -1: stop here
-        last = v.token;
-        ties += v.token_tie;
-        break;
-      }
+      ties += v[u].ties;
+      const int c = v[u].accepted;
+      if (c <= u || c >= n) break;  // -1: stop here
       if (L == g.max_depth) {
         over = true;
         break;
       }
-      path[++L] = v.accepted;
-      u = v.accepted;
+      path[++L] = c;
+      u = c;
     }
-    if (over) st::set_status(g.status, ST_STATUS_PATH_OVERFLOW);
+    if (over) {
+      st::set_status(g.status, ST_STATUS_PATH_OVERFLOW);
+    } else {
+      last = v[u].token;
+      ties += v[u].token_tie;
+    }
     if (g.near_ties) g.near_ties[b] = ties;
   }
   L = __shfl(L, 0, ST_WAVE);
@@ -761,8 +842,7 @@ extern "C" int st_verify_greedy(const st_tree* tree, int V, const int32_t* token
 extern "C" size_t st_verify_stochastic_workspace(const st_tree* tree, int V) {
   (void)V;
   if (st::check_tree_host(tree)) return 0;
-  return st::align_up((size_t)tree->total_nodes * (2 * sizeof(RowStat) + sizeof(NodeVerdict)),
-                      256);
+  return st::align_up((size_t)tree->total_nodes * sizeof(NodeVerdict), 256);
 }
 
 extern "C" int st_verify_stochastic(const st_tree* tree, int V, const int32_t* tokens,
@@ -779,21 +859,15 @@ extern "C" int st_verify_stochastic(const st_tree* tree, int V, const int32_t* t
   if (V > kStochMaxV || tree->max_depth + 1 > kMaxPath) return ST_E_UNSUPPORTED;
   if (ws_bytes < st_verify_stochastic_workspace(tree, V)) return ST_E_WORKSPACE;
   const int T = tree->total_nodes;
-  RowStat* stat = (RowStat*)workspace;
-  const StochArgs g{tree->node_off, tree->parent, tokens, target_logits, draft_logits, stat,
-                    (NodeVerdict*)(stat + 2 * T), tree->B, T, V, tree->max_nodes,
-                    tree->max_depth, temperature, seed, offset, accept_len, accept_nodes,
-                    out_tokens, near_ties, status};
+  const StochArgs g{tree->node_off, tree->parent, tokens, target_logits, draft_logits,
+                    (NodeVerdict*)workspace, tree->B, T, V, tree->max_nodes, tree->max_depth,
+                    temperature, seed, offset, accept_len, accept_nodes, out_tokens, near_ties,
+                    status};
   hipStream_t s = (hipStream_t)stream;
-  // one persistent statistics workgroup per compute unit
-  const int stat_wg = 2 * T < st::device_cus() ? 2 * T : st::device_cus();
-  if ((V & 3) == 0) {
-    hipLaunchKernelGGL(row_stat_kernel<true>, dim3(stat_wg), dim3(kStochBlock), 0, s, g);
-    hipLaunchKernelGGL(stoch_node_kernel<true>, dim3(T), dim3(kStochBlock), 0, s, g);
-  } else {
-    hipLaunchKernelGGL(row_stat_kernel<false>, dim3(stat_wg), dim3(kStochBlock), 0, s, g);
-    hipLaunchKernelGGL(stoch_node_kernel<false>, dim3(T), dim3(kStochBlock), 0, s, g);
-  }
+  if ((V & 3) == 0)
+    hipLaunchKernelGGL(stoch_node_kernel<true>, dim3(T), dim3(kNodeBlock), 0, s, g);
+  else
+    hipLaunchKernelGGL(stoch_node_kernel<false>, dim3(T), dim3(kNodeBlock), 0, s, g);
   if ((rc = st::check_launch())) return rc;
   hipLaunchKernelGGL(stoch_walk_kernel, dim3(tree->B), dim3(ST_WAVE), 0, s, g);
   return st::check_launch();
