@@ -36,7 +36,7 @@ int fill_compact_args(int B, int Hkv, int D, st_dtype dtype, void* k_cache, void
   c.src_slot = src_slot;
   c.new_len = new_len;
   c.status = status;
-  c.walk = false;
+  c.walk = kWalkNone;
   c.g = GreedyWalkArgs{};
   return ST_OK;
 }

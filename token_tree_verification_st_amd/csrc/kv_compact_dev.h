@@ -2,7 +2,8 @@
 // update of the SpecInfer news article, "Token 樹驗證器"): slot P + j of every
 // kv head takes what slot P + path[j] held before, for j = 0..L.  Shared by
 // st_kv_compact and by the last launch of st_verification_step, where each
-// compaction workgroup can also run the greedy walk that yields the path.
+// compaction workgroup can also run the walk (greedy or stochastic) that
+// yields the path.
 //
 // The copy is in place.  A path strictly increases (path[j] >= j), so the
 // source of a later move is never the destination of an earlier one.  One
@@ -12,6 +13,7 @@
 // is read, and later batches read only slots no earlier move wrote.
 #pragma once
 #include "greedy_walk_dev.h"
+#include "stoch_walk_dev.h"
 
 namespace st {
 
@@ -26,9 +28,12 @@ struct CompactArgs {
   int32_t* src_slot;
   int32_t* new_len;
   int32_t* status;
-  bool walk;            // take the path from a greedy walk run in the workgroup
-  GreedyWalkArgs g;     // ... with these inputs (the step's argmax partials)
+  int walk;             // 0: the path is in accept_len / accept_nodes; 1: run the
+  GreedyWalkArgs g;     // greedy walk with these inputs (the argmax partials);
+  StochWalkArgs sw;     // 2: the stochastic walk over these node verdicts
 };
+
+enum { kWalkNone = 0, kWalkGreedy = 1, kWalkStochastic = 2 };
 
 // Moves of one workgroup (blockDim.x == 256): request b, cache row set y
 // (< Hkv: keys of head y, else values of head y - Hkv), path[0..L] of the
@@ -68,21 +73,25 @@ __device__ inline void kv_compact_rows(const CompactArgs& c, int b, int y, int L
 }
 
 // One compaction workgroup: the path comes from accept_len / accept_nodes,
-// or (c.walk) from the greedy walk that the first wavefront runs here; row
-// set 0's workgroup also stores the walk's outputs.
+// or from the walk that the first wavefront runs here; row set 0's
+// workgroup also stores the walk's outputs.
 __device__ inline void kv_compact_block(const CompactArgs& c, int b, int y) {
-  if (!c.walk) {
+  if (c.walk == kWalkNone) {
     kv_compact_rows(c, b, y, c.accept_len[b], c.accept_nodes + (size_t)b * c.max_path);
     return;
   }
-  __shared__ GreedyWalkLds s;
+  __shared__ union {
+    GreedyWalkLds gr;
+    StochWalkLds sw;
+  } s;
   __shared__ int sL;
   if (threadIdx.x < ST_WAVE) {
-    const int L = greedy_walk_wave(c.g, b, s, y == 0);
+    const int L = c.walk == kWalkGreedy ? greedy_walk_wave(c.g, b, s.gr, y == 0)
+                                        : stoch_walk_wave(c.sw, b, s.sw, y == 0);
     if (threadIdx.x == 0) sL = L;
   }
   __syncthreads();
-  kv_compact_rows(c, b, y, sL, s.path);
+  kv_compact_rows(c, b, y, sL, c.walk == kWalkGreedy ? s.gr.path : s.sw.path);
 }
 
 }  // namespace st

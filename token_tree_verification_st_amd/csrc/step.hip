@@ -1,8 +1,9 @@
 // st_verification_step: acceptance, attention with in-kernel ancestor masks,
-// then the split merge and the KV compaction in one launch.  For greedy
-// acceptance the vocab argmax runs inside the attention launch when it fits
-// (one 8192-entry slice per workgroup) and the tree walk inside the
-// compaction workgroups, so the step is two launches.
+// then the split merge and the KV compaction in one launch, whose workgroups
+// also walk the trees.  For greedy acceptance the vocab argmax runs inside
+// the attention launch when it fits (one 8192-entry slice per workgroup), so
+// the step is two launches; for stochastic acceptance the node kernel runs
+// first.
 #include "step_internal.h"
 
 #include <math.h>
@@ -52,25 +53,32 @@ extern "C" int st_verification_step(const st_tree* tree, const st_step* s, void*
                              s->src_slot, s->new_len, status, c);
   if (rc) return rc;
 
-  // Greedy: each compaction workgroup of the last launch walks its request's
-  // tree itself (a few microseconds of latency-bound work that then needs no
-  // launch of its own).  Stochastic: both acceptance kernels go first.
+  // Each compaction workgroup of the last launch walks its request's tree
+  // itself (a few microseconds of latency-bound work that then needs no
+  // launch of its own).  Stochastic: the node kernel goes first.
   if (s->draft_logits) {
-    rc = st_verify_stochastic(tree, s->V, s->tokens, s->logits, s->draft_logits, s->temperature,
-                              s->seed, s->offset, s->accept_len, s->accept_nodes, s->out_tokens,
-                              s->near_ties, workspace, vws, status, stream);
+    rc = st::stochastic_prepare(tree, s->V, s->tokens, s->logits, s->draft_logits,
+                                s->temperature, s->accept_len, s->accept_nodes, s->out_tokens,
+                                s->near_ties, workspace, vws, status, c.sw);
+    c.walk = st::kWalkStochastic;
   } else {
     rc = st::greedy_prepare(tree, s->V, s->tokens, s->logits, s->accept_len, s->accept_nodes,
                             s->out_tokens, workspace, vws, status, c.g);
-    c.walk = true;
+    c.walk = st::kWalkGreedy;
   }
   if (rc) return rc;
+  if (s->draft_logits &&
+      (rc = st::stochastic_node_launch(c.sw, s->logits, s->draft_logits, s->temperature, s->seed,
+                                       s->offset, tree->B, stream)))
+    return rc;
   // Greedy with bf16 attention: when there is at most one argmax slice per
   // attention workgroup (and V is a multiple of 4), the workgroups reduce them
   // in their prologue (the slice's loads overlap the first K/V chunk's);
   // otherwise the argmax gets a launch of its own first.
-  const st::ArgmaxJob job{s->logits, (st::ArgmaxPart*)c.g.part, s->V, c.g.nslices,
-                          tree->total_nodes * c.g.nslices, status};
+  const st::ArgmaxJob job =
+      s->draft_logits ? st::ArgmaxJob{}
+                      : st::ArgmaxJob{s->logits, (st::ArgmaxPart*)c.g.part, s->V, c.g.nslices,
+                                      tree->total_nodes * c.g.nslices, status};
   const bool fuse_argmax =
       !s->draft_logits && s->dtype == ST_BF16 && (s->V & 3) == 0 &&
       job.units <= st::attention_workgroups(tree, s->Hq, s->Hkv, s->D, s->dtype, s->max_prefix);

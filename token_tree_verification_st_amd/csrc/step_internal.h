@@ -14,6 +14,18 @@ int greedy_prepare(const st_tree* tree, int V, const int32_t* tokens, const floa
                    void* workspace, size_t ws_bytes, int32_t* status, GreedyWalkArgs& walk);
 int greedy_argmax_launch(const GreedyWalkArgs& walk, const float* logits, void* stream);
 
+// st_verify_stochastic in parts (verify.hip): check the arguments and fill the
+// walk's inputs (the node verdicts go to the start of `workspace`), launch the
+// node kernel.  The one-call step runs the walk in its compaction workgroups.
+int stochastic_prepare(const st_tree* tree, int V, const int32_t* tokens,
+                       const float* target_logits, const float* draft_logits, float temperature,
+                       int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                       int32_t* near_ties, void* workspace, size_t ws_bytes, int32_t* status,
+                       StochWalkArgs& walk);
+int stochastic_node_launch(const StochWalkArgs& walk, const float* target_logits,
+                           const float* draft_logits, float temperature, uint64_t seed,
+                           uint64_t offset, int B, void* stream);
+
 // Vocab argmax slices handed to the attention launch: its workgroups load them
 // while their first K/V chunk is in flight and reduce them before their loop.
 struct ArgmaxJob {

@@ -262,13 +262,9 @@ __device__ inline void node_uniforms(uint64_t seed, uint64_t offset, int req, in
 
 // ---------------------------------------------------------------- stochastic
 
-// What the walk needs from a node: its first accepted child (local index, -1
-// if none), the near ties among its tests and, when no child is accepted, the
-// replacement token drawn there and whether that draw was a near tie.
-struct NodeVerdict {
-  int accepted, ties, token, token_tie;
-};
+using st::NodeVerdict;
 
+// Inputs of the node kernel.
 struct StochArgs {
   const int32_t* node_off;
   const int32_t* parent;
@@ -276,13 +272,9 @@ struct StochArgs {
   const float* tl;
   const float* dl;
   NodeVerdict* verdict;
-  int B, T, V, max_nodes, max_depth;
+  int B, T, V, max_nodes;
   float temperature;
   uint64_t seed, offset;
-  int32_t* accept_len;
-  int32_t* accept_nodes;
-  int32_t* out_tokens;
-  int32_t* near_ties;
   int32_t* status;
 };
 
@@ -746,52 +738,11 @@ stoch_node_kernel(StochArgs g) {
   if (tid == 0) g.verdict[t] = NodeVerdict{accepted, ties, token, tie};
 }
 
-// One wavefront per request follows the verdicts from the root (staged in
-// LDS): step to the accepted child while there is one (at most max_depth
-// steps), then emit the token drawn at the stop node.
+// One wavefront per request follows the verdicts from the root.
 __global__ void __launch_bounds__(ST_WAVE)
-stoch_walk_kernel(StochArgs g) {
-  __shared__ NodeVerdict v[ST_MAX_NODES];
-  __shared__ int path[kMaxPath + 1];
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const int lo = g.node_off[b], hi = g.node_off[b + 1], n = hi - lo;
-  if (lo < 0 || hi > g.T || n < 1 || n > g.max_nodes) {
-    if (lane == 0) st::set_status(g.status, ST_STATUS_BAD_PARENT);
-    return;
-  }
-  const int bits = check_request(g.parent, g.tokens, lo, n, g.V);
-  if (bits) st::set_status(g.status, bits);
-  for (int i = lane; i < n; i += ST_WAVE) v[i] = g.verdict[lo + i];
-  st::wave_lds_sync();
-  int L = 0, ties = 0, last = -1;
-  if (lane == 0) {
-    int u = 0;
-    bool over = false;
-    path[0] = 0;
-    while (true) {
-      ties += v[u].ties;
-      const int c = v[u].accepted;
-      if (c <= u || c >= n) break;  // -1: stop here
-      if (L == g.max_depth) {
-        over = true;
-        break;
-      }
-      path[++L] = c;
-      u = c;
-    }
-    if (over) {
-      st::set_status(g.status, ST_STATUS_PATH_OVERFLOW);
-    } else {
-      last = v[u].token;
-      ties += v[u].token_tie;
-    }
-    if (g.near_ties) g.near_ties[b] = ties;
-  }
-  L = __shfl(L, 0, ST_WAVE);
-  last = __shfl(last, 0, ST_WAVE);
-  st::wave_lds_sync();
-  write_path_outputs(b, L, g.max_depth, path, g.tokens, lo, last, g.accept_len, g.accept_nodes,
-                     g.out_tokens);
+stoch_walk_kernel(st::StochWalkArgs g) {
+  __shared__ st::StochWalkLds s;
+  st::stoch_walk_wave(g, blockIdx.x, s, true);
 }
 
 }  // namespace
@@ -845,12 +796,11 @@ extern "C" size_t st_verify_stochastic_workspace(const st_tree* tree, int V) {
   return st::align_up((size_t)tree->total_nodes * sizeof(NodeVerdict), 256);
 }
 
-extern "C" int st_verify_stochastic(const st_tree* tree, int V, const int32_t* tokens,
-                                    const float* target_logits, const float* draft_logits,
-                                    float temperature, uint64_t seed, uint64_t offset,
-                                    int32_t* accept_len, int32_t* accept_nodes,
-                                    int32_t* out_tokens, int32_t* near_ties, void* workspace,
-                                    size_t ws_bytes, int32_t* status, void* stream) {
+int st::stochastic_prepare(const st_tree* tree, int V, const int32_t* tokens,
+                           const float* target_logits, const float* draft_logits,
+                           float temperature, int32_t* accept_len, int32_t* accept_nodes,
+                           int32_t* out_tokens, int32_t* near_ties, void* workspace,
+                           size_t ws_bytes, int32_t* status, st::StochWalkArgs& walk) {
   int rc = st::check_tree_host(tree);
   if (rc) return rc;
   if (V < 1 || !tokens || !target_logits || !draft_logits || !accept_len || !accept_nodes ||
@@ -858,17 +808,39 @@ extern "C" int st_verify_stochastic(const st_tree* tree, int V, const int32_t* t
     return ST_E_INVALID;
   if (V > kStochMaxV || tree->max_depth + 1 > kMaxPath) return ST_E_UNSUPPORTED;
   if (ws_bytes < st_verify_stochastic_workspace(tree, V)) return ST_E_WORKSPACE;
-  const int T = tree->total_nodes;
-  const StochArgs g{tree->node_off, tree->parent, tokens, target_logits, draft_logits,
-                    (NodeVerdict*)workspace, tree->B, T, V, tree->max_nodes, tree->max_depth,
-                    temperature, seed, offset, accept_len, accept_nodes, out_tokens, near_ties,
-                    status};
+  walk = st::StochWalkArgs{tree->node_off, tree->parent, tokens, (const NodeVerdict*)workspace,
+                           tree->total_nodes, V, tree->max_nodes, tree->max_depth, accept_len,
+                           accept_nodes, out_tokens, near_ties, status};
+  return ST_OK;
+}
+
+int st::stochastic_node_launch(const st::StochWalkArgs& w, const float* target_logits,
+                               const float* draft_logits, float temperature, uint64_t seed,
+                               uint64_t offset, int B, void* stream) {
+  const StochArgs g{w.node_off, w.parent, w.tokens, target_logits, draft_logits,
+                    const_cast<NodeVerdict*>(w.verdict), B, w.T, w.V, w.max_nodes, temperature,
+                    seed, offset, w.status};
   hipStream_t s = (hipStream_t)stream;
-  if ((V & 3) == 0)
-    hipLaunchKernelGGL(stoch_node_kernel<true>, dim3(T), dim3(kNodeBlock), 0, s, g);
+  if ((w.V & 3) == 0)
+    hipLaunchKernelGGL(stoch_node_kernel<true>, dim3(w.T), dim3(kNodeBlock), 0, s, g);
   else
-    hipLaunchKernelGGL(stoch_node_kernel<false>, dim3(T), dim3(kNodeBlock), 0, s, g);
-  if ((rc = st::check_launch())) return rc;
-  hipLaunchKernelGGL(stoch_walk_kernel, dim3(tree->B), dim3(ST_WAVE), 0, s, g);
+    hipLaunchKernelGGL(stoch_node_kernel<false>, dim3(w.T), dim3(kNodeBlock), 0, s, g);
+  return st::check_launch();
+}
+
+extern "C" int st_verify_stochastic(const st_tree* tree, int V, const int32_t* tokens,
+                                    const float* target_logits, const float* draft_logits,
+                                    float temperature, uint64_t seed, uint64_t offset,
+                                    int32_t* accept_len, int32_t* accept_nodes,
+                                    int32_t* out_tokens, int32_t* near_ties, void* workspace,
+                                    size_t ws_bytes, int32_t* status, void* stream) {
+  st::StochWalkArgs w;
+  int rc = st::stochastic_prepare(tree, V, tokens, target_logits, draft_logits, temperature,
+                                  accept_len, accept_nodes, out_tokens, near_ties, workspace,
+                                  ws_bytes, status, w);
+  if (rc || (rc = st::stochastic_node_launch(w, target_logits, draft_logits, temperature, seed,
+                                             offset, tree->B, stream)))
+    return rc;
+  hipLaunchKernelGGL(stoch_walk_kernel, dim3(tree->B), dim3(ST_WAVE), 0, (hipStream_t)stream, w);
   return st::check_launch();
 }
