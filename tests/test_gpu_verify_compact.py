@@ -143,6 +143,54 @@ def test_stochastic_equal_distributions_accept_first_children():
         assert an[b, :al[b] + 1].tolist() == path
 
 
+def _star_tree(n):
+    parent = np.array([-1] + [0] * (n - 1), dtype=np.int32)
+    level = np.array([0] + [1] * (n - 1), dtype=np.int32)
+    return parent, level
+
+
+@pytest.mark.parametrize("V", [32768, 32764, 32767, 32001])
+def test_stochastic_full_vocab_long_chains(V):
+    """The largest vocabulary a node workgroup holds (no padding), a partial
+    last slice with 16-byte loads (V % 4 == 0) and the scalar path
+    (V % 4 != 0).  Uniform draft tokens are mostly rejected, so the star root's
+    23 children run a long chain of residual passes before the draw."""
+    rng = np.random.default_rng(V)
+    trees = [_star_tree(24), tree_random_attach(rng, 40, 6), tree_chain(8)]
+    wl = build_workload("full", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=V, prefix_lens=[1] * 3,
+                        trees=trees, max_depth=8, token_rule="uniform", logit_sigma=3.0,
+                        draft_noise_sigma=1.0, temperature=0.7)
+    dw = to_device(wl)
+    for off in range(3):
+        wl.rng_offset = off
+        dw.rng_offset = off
+        _, (al, _, _), res, _ = _stochastic_check(wl, dw)
+        say(f"V={V} offset {off}: accept_len {al.tolist()}")
+
+
+def test_stochastic_path_overflow():
+    """Draft equal to target: every test accepts (u q < p = q), so a chain
+    longer than max_depth overflows; status bit 8 and a -1 last token."""
+    rng = np.random.default_rng(17)
+    trees = [tree_chain(12), tree_chain(3)]
+    wl = build_workload("ovf", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=1000, prefix_lens=[1] * 2,
+                        trees=trees, max_depth=5, token_rule="uniform", logit_sigma=3.0,
+                        draft_noise_sigma=0.0, temperature=0.7)
+    dw = to_device(wl)
+    stp.run_verify(dw, stochastic=True)
+    torch.cuda.synchronize()
+    al, an, ot = device_paths(dw)
+    res = oracle.verify_stochastic(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.draft_logits,
+                                   wl.V, wl.temperature, wl.rng_seed, wl.rng_offset, wl.max_depth)
+    assert al.tolist() == res["accept_len"].tolist() == [5, 2]
+    assert np.array_equal(an, res["accept_nodes"])
+    assert np.array_equal(ot[0], res["out_tokens"][0]) and ot[0, 5] == -1
+    # request 1 stops at its leaf and draws there: equal unless a near tie
+    assert np.array_equal(ot[1, :2], res["out_tokens"][1, :2])
+    assert ot[1, 2] == res["out_tokens"][1, 2] or res["bonus_tie"][1]
+    assert status_of(dw) == res["status"] == oracle.STATUS_PATH_OVERFLOW
+
+
 # ---------------------------------------------------------------- compaction and whole step
 
 

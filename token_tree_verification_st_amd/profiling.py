@@ -23,7 +23,8 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ATTENTION_SOURCES = ("csrc/attention.hip", "csrc/st_internal.h", "csrc/step_internal.h",
-                     "csrc/kv_compact_dev.h", "csrc/greedy_walk_dev.h", "build.py")
+                     "csrc/kv_compact_dev.h", "csrc/greedy_walk_dev.h", "csrc/stoch_walk_dev.h",
+                     "build.py")
 ATTENTION_KERNELS = ("attn_stream_kernel", "attn_valu_kernel", "attn_combine_kernel<")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
