@@ -25,6 +25,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published
 REPLICA_BYTES = 1 << 30        # cycle at least this much input per step round
 
 
@@ -56,6 +58,21 @@ def algorithmic_attention_bytes(wl) -> int:
         N = int(wl.node_off[b + 1] - wl.node_off[b])
         P = int(wl.prefix_len[b])
         n += (P + N) * wl.Hkv * wl.D * 2 * s + 2 * N * wl.Hq * wl.D * s
+    return n
+
+
+def algorithmic_attention_flops(wl) -> int:
+    """Useful matrix work: every query row against the keys it attends (the
+    request's prefix plus the node's root path), 2 flops per multiply-add in
+    Q K^T and again in P V."""
+    n = 0
+    for b in range(wl.B):
+        lo, hi = int(wl.node_off[b]), int(wl.node_off[b + 1])
+        P = int(wl.prefix_len[b])
+        depth = [0] * (hi - lo)
+        for i in range(1, hi - lo):
+            depth[i] = depth[int(wl.parent[lo + i])] + 1
+        n += wl.Hq * ((hi - lo) * P + sum(depth) + (hi - lo)) * wl.D * 4
     return n
 
 
@@ -188,9 +205,20 @@ def main():
     from token_tree_verification_st_amd.profiling import read_traffic
     traffic = read_traffic(args.traffic or os.path.join(
         ROOT, "profiles", f"attention_{wl.name}_traffic.md"))
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+    attn_flops = algorithmic_attention_flops(wl)
+    tflops = attn_flops / (attn_us * 1e-6) / 1e12
+    peak_tf = MFMA_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    # the bound is whichever of the two ideal times is longer
+    mfma_bound = attn_flops / (peak_tf * 1e12) > attn_bytes / (HBM_PEAK_GBS * 1e9)
+    roof = {"bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(tflops if mfma_bound else achieved, 1),
+            "peak": peak_tf if mfma_bound else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round(tflops / peak_tf if mfma_bound else achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
             "kernel": "st_tree_attention", "algorithmic_bytes": attn_bytes,
+            "algorithmic_flops": attn_flops, "hbm_gbs": round(achieved, 1),
+            "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / peak_tf, 4),
             "avg_launch_us": round(attn_us, 3),
             "timing": f"HIP events around a graph of {K} back-to-back st_tree_attention calls"}
     al = reps[0].buf["accept_len"].cpu().numpy() if wl.V else np.zeros(wl.B)
