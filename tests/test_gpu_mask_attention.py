@@ -104,9 +104,10 @@ def test_attention_forced_splits_and_combine(split_keys, monkeypatch):
 
 
 # bf16 kernel variants by plan shape: (64-row groups per workgroup, 16-row
-# blocks per wavefront) = (1,1) (1,2) (1,4) (2,4) (4,4) for shapes 0..4
+# blocks per wavefront) = (1,1) (1,2) (1,4) (2,4) (4,4) for shapes 0..4, then two
+# workgroups per CU: (2,2) (4,2) for shapes 5, 6
 @pytest.mark.parametrize("derive", [False, True])
-@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6])
 def test_attention_every_kernel_shape(shape, derive, monkeypatch):
     """derive: no mask is passed, the kernel builds it from the parent array."""
     monkeypatch.setenv("ST_ATTN_SHAPE", str(shape))

@@ -329,22 +329,34 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
           s[rb][kb][j] = (win >> (16 * kb + 4 * grp + j)) & 1u ? s[rb][kb][j] : -INFINITY;
     }
   }
-  bf16x8 pb[RBW];
+  // every row block's chunk maximum first, then one (rarely taken) branch
+  // for the rescales, so that the row blocks' exponentials below form one
+  // straight run of code that the scheduler can interleave with the MFMAs
+  float mc[RBW];
+  bool any = false;
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     float t = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
                     fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
     t = xor16_max(t);
     t = xor32_max(t);
-    const float mc = t * c;  // c > 0: the max of the scaled scores
-    const bool need = mc > m[rb] + kLazy;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m[rb] - mc) : 1.f;
-      m[rb] = need ? mc : m[rb];
+    mc[rb] = t * c;  // c > 0: the max of the scaled scores
+    any |= mc[rb] > m[rb] + kLazy;
+  }
+  if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      const bool need = mc[rb] > m[rb] + kLazy;
+      const float alpha = need ? fast_exp2(m[rb] - mc[rb]) : 1.f;
+      m[rb] = need ? mc[rb] : m[rb];
       l[rb] *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[rb][db] *= alpha;
     }
+  }
+  bf16x8 pb[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
     const float nm = m[rb] == -INFINITY ? 0.f : -m[rb];
     float ps = 0.f;
 #pragma unroll
@@ -393,9 +405,11 @@ __device__ __forceinline__ void write_row_out(const AttnArgs& a, int grow, int g
   if (a.lse && grp == 0) a.lse[grow] = (m + log2f(l)) * kLn2;
 }
 
-// RWV row groups of RBW 16-row blocks; KWV = 4 / RWV key groups.
-template <int D, int NSTAGE, int RWV, int RBW>
-__global__ void __launch_bounds__(256, 1)
+// RWV row groups of RBW 16-row blocks; KWV = 4 / RWV key groups; MINB
+// workgroups per CU (two let one workgroup's softmax run while the other's
+// MFMAs do).
+template <int D, int NSTAGE, int RWV, int RBW, int MINB = 1>
+__global__ void __launch_bounds__(256, MINB)
 attn_stream_kernel(AttnArgs a) {
   constexpr int KWV = 4 / RWV;
   constexpr bool PRIVATE = RWV == 1;                  // every wavefront owns its ring
@@ -950,10 +964,16 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
     p.rwv = rows_max <= 64 ? 1 : rows_max <= 128 ? 2 : 4;
     p.rbw = rows_max <= 16 ? 1 : rows_max <= 32 ? 2 : 4;
     if (rows_max <= 64 && (long)t->B * Hkv * 2 <= 256) p.rbw = 2;
-    const int forced = env_int("ST_ATTN_SHAPE", -1);  // 0..4: (1,1) (1,2) (1,4) (2,4) (4,4)
-    if (forced >= 0 && forced <= 4) {
-      p.rwv = forced <= 2 ? 1 : forced == 3 ? 2 : 4;
-      p.rbw = forced == 0 ? 1 : forced == 1 ? 2 : 4;
+    // More than 64 rows a kv head: the MFMAs and the softmax of a chunk take
+    // longer than its loads, so run two workgroups per CU (32 rows a
+    // wavefront, half the registers), whose softmax and MFMA phases overlap.
+    if (rows_max > 64) p.rbw = 2;
+    // 0..6: (1,1) (1,2) (1,4) (2,4) (4,4), then two workgroups per CU: (2,2) (4,2)
+    const int forced = env_int("ST_ATTN_SHAPE", -1);
+    if (forced >= 0 && forced <= 6) {
+      static const int kRwv[7] = {1, 1, 1, 2, 4, 2, 4}, kRbw[7] = {1, 2, 4, 4, 4, 2, 2};
+      p.rwv = kRwv[forced];
+      p.rbw = kRbw[forced];
     }
     p.RB = 16 * p.rbw * p.rwv;
     gran = 32;
@@ -962,8 +982,10 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
   const long keys_max = (long)max_prefix + t->max_nodes;
   const long base = (long)t->B * Hkv * p.n_rblk;
   // aim for about `target` workgroups over the whole batch (one per CU for
-  // the streaming kernel); splits are even, in multiples of `gran` keys
-  const long target = env_int("ST_ATTN_TARGET_WG", p.stream ? 256 : 512);
+  // the streaming kernel, two for its two-per-CU shapes); splits are even, in
+  // multiples of `gran` keys
+  const bool two_per_cu = p.stream && p.rbw == 2 && p.rwv > 1;
+  const long target = env_int("ST_ATTN_TARGET_WG", !p.stream ? 512 : two_per_cu ? 512 : 256);
   long ns = (target + base - 1) / base;
   if (ns < 1) ns = 1;
   long ks = (keys_max + ns - 1) / ns;
@@ -1052,18 +1074,22 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
   if (p.stream) {
     const dim3 sblock(256);
     const int shape = p.rwv * 8 + p.rbw;
-#define ST_LAUNCH_STREAM(RWV_, RBW_, NS128_, NS64_)                                          \
-  if (shape == RWV_ * 8 + RBW_) {                                                            \
-    if (D == 128)                                                                            \
-      hipLaunchKernelGGL((attn_stream_kernel<128, NS128_, RWV_, RBW_>), grid, sblock, 0, s, a); \
-    else                                                                                     \
-      hipLaunchKernelGGL((attn_stream_kernel<64, NS64_, RWV_, RBW_>), grid, sblock, 0, s, a);   \
+#define ST_LAUNCH_STREAM(RWV_, RBW_, NS128_, NS64_, MINB_)                                    \
+  if (shape == RWV_ * 8 + RBW_) {                                                              \
+    if (D == 128)                                                                              \
+      hipLaunchKernelGGL((attn_stream_kernel<128, NS128_, RWV_, RBW_, MINB_>), grid, sblock, 0, \
+                         s, a);                                                                \
+    else                                                                                       \
+      hipLaunchKernelGGL((attn_stream_kernel<64, NS64_, RWV_, RBW_, MINB_>), grid, sblock, 0,   \
+                         s, a);                                                                \
   }
-    ST_LAUNCH_STREAM(1, 1, 2, 4)
-    ST_LAUNCH_STREAM(1, 2, 2, 4)
-    ST_LAUNCH_STREAM(1, 4, 2, 4)
-    ST_LAUNCH_STREAM(2, 4, 4, 8)
-    ST_LAUNCH_STREAM(4, 4, 8, 16)
+    ST_LAUNCH_STREAM(1, 1, 2, 4, 1)
+    ST_LAUNCH_STREAM(1, 2, 2, 4, 1)
+    ST_LAUNCH_STREAM(1, 4, 2, 4, 1)
+    ST_LAUNCH_STREAM(2, 4, 4, 8, 1)
+    ST_LAUNCH_STREAM(4, 4, 8, 16, 1)
+    ST_LAUNCH_STREAM(2, 2, 2, 4, 2)
+    ST_LAUNCH_STREAM(4, 2, 4, 8, 2)
 #undef ST_LAUNCH_STREAM
   } else {
     if (D == 128) hipLaunchKernelGGL((attn_valu_kernel<float, 128>), grid, block, 0, s, a);

@@ -83,7 +83,9 @@ __device__ inline void argmax_slice_finish(const ArgmaxRegs& r, int V, int t, in
                         : base + tid + (4 * k + j) * kArgmaxBlock;
       if (v < V) {
         const float x = r.x[k][j];
-        finite = finite && isfinite(x);
+        // exponent bits all set: inf or NaN (a bit test, whatever the
+        // compiler may assume about NaNs)
+        finite = finite && (__float_as_uint(x) & 0x7f800000u) != 0x7f800000u;
         argmax_merge(best, bidx, x, v);
       }
     }
