@@ -862,6 +862,16 @@ __device__ inline void combine_block(const AttnArgs& a, int blk) {
   const int d = 4 * (threadIdx.x % LPR);
   const int TH = a.T * a.Hq;
   if (grow >= TH) return;
+  // Every row has a.NS partial slots: the first CHUNK splits' loads go out
+  // before the row's request (and with it its split count) is known.
+  float2 ml[CHUNK];
+  f32x4 x[CHUNK];
+#pragma unroll
+  for (int j = 0; j < CHUNK; ++j) {
+    const size_t pr = (size_t)min(j, a.NS - 1) * TH + grow;
+    ml[j] = a.ws_ml[pr];
+    x[j] = *(const f32x4*)(a.ws_acc + pr * D + d);
+  }
   const int t = grow / a.Hq;
   const int b = st::request_of(a.node_off, a.B, t);
   const ReqInfo rq = request_info(a, b);
@@ -870,27 +880,27 @@ __device__ inline void combine_block(const AttnArgs& a, int blk) {
   float M = -INFINITY, L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < ns; s0 += CHUNK) {
-    float2 ml[CHUNK];
-    f32x4 x[CHUNK];
+    if (s0 > 0) {
 #pragma unroll
-    for (int j = 0; j < CHUNK; ++j) {
-      const int s = min(s0 + j, ns - 1);
-      const size_t pr = (size_t)s * TH + grow;
-      ml[j] = a.ws_ml[pr];
-      x[j] = *(const f32x4*)(a.ws_acc + pr * D + d);
+      for (int j = 0; j < CHUNK; ++j) {
+        const int s = min(s0 + j, ns - 1);
+        const size_t pr = (size_t)s * TH + grow;
+        ml[j] = a.ws_ml[pr];
+        x[j] = *(const f32x4*)(a.ws_acc + pr * D + d);
+      }
     }
     float Mc = M;
 #pragma unroll
     for (int j = 0; j < CHUNK; ++j)
       if (s0 + j < ns) Mc = fmaxf(Mc, ml[j].x);
     const float ref = Mc == -INFINITY ? 0.f : Mc;
-    const float sc = exp2f(M - ref);  // rescale what is merged so far
+    const float sc = fast_exp2(M - ref);  // rescale what is merged so far
     L *= sc;
     o *= sc;
 #pragma unroll
     for (int j = 0; j < CHUNK; ++j) {
       if (s0 + j < ns) {
-        const float w = exp2f(ml[j].x - ref);  // empty split: exp2(-inf) = 0
+        const float w = fast_exp2(ml[j].x - ref);  // empty split: exp2(-inf) = 0
         L += w * ml[j].y;
         o += w * x[j];
       }
