@@ -168,6 +168,40 @@ def test_stochastic_full_vocab_long_chains(V):
         say(f"V={V} offset {off}: accept_len {al.tolist()}")
 
 
+@pytest.mark.parametrize("V", [1, 2, 4, 5])
+def test_stochastic_tiny_vocab(V):
+    """One to five tokens: a single 16-byte group (V = 4) or single values on the
+    scalar path; with V = 1 every test accepts and the draw returns token 0."""
+    rng = np.random.default_rng(40 + V)
+    trees = [tree_random_attach(rng, 12, 4), tree_chain(5), _star_tree(6)]
+    wl = build_workload("tiny", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=V, prefix_lens=[1] * 3,
+                        trees=trees, max_depth=5, token_rule="uniform", logit_sigma=2.0,
+                        draft_noise_sigma=1.0, temperature=0.9)
+    dw = to_device(wl)
+    for off in range(4):
+        wl.rng_offset = off
+        dw.rng_offset = off
+        _, (al, _, ot), _, _ = _stochastic_check(wl, dw)
+        if V == 1:
+            assert (ot[np.arange(wl.B), al] == 0).all()
+
+
+def test_stochastic_widest_node():
+    """A request at the node limit (256): a root with 255 children, drafts
+    drawn uniformly (mostly rejected), so the root runs up to 254 residual
+    passes before the draw."""
+    rng = np.random.default_rng(77)
+    wl = build_workload("wide", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=4000, prefix_lens=[1],
+                        trees=[_star_tree(256)], max_depth=2, token_rule="uniform",
+                        logit_sigma=3.0, draft_noise_sigma=1.0, temperature=0.7)
+    dw = to_device(wl)
+    for off in range(2):
+        wl.rng_offset = off
+        dw.rng_offset = off
+        _, (al, _, _), _, _ = _stochastic_check(wl, dw)
+        say(f"widest node offset {off}: accept_len {al.tolist()}")
+
+
 def test_stochastic_path_overflow():
     """Draft equal to target: every test accepts (u q < p = q), so a chain
     longer than max_depth overflows; status bit 8 and a -1 last token."""
