@@ -136,6 +136,8 @@ __device__ inline double block_sum(double v, double* lds, int set) {
   return tree_fold<NW>(lds + set * NW, [](double a, double b) { return a + b; });
 }
 // Two reductions sharing one barrier: (x, y) -> (max x, max y) and sums.
+// They fill both slot sets of `lds`, so a barrier must separate them from
+// the previous reduction on that array and from the next one.
 template <int BLOCK>
 __device__ inline void block_max2(float& x, float& y, float* lds) {
   constexpr int NW = BLOCK / ST_WAVE;
@@ -162,14 +164,6 @@ __device__ inline void block_sum2(double& x, double& y, double* lds) {
   x = tree_fold<NW>(lds, [](double a, double b) { return a + b; });
   y = tree_fold<NW>(lds + NW, [](double a, double b) { return a + b; });
 }
-template <int BLOCK>
-__device__ inline float block_max(float v, float* lds, int set) {
-  constexpr int NW = BLOCK / ST_WAVE;
-  v = wave_max(v);
-  if (threadIdx.x % ST_WAVE == 0) lds[set * NW + threadIdx.x / ST_WAVE] = v;
-  __syncthreads();
-  return tree_fold<NW>(lds + set * NW, [](float a, float b) { return fmaxf(a, b); });
-}
 
 using st::argmax_merge;
 using st::ArgmaxPart;
@@ -194,21 +188,6 @@ row_argmax_kernel(const float* __restrict__ logits, int V, ArgmaxPart* __restric
     st::argmax_slice_load<false>(logits, V, blockIdx.x, blockIdx.y, r);
     st::argmax_slice_finish<false>(r, V, blockIdx.x, blockIdx.y, gridDim.y, part, status, scratch);
   }
-}
-
-// Checks the request's parents and draft tokens; returns the status bits.
-__device__ inline int check_request(const int32_t* parent, const int32_t* tokens, int lo, int n,
-                                    int V) {
-  int bits = 0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int p = parent[lo + i];
-    if (i == 0 ? (p != -1) : (p < 0 || p >= i)) bits |= ST_STATUS_BAD_PARENT;
-    if (i > 0) {
-      const int tok = tokens[lo + i];
-      if (tok < 0 || tok >= V) bits |= ST_STATUS_BAD_TOKEN;
-    }
-  }
-  return bits;
 }
 
 __device__ inline void write_path_outputs(int b, int L, int max_depth, const int* path,
