@@ -18,6 +18,8 @@ Sources (web pages, cited by title and section):
   [SpecInfer-dev]   "SpecInfer：基于树结构的LLM推测性推理加速技术", §2.1
                     (tree node with parent pointer; tree_attention with a
                     [batch, heads, seq, seq] mask; longest verified prefix)
+  [Specular]        Specular project page, "主要特性" (greedy output identical
+                    to the original model's)
   [SpecDec]         speculative-decoding explainer (intelliparadigm.com),
                     §2.2 (acceptance probability min(1, p_main/p_draft),
                     left-to-right check, replacement at the first rejection,
@@ -48,3 +50,13 @@ from .attention import decode_values, tree_attention  # noqa: F401
 from .philox import philox4x64_10, uniforms_for_node  # noqa: F401
 from .verify import verify_greedy, verify_stochastic  # noqa: F401
 from .compact import kv_compact  # noqa: F401
+from .layer import (  # noqa: F401
+    ROPE_THETA,
+    ar_greedy_decode,
+    linear,
+    node_positions,
+    prefix_cache,
+    rope,
+    rope_angles,
+    tree_layer,
+)

@@ -25,6 +25,8 @@ from .tree import dense_tree_mask
 def decode_values(arr: np.ndarray, dtype: str) -> np.ndarray:
     """Values as fp64.  ``bf16`` arrays hold raw 16-bit patterns: a bfloat16 is
     the upper half of a float32."""
+    if dtype == "f64":
+        return np.asarray(arr, dtype=np.float64)
     if dtype == "f32":
         return np.asarray(arr, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":

@@ -22,3 +22,4 @@ from .workloads import (  # noqa: F401
     tree_random_attach,
     tree_beam_plus_leaves,
 )
+from .model import model_config, model_weights  # noqa: F401,E402
