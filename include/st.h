@@ -242,6 +242,55 @@ size_t st_verification_step_workspace(const st_tree* tree, const st_step* step);
 int st_verification_step(const st_tree* tree, const st_step* step, void* workspace,
                          size_t ws_bytes, int32_t* status, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The target layer around verification.  The pages fix no architecture; the
+ * calls below are the pieces one attention layer needs to run over a token
+ * tree (news article, "研究現狀": decoded tokens' keys and values are cached;
+ * explainer §3.2: all candidates are scored in one forward pass).  Every
+ * matrix is bf16, row-major.
+ * ------------------------------------------------------------------------- */
+
+/* out[t][:] = table[tokens[t]][:] for t < T: a gather of d-wide bf16 rows
+ * (d a multiple of 8, table [V][d]).  A token outside [0, V) sets
+ * ST_STATUS_BAD_TOKEN and gives a row of zeros.  table and out 16-byte
+ * aligned. */
+int st_embed(int T, int d, int V, const int32_t* tokens, const void* table, void* out,
+             int32_t* status, void* stream);
+
+/* Rotary position embedding of the tree nodes' queries and keys, and the
+ * append of their keys and values to the cache.  qkv [T][(Hq + 2 Hkv) D]
+ * holds each node's Hq query heads, then Hkv key heads, then Hkv value heads
+ * (the output of the fused projection).  Node i of request b sits at position
+ * pos = prefix_len[b] + depth(i), the index its token has in the sequence of
+ * its root path; dims j and j + D/2 (j < D/2) of a query or key head are
+ * turned by the angle pos * theta^(-2j/D) ("rotate half" form; theta = 10000
+ * is the usual value).  Writes q_out[T][Hq][D] (the rotated queries, as
+ * st_tree_attention takes them), and for every kv head g the rotated key and
+ * the value at slot prefix_len[b] + i of k_cache / v_cache [B][Hkv][S_max][D].
+ * D is 64 or 128.  A bad parent array sets ST_STATUS_BAD_PARENT, a prefix
+ * length outside [0, max_prefix] or slots past S_max ST_STATUS_BAD_PREFIX;
+ * such a request's nodes write nothing.  Angles are formed in fp64, the
+ * rotation in fp32, rounded once to bf16. */
+int st_tree_rope_append(const st_tree* tree, int Hq, int Hkv, int D, float theta,
+                        const void* qkv, const int32_t* prefix_len, int max_prefix, int S_max,
+                        void* q_out, void* k_cache, void* v_cache, int32_t* status,
+                        void* stream);
+
+/* Bytes of workspace st_linear needs for these sizes (0 if none, or on
+ * invalid sizes). */
+size_t st_linear_workspace(int M, int N, int K);
+
+/* y[M][N] = x[M][K] . w[N][K]^T (+ residual[M][N] if not NULL): bf16 inputs,
+ * fp32 accumulation, y in y_dtype (ST_BF16 rounds to nearest even, ST_F32 as
+ * accumulated).  w is a weight matrix in the usual [out][in] layout, read once
+ * from HBM; x is the few dozen to few hundred rows of a token tree.  K must be
+ * a multiple of 64 and N of 4 (ST_E_UNSUPPORTED otherwise); all pointers
+ * 16-byte aligned.  The reduction may be split over workgroups (then the
+ * workspace holds fp32 partials that a second kernel adds in a fixed order:
+ * results do not depend on timing). */
+int st_linear(int M, int N, int K, const void* x, const void* w, const void* residual, void* y,
+              st_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
+
 /* Text for a return code or for a status bit (host memory, static). */
 const char* st_status_str(int code);
 

@@ -27,7 +27,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("st_tree_mask", "st_tree_attention", "st_verify_greedy", "st_verify_stochastic",
-              "st_kv_compact", "st_status_str"):
+              "st_kv_compact", "st_status_str", "st_embed", "st_tree_rope_append", "st_linear",
+              "st_linear_workspace"):
         assert n in names
 
 
@@ -45,6 +46,12 @@ def test_host_only_calls():
     assert st.st_mask_words(256) == 4
     assert "workspace" in st.st_status_str(-3)
     assert "parent" in st.st_status_str(1)
+    # projections: K a multiple of 64 and N of 4; a split reduction needs fp32 partials
+    assert st.st_linear_workspace(64, 4096, 100) == 0
+    assert st.st_linear_workspace(64, 4094, 4096) == 0
+    assert st.st_linear_workspace(64, 32000, 4096) == 0          # 500 feature tiles: no split
+    ws = st.st_linear_workspace(64, 4096, 4096)                   # 64 tiles: split
+    assert ws > 0 and ws % (64 * 4096 * 4) == 0
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

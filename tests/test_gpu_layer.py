@@ -1,0 +1,326 @@
+"""GPU parity of the layer pieces around verification (embedding, skinny bf16
+projection, rotary embedding with tree-KV append) against the oracle, and the
+end-to-end property: a one-layer model verifying draft trees step after step
+on the GPU emits the tokens of plain autoregressive greedy decoding (oracle,
+fp64) with the same weights."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.attention import decode_values
+from synth import f32_to_bf16_bits, model_config, model_weights, tree_random_attach
+from tests.gpu_util import require_gpu, say
+from tests.test_oracle_layer import draft_tree
+import token_tree_verification_st_amd as st
+from token_tree_verification_st_amd.layer import (LayerWeights, layer_buffers, layer_forward,
+                                                  layer_step)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
+
+
+def _bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _rand_bf16(rng, shape, sigma=1.0):
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma))
+
+
+# ---------------------------------------------------------------- st_linear
+
+
+def _linear_case(M, N, K, out_f32, with_res, seed, env=None):
+    rng = np.random.default_rng(seed)
+    x = _rand_bf16(rng, (M, K))
+    w = _rand_bf16(rng, (N, K), 1.0 / np.sqrt(K))
+    r = _rand_bf16(rng, (M, N)) if with_res else None
+    xd, wd = _bf16_dev(x), _bf16_dev(w)
+    rd = _bf16_dev(r) if with_res else None
+    y = torch.full((M, N), float("nan"), dtype=torch.float32 if out_f32 else torch.bfloat16,
+                   device="cuda")
+    old = {}
+    for k, v in (env or {}).items():
+        old[k] = os.environ.get(k)
+        os.environ[k] = str(v)
+    try:
+        need = st.st_linear_workspace(M, N, K)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        st.st_linear(xd, wd, y, residual=rd, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                del os.environ[k]
+            else:
+                os.environ[k] = v
+    got = y.float().cpu().numpy().astype(np.float64)
+    X, W = decode_values(x, "bf16"), decode_values(w, "bf16")
+    R = decode_values(r, "bf16") if with_res else None
+    ref = oracle.linear(X, W, R)
+    # fp32 accumulation of K products: |err| <= K * 2^-24 * sum |x w| (+ |r|);
+    # a bf16 result adds half an ulp, at most 2^-8 of the value
+    mag = np.abs(X) @ np.abs(W).T + (np.abs(R) if with_res else 0.0)
+    tol = K * 2.0 ** -24 * mag + (2.0 ** -8 * np.abs(ref) if not out_f32 else 0.0) + 1e-30
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got))
+    bad = err > tol
+    assert not bad.any(), f"{bad.sum()} outputs off, worst {err.max():.3e}"
+    return float((err / (mag + 1e-30)).max())
+
+
+@pytest.mark.parametrize("M,N,K,out_f32,res", [
+    (1, 64, 64, True, False),          # smallest
+    (7, 384, 256, True, False),        # few rows, one row block of 32
+    (64, 512, 256, False, False),      # one tree, q/k/v shape of the small model
+    (100, 1000, 512, True, True),      # ragged rows (two blocks of 64) and features
+    (33, 4096, 4096, False, True),     # reduction split into fp32 partials
+    (576, 1024, 256, False, True),     # nine row blocks
+])
+def test_linear_matches_oracle(M, N, K, out_f32, res):
+    say(f"st_linear M={M} N={N} K={K} f32={out_f32} residual={res}")
+    rel = _linear_case(M, N, K, out_f32, res, seed=M + N + K)
+    say(f"  worst error / sum|x w| = {rel:.2e}")
+
+
+@pytest.mark.parametrize("env", [{"ST_LINEAR_STAGES": 4}, {"ST_LINEAR_KSPLIT": 2},
+                                 {"ST_LINEAR_KSPLIT": 16}, {"ST_LINEAR_STAGES": 4,
+                                                             "ST_LINEAR_KSPLIT": 8}])
+def test_linear_ring_depths_and_splits(env):
+    say(f"st_linear forced {env}")
+    _linear_case(64, 768, 1024, False, True, seed=7, env=env)
+    _linear_case(20, 128, 1024, True, False, seed=8, env=env)
+
+
+def test_linear_rejects_unsupported_shapes():
+    x = torch.zeros(4, 100, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(8, 100, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(4, 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError):
+        st.st_linear(x, w, y)
+
+
+# ---------------------------------------------------------------- embedding
+
+
+def test_embed_gathers_rows_and_flags_bad_tokens():
+    rng = np.random.default_rng(3)
+    V, d = 300, 136
+    table = _rand_bf16(rng, (V, d))
+    tokens = np.array([5, 0, 299, 17, 300, -1, 42], np.int32)
+    out = torch.empty(len(tokens), d, dtype=torch.bfloat16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st.st_embed(torch.from_numpy(tokens).cuda(), _bf16_dev(table), out, status)
+    torch.cuda.synchronize()
+    got = _bits(out)
+    for i, t in enumerate(tokens):
+        if 0 <= t < V:
+            assert np.array_equal(got[i], table[t])
+        else:
+            assert not got[i].any()
+    assert int(status.item()) == 2   # bad token
+
+
+# ---------------------------------------------------------------- rotary embedding + append
+
+
+def _rope_case(D, prefix, seed):
+    rng = np.random.default_rng(seed)
+    Hq, Hkv = 4, 2
+    trees = [tree_random_attach(rng, n, 6) for n in (13, 1, 40)]
+    sizes = [len(p) for p, _ in trees]
+    node_off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    parent = np.concatenate([p for p, _ in trees]).astype(np.int32)
+    T = int(node_off[-1])
+    prefix_len = np.array(prefix, np.int32)
+    S_max = int(max(prefix_len + np.array(sizes))) + 3
+    qkv = _rand_bf16(rng, (T, (Hq + 2 * Hkv) * D))
+    sentinel = np.uint16(0x7FC1)
+    kc = np.full((3, Hkv, S_max, D), sentinel, np.uint16)
+    vc = np.full((3, Hkv, S_max, D), sentinel, np.uint16)
+    tree = st.Tree(torch.from_numpy(node_off).cuda(), torch.from_numpy(parent).cuda(),
+                   max_nodes=64, max_depth=8)
+    q_out = torch.zeros(T, Hq, D, dtype=torch.bfloat16, device="cuda")
+    kd, vd = _bf16_dev(kc), _bf16_dev(vc)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st.st_tree_rope_append(tree, _bf16_dev(qkv), Hq, Hkv, torch.from_numpy(prefix_len).cuda(),
+                           int(prefix_len.max()), q_out, kd, vd, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    X = decode_values(qkv, "bf16")
+    pos = oracle.node_positions(node_off, parent, prefix_len)
+    q_ref = oracle.rope(X[:, :Hq * D].reshape(T, Hq, D), pos)
+    k_ref = oracle.rope(X[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D), pos)
+    v_bits = qkv[:, (Hq + Hkv) * D:].reshape(T, Hkv, D)
+    q_got = decode_values(_bits(q_out), "bf16")
+    kg, vg = _bits(kd), _bits(vd)
+
+    def tol(xin, ref):
+        # fp32 rotation: error below 2^-22 (|x_j| + |x_j+D/2|); then one
+        # rounding to bf16, at most 2^-9 of the value: 2^-8 |ref| covers both
+        pm = np.abs(xin[..., :D // 2]) + np.abs(xin[..., D // 2:])
+        return 2.0 ** -8 * np.abs(ref) + 2.0 ** -20 * np.concatenate([pm, pm], axis=-1)
+
+    xq = X[:, :Hq * D].reshape(T, Hq, D)
+    xk = X[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D)
+    assert np.all(np.abs(q_got - q_ref) <= tol(xq, q_ref))
+    touched = np.zeros(kc.shape[:3], bool)
+    for b in range(3):
+        lo, hi = int(node_off[b]), int(node_off[b + 1])
+        for i in range(hi - lo):
+            slot = int(prefix_len[b]) + i
+            touched[b, :, slot] = True
+            k_got = decode_values(kg[b, :, slot], "bf16")
+            assert np.all(np.abs(k_got - k_ref[lo + i]) <= tol(xk[lo + i], k_ref[lo + i]))
+            assert np.array_equal(vg[b, :, slot], v_bits[lo + i])
+    assert np.all(kg[~touched] == sentinel) and np.all(vg[~touched] == sentinel)
+    return float(np.max(np.abs(q_got - q_ref) / (np.abs(q_ref) + 1e-30)))
+
+
+@pytest.mark.parametrize("D,prefix", [(64, [0, 5, 17]), (128, [4096, 31000, 1]),
+                                      (128, [65000, 0, 300])])
+def test_rope_append_matches_oracle(D, prefix):
+    say(f"st_tree_rope_append D={D} prefix={prefix}")
+    rel = _rope_case(D, prefix, seed=D + prefix[0])
+    say(f"  worst relative q error {rel:.2e}")
+
+
+def test_rope_append_bad_prefix_writes_nothing():
+    node_off = np.array([0, 3], np.int32)
+    parent = np.array([-1, 0, 1], np.int32)
+    tree = st.Tree(torch.from_numpy(node_off).cuda(), torch.from_numpy(parent).cuda(),
+                   max_nodes=3, max_depth=2)
+    D, Hq, Hkv, S_max = 64, 2, 1, 8
+    qkv = torch.ones(3, (Hq + 2 * Hkv) * D, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(3, Hq, D, dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(1, Hkv, S_max, D, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    prefix = torch.tensor([6], dtype=torch.int32, device="cuda")   # 6 + 3 > S_max
+    st.st_tree_rope_append(tree, qkv, Hq, Hkv, prefix, 8, q, kc, vc, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & 16
+    assert not kc.any() and not vc.any() and not q.any()
+
+
+# ---------------------------------------------------------------- the model end to end
+
+
+CFG = model_config(V=512, Hq=4, Hkv=2, D=64)
+
+
+def _weights(seed):
+    wb = model_weights(seed, CFG)
+    dev = LayerWeights(E=_bf16_dev(wb["E"]), Wqkv=_bf16_dev(wb["Wqkv"]), Wo=_bf16_dev(wb["Wo"]),
+                       Wlm=_bf16_dev(wb["Wlm"]), Hq=CFG["Hq"], Hkv=CFG["Hkv"], D=CFG["D"])
+    host = {k: decode_values(v, "bf16") for k, v in wb.items()}
+    return dev, host
+
+
+def _tree(par, max_depth):
+    n = len(par)
+    return st.Tree(torch.tensor([0, n], dtype=torch.int32, device="cuda"),
+                   torch.from_numpy(np.asarray(par, np.int32)).cuda(), max_nodes=n,
+                   max_depth=max_depth)
+
+
+def test_layer_forward_logits_match_oracle():
+    wdev, host = _weights(11)
+    rng = np.random.default_rng(11)
+    P, S_max = 37, 96
+    prompt = rng.integers(0, CFG["V"], P)
+    kc_h, vc_h = oracle.prefix_cache(host, CFG, prompt, S_max)
+    kc = _bf16_dev(f32_to_bf16_bits(kc_h.astype(np.float32)))
+    vc = _bf16_dev(f32_to_bf16_bits(vc_h.astype(np.float32)))
+    par, _ = tree_random_attach(rng, 24, 5)
+    tok = rng.integers(0, CFG["V"], len(par)).astype(np.int32)
+    tree = st.Tree(torch.tensor([0, len(par)], dtype=torch.int32, device="cuda"),
+                   torch.from_numpy(par.astype(np.int32)).cuda(), max_nodes=len(par), max_depth=5)
+    lb = layer_buffers(wdev, tree, P)
+    prefix = torch.tensor([P], dtype=torch.int32, device="cuda")
+    layer_forward(wdev, tree, torch.from_numpy(tok).cuda(), prefix, P, kc, vc, lb)
+    torch.cuda.synchronize()
+    assert int(lb.buf["status"].item()) == 0
+    got = lb.buf["logits"].cpu().numpy().astype(np.float64)
+    kq = decode_values(_bits(kc), "bf16")
+    vq = decode_values(_bits(vc), "bf16")
+    ref = oracle.tree_layer(host, CFG, tok, np.array([0, len(par)], np.int32), par,
+                            np.array([P], np.int32), kq, vq)["logits"]
+    err = np.abs(got - ref).max()
+    say(f"layer logits: max |gpu - oracle| {err:.3e}, logit std {ref.std():.2f}")
+    # bf16 rounding of q/k/v, the attention output and h (relative 2^-9 each)
+    # moves a logit of size ~4 by a few hundredths
+    assert err < 0.15
+
+
+# Model seeds whose fp64 greedy decoding keeps a top-two logit gap of at least
+# 0.1 over its first 24 tokens (found by scanning seeds with the oracle); the
+# GPU logits of this model are within 0.03 of the oracle's, so no decision can
+# flip there.
+GEN_SEEDS = [4, 8, 15]
+GAP = 0.1
+
+
+@pytest.mark.parametrize("seed", GEN_SEEDS)
+def test_generation_equals_autoregressive_decoding(seed):
+    """[Specular, 主要特性]: greedy tree verification keeps the target's output.
+    The GPU runs prefill (a chain tree of the prompt) and then verification
+    steps with draft trees that follow the oracle's continuation for a few
+    levels (broken on purpose at some steps); the emitted tokens must be those
+    of fp64 autoregressive decoding, except after a step whose top-two gap is
+    within the bf16 error of the logits."""
+    wdev, host = _weights(200 + seed)
+    rng = np.random.default_rng(seed)
+    prompt = rng.integers(0, CFG["V"], 9).astype(np.int32)
+    n_new = 24
+    ar, margins = oracle.ar_greedy_decode(host, CFG, prompt, n_new + 8)
+    S_max = 128
+    Hkv, D = CFG["Hkv"], CFG["D"]
+    kc = torch.zeros(1, Hkv, S_max, D, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    # prefill: prompt[:-1] as a chain at positions 0..n-2 (its logits are unused)
+    pre = prompt[:-1]
+    tree = _tree(np.arange(-1, len(pre) - 1), len(pre) - 1)
+    lb = layer_buffers(wdev, tree, 0)
+    layer_forward(wdev, tree, torch.from_numpy(pre).cuda(),
+                  torch.zeros(1, dtype=torch.int32, device="cuda"), 0, kc, vc, lb)
+    P = len(pre)
+    root = int(prompt[-1])
+    gen, steps, lens = [], 0, []
+    while len(gen) < n_new:
+        truth = ar[len(gen):]
+        par, tok = draft_tree(rng, truth, 12, 4, break_at=(3 if steps % 3 == 2 else None),
+                              V=CFG["V"])
+        tok[0] = root
+        tree = _tree(par, 4)
+        lb = layer_buffers(wdev, tree, P)
+        prefix = torch.tensor([P], dtype=torch.int32, device="cuda")
+        layer_step(wdev, tree, torch.from_numpy(tok).cuda(), prefix, P, kc, vc, lb)
+        torch.cuda.synchronize()
+        assert int(lb.buf["status"].item()) == 0
+        L = int(lb.buf["accept_len"][0].item())
+        emitted = lb.buf["out_tokens"][0, :L + 1].cpu().tolist()
+        assert int(lb.buf["new_len"][0].item()) == P + L + 1
+        gen += emitted
+        lens.append(L)
+        P += L + 1
+        root = emitted[-1]
+        steps += 1
+    first = next((i for i in range(n_new) if gen[i] != int(ar[i])), n_new)
+    say(f"seed {seed}: {steps} steps, accepted {lens}, first difference at {first} of {n_new}")
+    if first < n_new:
+        assert margins[first] < GAP, f"tokens differ at {first} with gap {margins[first]:.3f}"
+    assert first == n_new or first >= 20
+    assert max(lens) >= 3   # the planted continuations were accepted

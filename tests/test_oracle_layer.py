@@ -122,7 +122,7 @@ def test_chain_tree_layer_equals_autoregressive_logits():
     np.testing.assert_allclose(out["v_cache"], pv, atol=1e-12)
 
 
-def draft_tree(rng, truth, n_nodes, depth, break_at=None):
+def draft_tree(rng, truth, n_nodes, depth, break_at=None, V=96):
     """Parent array and tokens of a draft tree whose node 1.. path follows
     ``truth`` (the model's own continuation) for ``depth`` levels, changed at
     level ``break_at`` if given; the other nodes attach at random with random
@@ -135,7 +135,7 @@ def draft_tree(rng, truth, n_nodes, depth, break_at=None):
         parent.append(prev)
         tok = int(truth[lvl - 1])
         if break_at is not None and lvl == break_at:
-            tok = (tok + 1) % 96
+            tok = (tok + 1) % V
         tokens.append(tok)
         level.append(lvl)
         prev = len(parent) - 1
@@ -143,7 +143,7 @@ def draft_tree(rng, truth, n_nodes, depth, break_at=None):
         cand = [i for i in range(len(parent)) if level[i] < depth]
         p = int(rng.choice(cand))
         parent.append(p)
-        tokens.append(int(rng.integers(0, 96)))
+        tokens.append(int(rng.integers(0, V)))
         level.append(level[p] + 1)
     # shuffle non-root labels while keeping parents before children
     order = [0] + sorted(range(1, len(parent)), key=lambda i: (level[i], rng.random()))

@@ -3,7 +3,8 @@
 The target model's side of tree-based speculative decoding for one attention
 layer, as hand-written HIP kernels behind a C ABI (include/st.h, libst.so):
 ancestor mask, tree-masked split-KV attention, greedy and rejection-sampling
-acceptance, KV compaction.  This package is the thin Python binding; torch
+acceptance, KV compaction; and the layer pieces around them (embedding,
+skinny bf16 projections, rotary embedding with the tree-KV append).  This package is the thin Python binding; torch
 provides device memory and streams.
 """
 
@@ -15,12 +16,16 @@ from .binding import (  # noqa: F401
     Tree,
     decode_status,
     load_library,
+    st_embed,
     st_kv_compact,
+    st_linear,
+    st_linear_workspace,
     st_mask_words,
     st_status_str,
     st_tree_attention,
     st_tree_attention_workspace,
     st_tree_mask,
+    st_tree_rope_append,
     st_verification_step,
     st_verification_step_workspace,
     st_verify_greedy,

@@ -77,6 +77,10 @@ def _declare(lib):
         "st_status_str": (_c.c_char_p, [I]),
         "st_verification_step_workspace": (S, [TP, _c.POINTER(StStep)]),
         "st_verification_step": (I, [TP, _c.POINTER(StStep), P, S, P, P]),
+        "st_embed": (I, [I, I, I, P, P, P, P, P]),
+        "st_tree_rope_append": (I, [TP, I, I, I, _c.c_float, P, P, I, I, P, P, P, P, P]),
+        "st_linear_workspace": (S, [I, I, I]),
+        "st_linear": (I, [I, I, I, P, P, P, P, I, P, S, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -329,6 +333,59 @@ def st_verification_step(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix
     _check(load_library().st_verification_step(
         tree.ref, ctypes.byref(step), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(status), _stream()), "st_verification_step")
+
+
+def st_embed(tokens, table, out, status=None):
+    """out[t] = table[tokens[t]] (bf16 rows)."""
+    V, d = table.shape
+    T = tokens.numel()
+    _dev(tokens, "tokens", torch.int32)
+    _dev(table, "table", torch.bfloat16)
+    _dev(out, "out", torch.bfloat16, T * d)
+    _check(load_library().st_embed(T, d, V, _ptr(tokens), _ptr(table), _ptr(out), _ptr(status),
+                                   _stream()), "st_embed")
+
+
+def st_tree_rope_append(tree: Tree, qkv, Hq: int, Hkv: int, prefix_len, max_prefix: int,
+                        q_out, k_cache, v_cache, theta: float = 10000.0, status=None):
+    """qkv [T][(Hq + 2 Hkv) D] bf16 -> q_out [T][Hq][D]; rotated keys and values
+    written at slots prefix_len[b] + i of k_cache / v_cache [B][Hkv][S_max][D]."""
+    B, Hkv2, S_max, D = k_cache.shape
+    if Hkv2 != Hkv or tuple(v_cache.shape) != tuple(k_cache.shape) or B != tree.B:
+        raise ValueError("cache shapes do not match the tree and heads")
+    _dev(qkv, "qkv", torch.bfloat16, tree.T * (Hq + 2 * Hkv) * D)
+    _dev(q_out, "q_out", torch.bfloat16, tree.T * Hq * D)
+    _dev(k_cache, "k_cache", torch.bfloat16)
+    _dev(v_cache, "v_cache", torch.bfloat16)
+    _dev(prefix_len, "prefix_len", torch.int32, B)
+    _check(load_library().st_tree_rope_append(
+        tree.ref, Hq, Hkv, D, float(theta), _ptr(qkv), _ptr(prefix_len), max_prefix, S_max,
+        _ptr(q_out), _ptr(k_cache), _ptr(v_cache), _ptr(status), _stream()),
+        "st_tree_rope_append")
+
+
+def st_linear_workspace(M: int, N: int, K: int) -> int:
+    return load_library().st_linear_workspace(M, N, K)
+
+
+def st_linear(x, w, y, residual=None, workspace=None):
+    """y[M][N] = x[M][K] . w[N][K]^T (+ residual), bf16 inputs, y bf16 or fp32."""
+    M, K = x.shape
+    N, K2 = w.shape
+    if K2 != K or tuple(y.shape) != (M, N):
+        raise ValueError("shape mismatch between x, w and y")
+    _dev(x, "x", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    _dev(y, "y")
+    if residual is not None:
+        _dev(residual, "residual", torch.bfloat16, M * N)
+    need = st_linear_workspace(M, N, K)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if need and ws_bytes < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check(load_library().st_linear(
+        M, N, K, _ptr(x), _ptr(w), _ptr(residual), _ptr(y), _dtype_code(y), _ptr(workspace),
+        ws_bytes, _stream()), "st_linear")
 
 
 def st_status_str(code: int) -> str:
