@@ -113,11 +113,202 @@ def cpu_baseline(wl, budget_s: float, stochastic: bool):
             f"{per * 1e3:.1f} ms per step", "seconds_per_step": per}
 
 
+def cpu_baseline_layer(host, cfg, wl, budget_s: float):
+    """The oracle's layer step (fp64 model layer, greedy acceptance,
+    compaction) on the host, repeated until the time budget is used."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    from oracle.attention import decode_values
+    kc = decode_values(wl.k_cache, "bf16")
+    vc = decode_values(wl.v_cache, "bf16")
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        out = oracle.tree_layer(host, cfg, wl.tokens, wl.node_off, wl.parent, wl.prefix_len,
+                                kc, vc)
+        res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, out["logits"], cfg["V"],
+                                   wl.max_depth)
+        oracle.kv_compact(out["k_cache"], out["v_cache"], wl.prefix_len, res["accept_len"],
+                          res["accept_nodes"], wl.max_depth + 1)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 100:
+            break
+    per = el / runs
+    return {"value": wl.T / per, "unit": "verified tree tokens/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{runs} full oracle layer step(s) of the same workload "
+            f"(fp64 projections, rotary, attention, acceptance, compaction) in {el:.1f} s; "
+            f"{per * 1e3:.1f} ms per step", "seconds_per_step": per}
+
+
+def bench_layer(args):
+    """One model layer verifying the llama7b tree: embedding, q/k/v projection,
+    rotary + append, tree attention, output projection with residual,
+    vocabulary projection, greedy acceptance, compaction (d = 4096, 32/32
+    heads, D = 128, V = 32000, prefix 4096, 64 nodes)."""
+    import numpy as np
+    import torch
+
+    from synth import make_workload, model_config, model_weights
+    from token_tree_verification_st_amd import Tree, load_library
+    from token_tree_verification_st_amd.layer import (LayerWeights, layer_buffers, layer_step)
+    from token_tree_verification_st_amd.binding import (st_embed, st_linear,
+                                                        st_tree_attention, st_tree_rope_append,
+                                                        st_verify_greedy, st_kv_compact)
+
+    load_library()
+    torch.cuda.set_device(0)
+    wl = make_workload("llama7b", args.seed)
+    cfg = model_config(V=wl.V, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D)
+    wb = model_weights(args.seed, cfg)
+    w_bytes = sum(v.nbytes for k, v in wb.items() if k != "E")
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
+
+    RW = 2                        # weight replicas: 2 x 396 MB cycles past the Infinity Cache
+    ws = [LayerWeights(E=dev(wb["E"]), Wqkv=dev(wb["Wqkv"]), Wo=dev(wb["Wo"]),
+                       Wlm=dev(wb["Wlm"]), Hq=cfg["Hq"], Hkv=cfg["Hkv"], D=cfg["D"])
+          for _ in range(RW)]
+    kv_bytes = wl.k_cache.nbytes + wl.v_cache.nbytes
+    R = max(RW, math.ceil(REPLICA_BYTES / kv_bytes))
+    tree = Tree(torch.from_numpy(wl.node_off).cuda(), torch.from_numpy(wl.parent).cuda(),
+                wl.max_nodes, wl.max_depth)
+    tokens = torch.from_numpy(wl.tokens).cuda()
+    prefix = torch.from_numpy(wl.prefix_len).cuda()
+    P = int(wl.prefix_len.max())
+    caches = [(dev(wl.k_cache), dev(wl.v_cache)) for _ in range(R)]
+    bufs = [layer_buffers(ws[0], tree, P) for _ in range(R)]
+    print(f"# workload llama7b_layer: T={wl.T} weights {w_bytes / 1e6:.0f} MB x {RW}, "
+          f"kv {kv_bytes / 1e6:.1f} MB x {R}", file=sys.stderr, flush=True)
+
+    def step(i):
+        kc, vc = caches[i % R]
+        layer_step(ws[i % RW], tree, tokens, prefix, P, kc, vc, bufs[i % R])
+
+    T, d, V = wl.T, cfg["d"], cfg["V"]
+    HD, QKV = cfg["Hq"] * cfg["D"], (cfg["Hq"] + 2 * cfg["Hkv"]) * cfg["D"]
+    calls = {
+        "embed": lambda i: st_embed(tokens, ws[i % RW].E, bufs[i % R].buf["x"],
+                                    bufs[i % R].buf["status"]),
+        "qkv_proj": lambda i: st_linear(bufs[i % R].buf["x"], ws[i % RW].Wqkv,
+                                        bufs[i % R].buf["qkv"], workspace=bufs[i % R].buf["ws_qkv"]),
+        "rope_append": lambda i: st_tree_rope_append(
+            tree, bufs[i % R].buf["qkv"], cfg["Hq"], cfg["Hkv"], prefix, P, bufs[i % R].buf["q"],
+            caches[i % R][0], caches[i % R][1], status=bufs[i % R].buf["status"]),
+        "attention": lambda i: st_tree_attention(
+            tree, bufs[i % R].buf["q"], caches[i % R][0], caches[i % R][1], prefix, P, None,
+            bufs[i % R].buf["attn"], None, bufs[i % R].buf["ws_attn"],
+            status=bufs[i % R].buf["status"]),
+        "o_proj": lambda i: st_linear(bufs[i % R].buf["attn"].view(T, HD), ws[i % RW].Wo,
+                                      bufs[i % R].buf["h"], residual=bufs[i % R].buf["x"],
+                                      workspace=bufs[i % R].buf["ws_o"]),
+        "lm_head": lambda i: st_linear(bufs[i % R].buf["h"], ws[i % RW].Wlm,
+                                       bufs[i % R].buf["logits"],
+                                       workspace=bufs[i % R].buf["ws_lm"]),
+        "verify": lambda i: st_verify_greedy(
+            tree, tokens, bufs[i % R].buf["logits"], bufs[i % R].buf["accept_len"],
+            bufs[i % R].buf["accept_nodes"], bufs[i % R].buf["out_tokens"],
+            bufs[i % R].buf["ws_verify"], bufs[i % R].buf["status"]),
+        "compact": lambda i: st_kv_compact(
+            caches[i % R][0], caches[i % R][1], prefix, bufs[i % R].buf["accept_len"],
+            bufs[i % R].buf["accept_nodes"], bufs[i % R].buf["src_slot"],
+            bufs[i % R].buf["new_len"], bufs[i % R].buf["status"]),
+    }
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                fn(i)
+        return g
+
+    def timed_replay(g):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t, e0.elapsed_time(e1)
+
+    wall, gpu_ms = timed_replay(capture(step))
+    ms_per_step = wall / K * 1e3
+    per_call = {}
+    for name, fn in calls.items():
+        _, ms = timed_replay(capture(fn))
+        per_call[name] = ms / K * 1e3
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    st_words = [int(b.buf["status"].item()) for b in bufs]
+    assert not any(st_words), f"device status {st_words}"
+
+    lm_bytes = V * d * 2 + T * d * 2 + T * V * 4
+    lm_us = per_call["lm_head"]
+    achieved = lm_bytes / (lm_us * 1e-6) / 1e9
+    proj_bytes = (QKV * d + d * HD + V * d) * 2
+    proj_us = per_call["qkv_proj"] + per_call["o_proj"] + per_call["lm_head"]
+    from token_tree_verification_st_amd.profiling import read_linear_traffic
+    traffic = read_linear_traffic(os.path.join(ROOT, "profiles",
+                                               "linear_llama7b_layer_traffic.md"))
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "st_linear (vocabulary projection, 32000 x 4096)",
+            "algorithmic_bytes": lm_bytes, "avg_launch_us": round(lm_us, 3),
+            "projections_gbs": round(proj_bytes / (proj_us * 1e-6) / 1e9, 1),
+            "timing": f"HIP events around a graph of {K} back-to-back calls"}
+    al = bufs[0].buf["accept_len"].cpu().numpy()
+    line = {
+        "metric": "verified tree tokens/s (7B-shaped layer step with projections, 64-node tree, "
+                  "4K prefix)",
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "verified tree tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "gpu_ms_per_step": round(gpu_ms / K, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded PCG64: bf16 weights N(0, 1/d), N(0,1) prefix K/V)",
+        "config": {"workload": "llama7b_layer", "requests": 1, "d_model": d,
+                   "q_heads": cfg["Hq"], "kv_heads": cfg["Hkv"], "head_dim": cfg["D"],
+                   "prefix": [P], "tree_nodes": T, "vocab": V, "acceptance": "greedy",
+                   "weight_replicas": RW, "kv_replicas": R, "launch": "hip graph"},
+        "per_call_us": {c: round(v, 3) for c, v in per_call.items()},
+        "accepted_tokens_per_step": int((al + 1).sum()),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle.attention import decode_values
+        host = {k: (decode_values(v, "bf16") if k != "E" else None) for k, v in wb.items()}
+        # the oracle gathers embedding rows; decode only the rows it reads
+        E = np.zeros((V, d))
+        rows = np.unique(wl.tokens)
+        E[rows] = decode_values(wb["E"][rows], "bf16")
+        host["E"] = E
+        line["cpu_baseline"] = cpu_baseline_layer(host, cfg, wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
+    if args.workload == "llama7b_layer":
+        bench_layer(args)
+        return
     import numpy as np
     import torch
 

@@ -95,8 +95,8 @@ def test_linear_matches_oracle(M, N, K, out_f32, res):
     say(f"  worst error / sum|x w| = {rel:.2e}")
 
 
-@pytest.mark.parametrize("env", [{"ST_LINEAR_STAGES": 4}, {"ST_LINEAR_KSPLIT": 2},
-                                 {"ST_LINEAR_KSPLIT": 16}, {"ST_LINEAR_STAGES": 4,
+@pytest.mark.parametrize("env", [{"ST_LINEAR_STAGES": 8}, {"ST_LINEAR_KSPLIT": 2},
+                                 {"ST_LINEAR_KSPLIT": 16}, {"ST_LINEAR_STAGES": 8,
                                                              "ST_LINEAR_KSPLIT": 8}])
 def test_linear_ring_depths_and_splits(env):
     say(f"st_linear forced {env}")

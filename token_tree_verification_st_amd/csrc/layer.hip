@@ -14,7 +14,7 @@
 // A workgroup owns 64 output features (16 per wavefront) and 32 or 64 rows,
 // and walks its range of the reduction in 64-wide stages.  Each stage of w
 // (64 features x 64) and of x (rows x 64) is copied to LDS by direct
-// global-to-LDS loads into an 8-deep ring shared by the 4 wavefronts; per
+// global-to-LDS loads into a 4-deep ring shared by the 4 wavefronts; per
 // 32-wide step a wavefront reads one w fragment and one x fragment per
 // 16 rows and issues v_mfma_f32_16x16x32_bf16 (A = w, B = x^T).  When one
 // pass over the features leaves CUs idle the reduction is split and a second
@@ -468,7 +468,9 @@ extern "C" int st_linear(int M, int N, int K, const void* x, const void* w, cons
     a.part = (float*)workspace;
   }
   const dim3 grid(8 * a.per_xcd);
-  const bool deep = env_int("ST_LINEAR_STAGES", 8) == 8;  // 8 stages, else 4
+  // 4 stages (64 KB of LDS at 64 rows: two workgroups per CU) measured
+  // faster than 8 (one per CU) on the 7B-shaped projections
+  const bool deep = env_int("ST_LINEAR_STAGES", 4) == 8;
   if (p.mblk_rows == 32) {
     if (deep)
       hipLaunchKernelGGL((linear_kernel<2, 8>), grid, dim3(256), 0, (hipStream_t)stream, a);

@@ -1,6 +1,9 @@
 """Summaries of rocprofv3 output for profiles/ (host-side text processing).
 
-    python -m token_tree_verification_st_amd.profiling stats   STATS_CSV OUT.md TITLE COMMAND
+    python -m token_tree_verification_st_amd.profiling stats   STATS_CSV OUT.md TITLE COMMAND \\
+        [TRACE_CSV KERNEL_PREFIX]
+    python -m token_tree_verification_st_amd.profiling linear_traffic FETCH_CSV WRITE_CSV \\
+        COPY_BYTES LM_GRID OUT.md CMD_F CMD_W
     python -m token_tree_verification_st_amd.profiling traffic FETCH_CSV WRITE_CSV COPY_BYTES \\
         WORKLOAD OUT.md COMMAND_FETCH COMMAND_WRITE
 
@@ -53,6 +56,84 @@ def stats_md(stats_csv: str, title: str, command: str) -> str:
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.1f}% |")
     return "\n".join(out) + "\n"
+
+
+LINEAR_SOURCES = ("csrc/layer.hip", "csrc/st_internal.h", "build.py")
+
+
+def linear_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in LINEAR_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def grid_table(trace_csv: str, prefix: str) -> str:
+    """Durations of the kernels whose short name starts with ``prefix``, per
+    launch shape (grid size), from a --kernel-trace csv."""
+    d = defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        if _short(r["Kernel_Name"]).startswith(prefix):
+            d[int(r["Grid_Size_X"])].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["", f"{prefix} by launch shape:", "", "| grid (threads) | calls | avg us | min us |"
+           " max us |", "|---|---|---|---|---|"]
+    for g in sorted(d):
+        v = d[g]
+        out.append(f"| {g} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _per_grid(counter_csv: str, counter: str, prefix: str):
+    """Per grid size of the kernels whose short name starts with ``prefix``:
+    mean counter value (KiB) and dispatch count."""
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(counter_csv)):
+        if r["Counter_Name"] == counter and _short(r["Kernel_Name"]).startswith(prefix):
+            vals[int(r["Grid_Size"])].append(float(r["Counter_Value"]))
+    return {g: (sum(v) / len(v), len(v)) for g, v in vals.items()}
+
+
+def linear_traffic_md(fetch_csv, write_csv, copy_bytes, lm_grid, cmd_f, cmd_w):
+    """HBM bytes of the projection kernel per dispatch shape (grid size), scaled
+    by the same run's calibration copy."""
+    f = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    w = _per_dispatch(write_csv, "WRITE_SIZE")
+    f_scale = copy_bytes / (f[COPY_KERNEL][2] * 1024.0)
+    w_scale = copy_bytes / (w[COPY_KERNEL][2] * 1024.0)
+    fg = _per_grid(fetch_csv, "FETCH_SIZE", "linear_kernel")
+    wg = _per_grid(write_csv, "WRITE_SIZE", "linear_kernel")
+    out = ["# st_linear HBM traffic, workload llama7b_layer", "",
+           "Commands (run from /tmp with TMPDIR=/tmp; $R = repository root):", "",
+           "```", cmd_f, cmd_w, "```", "",
+           f"Calibration: a device copy of {copy_bytes} bytes in the same process reads "
+           f"FETCH_SIZE x {f_scale:.3f} and WRITE_SIZE x {w_scale:.3f} of its true bytes.", "",
+           "| linear_kernel grid (threads) | dispatches | fetch bytes | write bytes |",
+           "|---|---|---|---|"]
+    lm = None
+    for g in sorted(set(fg) | set(wg)):
+        fb = fg.get(g, (0.0, 0))[0] * 1024.0 * f_scale
+        wb = wg.get(g, (0.0, 0))[0] * 1024.0 * w_scale
+        out.append(f"| {g} | {fg.get(g, (0, 0))[1]} | {fb:.0f} | {wb:.0f} |")
+        if g == lm_grid:
+            lm = fb + wb
+    out += ["", f"The vocabulary projection (32000 x 4096, 64 rows) is the grid of {lm_grid} "
+            "threads.", "", "Machine-readable (read by bench.py):", "",
+            f"source_sha256: {linear_source_hash()}",
+            f"bytes_per_launch: {lm:.0f}", ""]
+    return "\n".join(out)
+
+
+def read_linear_traffic(path: str):
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"^source_sha256: (\w+)", text, re.M)
+    b = re.search(r"^bytes_per_launch: (\d+)", text, re.M)
+    if not h or not b or h.group(1) != linear_source_hash():
+        return None
+    return int(b.group(1))
 
 
 def _per_dispatch(counter_csv: str, counter: str):
@@ -116,7 +197,14 @@ def read_traffic(path: str):
 def main(argv):
     if argv[0] == "stats":
         stats_csv, out, title, command = argv[1:5]
-        open(out, "w").write(stats_md(stats_csv, title, command))
+        text = stats_md(stats_csv, title, command)
+        if len(argv) > 6:   # TRACE_CSV KERNEL_PREFIX: add a per-launch-shape table
+            text += grid_table(argv[5], argv[6])
+        open(out, "w").write(text)
+    elif argv[0] == "linear_traffic":
+        fcsv, wcsv, copy_bytes, lm_grid, out, cmd_f, cmd_w = argv[1:8]
+        open(out, "w").write(linear_traffic_md(fcsv, wcsv, int(copy_bytes), int(lm_grid), cmd_f,
+                                               cmd_w))
     elif argv[0] == "traffic":
         fcsv, wcsv, copy_bytes, workload, out, cmd_f, cmd_w = argv[1:8]
         open(out, "w").write(traffic_md(fcsv, wcsv, int(copy_bytes), workload, cmd_f, cmd_w))
