@@ -48,7 +48,7 @@ from .tree import (  # noqa: F401
 )
 from .attention import decode_values, tree_attention  # noqa: F401
 from .philox import philox4x64_10, uniforms_for_node  # noqa: F401
-from .verify import verify_greedy, verify_stochastic  # noqa: F401
+from .verify import nucleus, verify_greedy, verify_stochastic  # noqa: F401
 from .compact import kv_compact  # noqa: F401
 from .layer import (  # noqa: F401
     ROPE_THETA,

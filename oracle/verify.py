@@ -25,7 +25,17 @@ Readings used here (the pages leave them open):
   * accept_len L counts accepted non-root nodes; out_tokens holds their tokens
     followed by the replacement token, so L + 1 tokens are emitted;
   * if an accepted path would grow past ``max_depth`` nodes below the root the
-    walk stops, status bit 8 is set and the replacement token is -1.
+    walk stops, status bit 8 is set and the replacement token is -1;
+  * nucleus sampling (the pages' configuration and tuning table recommend
+    top-p 0.9 alongside temperature 0.7): p and q are each restricted to their
+    nucleus -- sort descending, take the first rank where the running sum
+    reaches top_p of the total, keep every token at least as likely as that
+    one -- and renormalised before any test.  Both are filtered because the
+    draft tokens were drawn from the filtered draft and the output must follow
+    the filtered target;
+  * the draft may be given as probabilities (the explainer's
+    calculate_accept_prob takes draft probabilities): q is then the row as
+    given, normalised, with no temperature.
 """
 
 from __future__ import annotations
@@ -98,6 +108,25 @@ def softmax_with_temperature(row, temperature: float) -> np.ndarray:
     return e / e.sum()
 
 
+def nucleus(prob, top_p: float):
+    """prob restricted to its top-p nucleus and renormalised, and whether the
+    cut is a near tie (the running sum at the cut, or just before it, within
+    NEAR_TIE_EPS of top_p)."""
+    prob = np.asarray(prob, dtype=np.float64)
+    if top_p >= 1.0:
+        return prob, False
+    total = float(prob.sum())
+    order = np.argsort(-prob, kind="stable")
+    csum = np.cumsum(prob[order])
+    target = top_p * total
+    k = int(np.nonzero(csum >= target)[0][0])
+    thr = prob[order[k]]
+    kept = np.where(prob >= thr, prob, 0.0)
+    tie = abs(csum[k] - target) < NEAR_TIE_EPS * total or \
+        (k > 0 and abs(csum[k - 1] - target) < NEAR_TIE_EPS * total)
+    return kept / kept.sum(), bool(tie)
+
+
 def inverse_cdf(r: np.ndarray, u: float):
     """Smallest v whose running sum (ascending v) exceeds u * sum(r); if
     rounding leaves none, the last v with r[v] > 0.  Also reports whether the
@@ -118,7 +147,7 @@ def inverse_cdf(r: np.ndarray, u: float):
 
 def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: int,
                       temperature: float, seed: int, offset: int, max_depth: int,
-                      follow=None, uniforms=None):
+                      follow=None, uniforms=None, top_p: float = 1.0, draft_probs: bool = False):
     """Multi-step rejection sampling down the tree.
 
     ``follow`` (optional) maps request -> accepted path observed elsewhere.  The
@@ -129,8 +158,12 @@ def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: 
     ``uniforms`` (optional) replaces the Philox draws: a callable
     (request, local_node) -> (u_acc, u_smp), for hand-worked examples.
 
+    ``top_p`` < 1 restricts p and q to their nuclei; ``draft_probs`` takes
+    draft_logits as probabilities (rows of q as given).
+
     Returns dict(accept_len, accept_nodes, out_tokens, near_ties [B], status,
-    divergences [B] (list of (node, child, near_tie)), bonus_tie [B]).
+    divergences [B] (list of (node, child, near_tie)), bonus_tie [B],
+    nucleus_ties [B] (near-tie nucleus cuts met on the walk)).
     """
     B = len(node_off) - 1
     if uniforms is None:
@@ -143,18 +176,42 @@ def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: 
     near_ties = np.zeros(B, dtype=np.int32)
     divergences = [[] for _ in range(B)]
     bonus_tie = np.zeros(B, dtype=bool)
+    nucleus_ties = np.zeros(B, dtype=np.int32)
+    if draft_probs:
+        T = int(node_off[-1])
+        for t in range(T):
+            row = np.asarray(draft_logits[t], dtype=np.float64)
+            if np.any(row < 0) or not row.sum() > 0:
+                status |= STATUS_NONFINITE
+
+    def target_dist(b, t):
+        d, tie = nucleus(softmax_with_temperature(target_logits[t], temperature), top_p)
+        nucleus_ties[b] += int(tie)
+        return d
+
+    def draft_dist(b, t):
+        if draft_probs:
+            row = np.asarray(draft_logits[t], dtype=np.float64)
+            row = row / row.sum()
+        else:
+            row = softmax_with_temperature(draft_logits[t], temperature)
+        d, tie = nucleus(row, top_p)
+        nucleus_ties[b] += int(tie)
+        return d
+
     for b in range(B):
         lo, hi = int(node_off[b]), int(node_off[b + 1])
         par = [int(x) for x in parent[lo:hi]]
         path = [0]
         u = 0
-        r = softmax_with_temperature(target_logits[lo], temperature)
+        r = target_dist(b, lo)
         overflow = False
         forced = None if follow is None else [int(x) for x in follow[b]]
         while True:
-            q_u = softmax_with_temperature(draft_logits[lo + u], temperature)
+            kids = children_of(par, u)
+            q_u = draft_dist(b, lo + u) if kids else None
             accepted = None
-            for c in children_of(par, u):
+            for c in kids:
                 x = int(tokens[lo + c])
                 u_acc, _ = uniforms(b, c)
                 lhs = u_acc * q_u[x]
@@ -182,7 +239,7 @@ def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: 
                 break
             path.append(accepted)
             u = accepted
-            r = softmax_with_temperature(target_logits[lo + u], temperature)
+            r = target_dist(b, lo + u)
         L = len(path) - 1
         accept_len[b] = L
         accept_nodes[b, :L + 1] = path
@@ -198,4 +255,4 @@ def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: 
             near_ties[b] += int(tie)
     return dict(accept_len=accept_len, accept_nodes=accept_nodes, out_tokens=out_tokens,
                 near_ties=near_ties, status=status, divergences=divergences,
-                bonus_tie=bonus_tie)
+                bonus_tie=bonus_tie, nucleus_ties=nucleus_ties)

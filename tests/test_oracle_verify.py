@@ -295,3 +295,101 @@ def test_follow_mode_records_divergences():
     assert forced["accept_nodes"][:, :6].tolist() == other
     changed = [b for b in range(2) if int(own["accept_len"][b]) != 5]
     assert all(len(forced["divergences"][b]) >= 1 for b in changed)
+
+
+# ---------------------------------------------------------------- nucleus and draft probabilities
+
+
+def test_nucleus_hand_worked():
+    p = np.array([0.05, 0.5, 0.15, 0.3])
+    d, tie = oracle.nucleus(p, 0.9)          # running sums 0.5, 0.8, 0.95: three kept
+    np.testing.assert_allclose(d, [0.0, 0.5 / 0.95, 0.15 / 0.95, 0.3 / 0.95], atol=1e-15)
+    assert not tie
+    d, _ = oracle.nucleus(p, 0.75)           # 0.5, 0.8: two kept
+    np.testing.assert_allclose(d, [0.0, 0.5 / 0.8, 0.0, 0.3 / 0.8], atol=1e-15)
+    d, _ = oracle.nucleus(p, 0.3)            # the top token alone
+    np.testing.assert_array_equal(d, [0.0, 1.0, 0.0, 0.0])
+    d, _ = oracle.nucleus(p, 1.0)
+    np.testing.assert_array_equal(d, p)
+    # tokens as likely as the last one needed are all kept
+    d, _ = oracle.nucleus(np.array([0.4, 0.2, 0.2, 0.2]), 0.5)
+    np.testing.assert_allclose(d, [0.4, 0.2, 0.2, 0.2], atol=1e-15)
+    _, tie = oracle.nucleus(np.array([0.5, 0.25, 0.25]), 0.75)   # the cut lands on 0.75
+    assert tie
+
+
+def test_draft_probabilities_equal_draft_logits():
+    wl = make_workload("stochastic_tree", 0)
+    sl = slice(0, int(wl.node_off[3]))
+    T = wl.temperature
+    dl = wl.draft_logits[sl].astype(np.float64) / T
+    probs = np.exp(dl - dl.max(axis=1, keepdims=True))
+    probs /= probs.sum(axis=1, keepdims=True)
+    base = (wl.node_off[:4], wl.parent[sl], wl.tokens[sl], wl.logits[sl])
+    tail = (wl.V, T, wl.rng_seed, wl.rng_offset, wl.max_depth)
+    a = oracle.verify_stochastic(*base, wl.draft_logits[sl], *tail)
+    b = oracle.verify_stochastic(*base, probs, *tail, draft_probs=True)
+    for k in ("accept_len", "accept_nodes", "out_tokens"):
+        assert np.array_equal(a[k], b[k]), k
+    bad = probs.copy()
+    bad[0, 0] = -0.1
+    assert oracle.verify_stochastic(*base, bad, *tail, draft_probs=True)["status"] & STATUS_NONFINITE
+
+
+def _draft_tree_nucleus(pair, T, root_ctx, widths, rng, top_p):
+    parent, ctxs, frontier = [-1], [root_ctx], [0]
+    for w in widths:
+        nxt = []
+        for u in frontier:
+            _, d = pair.logits(ctxs[u])
+            qd, _ = oracle.nucleus(_softmax(d.astype(np.float64) / T), top_p)
+            for tok in rng.choice(pair.V, size=w, p=qd):
+                parent.append(u)
+                ctxs.append(ctxs[u] + (int(tok),))
+                nxt.append(len(parent) - 1)
+        frontier = nxt
+    tl = np.stack([pair.logits(c)[0] for c in ctxs])
+    dl = np.stack([pair.logits(c)[1] for c in ctxs])
+    tokens = np.array([c[-1] for c in ctxs], np.int32)
+    return np.array(parent, np.int32), tokens, tl, dl
+
+
+def test_nucleus_output_has_the_filtered_target_distribution():
+    """With drafts drawn from the draft's nucleus, the first emitted token
+    follows the target's nucleus distribution (and never leaves it)."""
+    V, T, top_p, trials = 8, 1.5, 0.8, 12000
+    pair = _ToyPair(V, salt=11)             # a nucleus of 4 of the 8 tokens at the root
+    root_ctx = (4,)
+    rng = np.random.default_rng(77)
+    first = np.zeros(V, np.int64)
+    for t in range(trials):
+        parent, tokens, tl, dl = _draft_tree_nucleus(pair, T, root_ctx, (3, 2), rng, top_p)
+        res = oracle.verify_stochastic(np.array([0, len(parent)]), parent, tokens, tl, dl, V, T,
+                                       seed=5, offset=t, max_depth=4, top_p=top_p)
+        first[int(res["out_tokens"][0, 0])] += 1
+    p1, _ = oracle.nucleus(_softmax(pair.logits(root_ctx)[0].astype(np.float64) / T), top_p)
+    keep = p1 > 0
+    assert keep.sum() < V and first[~keep].sum() == 0
+    assert chisquare(first[keep], p1[keep] * trials).pvalue > 1e-3
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_tiny_nucleus_reduces_to_greedy(seed):
+    """A nucleus that keeps only the top target token makes acceptance greedy."""
+    rng = np.random.default_rng(seed)
+    n, V = 24, 30
+    parent, _ = tree_random_attach(rng, n, 5)
+    tl = (rng.standard_normal((n, V)) * 2).astype(np.float32)
+    dl = (rng.standard_normal((n, V)) * 2).astype(np.float32)
+    best = tl.argmax(axis=1)
+    tokens = rng.integers(0, V, n).astype(np.int32)
+    for i in range(1, n):
+        if rng.random() < 0.5:
+            tokens[i] = best[parent[i]]
+    st = oracle.verify_stochastic(np.array([0, n]), parent, tokens, tl, dl, V, 1.0, 4, seed, 8,
+                                  top_p=1e-6)
+    gr = oracle.verify_greedy(np.array([0, n]), parent, tokens, tl, V, 8)
+    # r is one-hot at the argmax: a child carrying it is accepted whatever q
+    # says (u q < 1), any other is rejected, and a rejection leaves r one-hot
+    for k in ("accept_len", "accept_nodes", "out_tokens"):
+        assert np.array_equal(st[k], gr[k]), k
