@@ -41,6 +41,10 @@ def parse():
                     help="wall-time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of a graph")
+    ap.add_argument("--top-p", type=float, default=1.0,
+                    help="stochastic workloads: nucleus sampling on target and draft")
+    ap.add_argument("--draft-probs", action="store_true",
+                    help="stochastic workloads: pass the draft as probabilities")
     ap.add_argument("--traffic", default=None,
                     help="traffic summary (default profiles/attention_<workload>_traffic.md); "
                          "used only if it was taken from the current attention sources")
@@ -329,11 +333,34 @@ def main():
           file=sys.stderr, flush=True)
 
     calls = ["mask", "attention"] + (["verify", "compact"] if wl.V else [])
-    fns = {"mask": stp.run_mask, "attention": stp.run_attention,
-           "verify": lambda d: stp.run_verify(d, stochastic), "compact": stp.run_compact}
+    ext = stochastic and (args.top_p < 1.0 or args.draft_probs)
+    if ext and args.draft_probs:
+        z = wl.draft_logits.astype(np.float64) / wl.temperature
+        pr = np.exp(z - z.max(axis=1, keepdims=True))
+        pr = (pr / pr.sum(axis=1, keepdims=True)).astype(np.float32)
+        for d in reps:
+            d.buf["draft_probs"] = torch.from_numpy(pr).cuda()
+
+    def verify(d):
+        if ext:
+            stp.run_verify(d, True, top_p=args.top_p, draft=d.buf.get("draft_probs"))
+        else:
+            stp.run_verify(d, stochastic)
+
+    fns = {"mask": stp.run_mask, "attention": stp.run_attention, "verify": verify,
+           "compact": stp.run_compact}
+
+    def one_step(d):
+        if ext:   # the options exist on the separate entry points only
+            stp.run_mask(d)
+            stp.run_attention(d)
+            verify(d)
+            stp.run_compact(d)
+        else:
+            stp.verification_step(d, stochastic=stochastic)
 
     for i in range(args.warmup):
-        stp.verification_step(reps[i % R], stochastic=stochastic)
+        one_step(reps[i % R])
     torch.cuda.synchronize()
 
     # The K timed steps are captured into one HIP graph (replica i % R for step
@@ -360,7 +387,7 @@ def main():
         torch.cuda.synchronize()
         return time.perf_counter() - t, e0.elapsed_time(e1)
 
-    step_fn = lambda d: stp.verification_step(d, stochastic=stochastic)
+    step_fn = one_step
     if args.eager:
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -427,6 +454,8 @@ def main():
                    "head_dim": wl.D, "prefix": [int(x) for x in wl.prefix_len][:8],
                    "tree_nodes": int(wl.T), "vocab": wl.V,
                    "acceptance": "stochastic" if stochastic else "greedy",
+                   **({"top_p": args.top_p, "draft": "probabilities" if args.draft_probs
+                       else "logits"} if ext else {}),
                    "replicas": R, "launch": "eager" if args.eager else "hip graph"},
         "per_call_us": {c: round(v, 3) for c, v in per_call.items()},
         "hbm_frac_step": round(attn_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -155,7 +155,8 @@ size_t st_verify_stochastic_workspace(const st_tree* tree, int V);
  * distributions for the children of node i.  At node u with residual r
  * (initially p_u) the children are tested in ascending index: child c with
  * token x is accepted iff u_acc(c) * q_u[x] < r[x]; after a rejection
- * r <- normalise(max(0, r - q_u)) (unchanged if that has no mass).  On an
+ * r <- normalise(max(0, r - q_u)), left unchanged if that has a mass of at
+ * most 1e-6 of the row (the rounding residue of r and q that agree).  On an
  * acceptance the walk moves to c with r = p_c.  When no child is accepted the
  * replacement token is the smallest v whose running sum of r (ascending v)
  * exceeds u_smp(u) * sum(r).  Uniforms come from Philox4x64-10 with key
@@ -173,6 +174,34 @@ int st_verify_stochastic(const st_tree* tree, int V, const int32_t* tokens,
                          uint64_t seed, uint64_t offset, int32_t* accept_len,
                          int32_t* accept_nodes, int32_t* out_tokens, int32_t* near_ties,
                          void* workspace, size_t ws_bytes, int32_t* status, void* stream);
+
+/*
+ * st_verify_stochastic_ex -- st_verify_stochastic with the two sampling
+ * options the pages pair with it: nucleus (top-p) sampling (the SpecInfer
+ * developer article's configuration example and the explainer's tuning
+ * table recommend top-p 0.9 with temperature 0.7), and a draft given as
+ * probabilities (the explainer's acceptance call takes the draft's
+ * probabilities).
+ *   draft_is_probs 0: `draft` holds logits, q_i = softmax(draft[i] / T);
+ *                  1: `draft` holds probabilities (>= 0, any positive scale),
+ *                     q_i = draft[i] / sum(draft[i]), no temperature; a
+ *                     negative or non-finite entry sets ST_STATUS_NONFINITE.
+ *   top_p in (0, 1]: below 1 both p_i and q_i are restricted to their nucleus
+ *     before any test -- the smallest set of most likely tokens whose mass
+ *     reaches top_p of the row, together with every token as likely as the
+ *     least likely one kept -- and renormalised (the draft tokens are taken
+ *     to come from the filtered draft, the output follows the filtered
+ *     target).  The cut is found by bisection over fp32 values with fp64
+ *     sums.  top_p = 1 and draft_is_probs = 0 give st_verify_stochastic.
+ * Other arguments as for st_verify_stochastic; ST_E_INVALID for top_p
+ * outside (0, 1] or draft_is_probs not 0/1.
+ */
+int st_verify_stochastic_ex(const st_tree* tree, int V, const int32_t* tokens,
+                            const float* target_logits, const float* draft, int draft_is_probs,
+                            float temperature, float top_p, uint64_t seed, uint64_t offset,
+                            int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                            int32_t* near_ties, void* workspace, size_t ws_bytes,
+                            int32_t* status, void* stream);
 
 /*
  * st_kv_compact -- move the accepted path's keys and values into contiguous

@@ -18,7 +18,10 @@ Readings used here (the pages leave them open):
     node u with residual r (initially p_u), test the children in ascending
     index: child c with token x is accepted iff u_acc(c) * q_u[x] < r[x]
     (that is u < min(1, r/q) without a division); after a rejection
-    r <- max(0, r - q_u) renormalised (kept as it was if the mass is 0); when
+    r <- max(0, r - q_u) renormalised, kept as it was if its mass is at most
+    1e-6 (a residual of the rounding of nearly equal r and q, which must not
+    be renormalised into a distribution: two one-token nuclei on the same
+    token leave exactly such a residual); when
     no child is accepted the replacement token is drawn from r by inverse CDF
     with u_smp(u), summing r in ascending vocab order.  The residual draw is
     what makes the equal-distribution guarantee hold;
@@ -163,7 +166,9 @@ def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: 
 
     Returns dict(accept_len, accept_nodes, out_tokens, near_ties [B], status,
     divergences [B] (list of (node, child, near_tie)), bonus_tie [B],
-    nucleus_ties [B] (near-tie nucleus cuts met on the walk)).
+    nucleus_ties [B] (near-tie nucleus cuts met on the walk), mass_ties [B]
+    (residual masses within 2e-6 of zero after a rejection, where the
+    no-mass rule below is decided by rounding)).
     """
     B = len(node_off) - 1
     if uniforms is None:
@@ -177,6 +182,7 @@ def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: 
     divergences = [[] for _ in range(B)]
     bonus_tie = np.zeros(B, dtype=bool)
     nucleus_ties = np.zeros(B, dtype=np.int32)
+    mass_ties = np.zeros(B, dtype=np.int32)
     if draft_probs:
         T = int(node_off[-1])
         for t in range(T):
@@ -230,8 +236,10 @@ def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: 
                     break
                 resid = np.maximum(0.0, r - q_u)
                 mass = resid.sum()
-                if mass > 0:
+                if mass > NEAR_TIE_EPS:
                     r = resid / mass
+                if 0.0 < mass <= 2 * NEAR_TIE_EPS:
+                    mass_ties[b] += 1
             if accepted is None:
                 break
             if len(path) - 1 == max_depth:
@@ -255,4 +263,4 @@ def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: 
             near_ties[b] += int(tie)
     return dict(accept_len=accept_len, accept_nodes=accept_nodes, out_tokens=out_tokens,
                 near_ties=near_ties, status=status, divergences=divergences,
-                bonus_tie=bonus_tie, nucleus_ties=nucleus_ties)
+                bonus_tie=bonus_tie, nucleus_ties=nucleus_ties, mass_ties=mass_ties)

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("st_tree_mask", "st_tree_attention", "st_verify_greedy", "st_verify_stochastic",
               "st_kv_compact", "st_status_str", "st_embed", "st_tree_rope_append", "st_linear",
-              "st_linear_workspace"):
+              "st_linear_workspace", "st_verify_stochastic_ex"):
         assert n in names
 
 
@@ -79,3 +79,11 @@ def test_step_struct_layout_matches_header(tmp_path):
     assert int(got["sizeof"]) == ctypes.sizeof(binding.StStep)
     for n in names:
         assert int(got[n]) == getattr(binding.StStep, n).offset, n
+
+
+def test_candidate_length_schedule():
+    # explainer §3.3: K_t = max(1, round(K_max (1 - t/T)))
+    assert [st.candidate_length(t, 10, 5) for t in (0, 2, 5, 9, 10, 20)] == [5, 4, 2, 1, 1, 1]
+    with pytest.raises(ValueError):
+        st.candidate_length(0, 0, 5)
+

@@ -1,0 +1,113 @@
+"""GPU parity of stochastic acceptance with nucleus (top-p) sampling and with
+the draft given as probabilities (st_verify_stochastic_ex) against the oracle.
+Decisions may differ only at near ties: a comparison within 1e-6, a
+replacement draw on a bin edge, or a nucleus cut whose running sum lies
+within 1e-6 of top_p."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import build_workload, make_workload, tree_random_attach
+from token_tree_verification_st_amd import to_device
+from token_tree_verification_st_amd import step as stp
+from tests.gpu_util import device_paths, require_gpu, say, status_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _probs(wl):
+    z = wl.draft_logits.astype(np.float64) / wl.temperature
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    return (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def _check(wl, top_p, probs=False, dw=None):
+    dw = dw or to_device(wl)
+    draft_host = _probs(wl) if probs else wl.draft_logits
+    draft = torch.from_numpy(draft_host).cuda() if probs else None
+    stp.run_verify(dw, stochastic=True, top_p=top_p, draft=draft)
+    torch.cuda.synchronize()
+    al, an, ot = device_paths(dw)
+    follow = [an[b][:al[b] + 1] for b in range(wl.B)]
+    res = oracle.verify_stochastic(wl.node_off, wl.parent, wl.tokens, wl.logits, draft_host,
+                                   wl.V, wl.temperature, wl.rng_seed, wl.rng_offset,
+                                   wl.max_depth, follow=follow, top_p=top_p, draft_probs=probs)
+    excused = 0
+    for b in range(wl.B):
+        if res["nucleus_ties"][b] or res["mass_ties"][b]:
+            excused += 1
+            continue
+        for (u, c, tie) in res["divergences"][b]:
+            assert tie, f"request {b}: decision at node {u} child {c} differs without a near tie"
+        L = int(al[b])
+        assert np.array_equal(ot[b, :L], res["out_tokens"][b, :L])
+        if ot[b, L] != res["out_tokens"][b, L]:
+            assert res["bonus_tie"][b], f"request {b}: replacement token differs"
+    assert status_of(dw) == 0
+    return al, excused
+
+
+@pytest.mark.parametrize("name", ["stochastic_tree", "stochastic_chain"])
+@pytest.mark.parametrize("top_p,probs", [(0.9, False), (1.0, True), (0.9, True), (0.5, False)])
+def test_nucleus_named_workloads(name, top_p, probs):
+    wl = make_workload(name, 0)
+    al, excused = _check(wl, top_p, probs)
+    say(f"{name} top_p={top_p} probs={probs}: accept_len {al.tolist()[:8]}... "
+        f"nucleus near ties excused {excused}")
+    assert excused <= wl.B // 4
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_nucleus_many_offsets_small_vocab(seed):
+    rng = np.random.default_rng(300 + seed)
+    B = 8
+    trees = [tree_random_attach(rng, int(rng.integers(1, 40)), 6) for _ in range(B)]
+    wl = build_workload("nuc", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=int(rng.integers(3, 60)),
+                        prefix_lens=[1] * B, trees=trees, max_depth=6, token_rule="draft_sample",
+                        logit_sigma=2.0, draft_noise_sigma=1.0, temperature=0.7 + 0.3 * seed)
+    dw = to_device(wl)
+    for off in range(12):
+        wl.rng_offset = off
+        dw.rng_offset = off
+        _check(wl, (0.9, 0.6, 0.3)[off % 3], probs=bool(off & 1), dw=dw)
+
+
+def test_ex_with_plain_options_equals_plain_entry_point():
+    from token_tree_verification_st_amd import st_verify_stochastic_ex
+    wl = make_workload("stochastic_tree", 1)
+    dw = to_device(wl)
+    stp.run_verify(dw, stochastic=True)
+    torch.cuda.synchronize()
+    plain = [x.copy() for x in device_paths(dw)]
+    b = dw.buf
+    for k in ("accept_len", "accept_nodes", "out_tokens"):
+        b[k].fill_(-7)
+    st_verify_stochastic_ex(dw.tree, dw.tokens, dw.logits, dw.draft_logits, dw.temperature,
+                            dw.rng_seed, dw.rng_offset, b["accept_len"], b["accept_nodes"],
+                            b["out_tokens"], b["verify_ws"], b["near_ties"], b["status"],
+                            top_p=1.0, draft_is_probs=False)
+    torch.cuda.synchronize()
+    for x, y in zip(plain, device_paths(dw)):
+        assert np.array_equal(x, y)
+
+
+def test_rejects_bad_arguments_and_flags_negative_probabilities():
+    wl = make_workload("stochastic_chain", 0)
+    dw = to_device(wl)
+    for top_p in (0.0, -0.5, 1.5, float("nan")):
+        with pytest.raises(RuntimeError):
+            stp.run_verify(dw, stochastic=True, top_p=top_p,
+                           draft=torch.from_numpy(_probs(wl)).cuda())
+    bad = _probs(wl)
+    bad[0, 3] = -1e-3
+    dw.buf["status"].zero_()
+    stp.run_verify(dw, stochastic=True, top_p=0.9, draft=torch.from_numpy(bad).cuda())
+    torch.cuda.synchronize()
+    assert status_of(dw) & 4

@@ -393,3 +393,27 @@ def test_tiny_nucleus_reduces_to_greedy(seed):
     # says (u q < 1), any other is rejected, and a rejection leaves r one-hot
     for k in ("accept_len", "accept_nodes", "out_tokens"):
         assert np.array_equal(st[k], gr[k]), k
+
+
+def test_rounding_residue_is_no_residual_mass():
+    """After a rejection a residual of at most 1e-6 is kept as no mass: r
+    stays as it was (and a mass that small is reported as a near tie)."""
+    V = 2
+    parent = np.array([-1, 0, 0], np.int32)
+    uni = {1: (0.999, 0.5), 2: (0.9, 0.5), 0: (0.5, 0.5)}
+    # equal one-token rows: child 1 (token 1) is rejected, child 2 (token 0) accepted
+    tl = np.array([[0.0, -1000.0]] * 3, np.float32)     # exp(-1000) is 0 in fp64
+    res = oracle.verify_stochastic(np.array([0, 3]), parent, np.array([0, 1, 0], np.int32), tl,
+                                   tl, V, 1.0, 0, 0, 2, uniforms=lambda b, i: uni[i])
+    assert res["accept_nodes"][0, :2].tolist() == [0, 2]
+    # p exceeds q by 5e-7 on token 0: after child 1 (token 1) is rejected that
+    # residue is not a distribution, r stays p, and child 2 (token 1) is
+    # accepted (renormalising the residue would have put all of r on token 0)
+    p = np.log(np.array([[0.5 + 5e-7, 0.5 - 5e-7]] * 3))
+    q = np.array([[0.5, 0.5]] * 3)
+    uni = {1: (0.9999999, 0.5), 2: (0.9, 0.5), 0: (0.5, 0.5)}
+    res = oracle.verify_stochastic(np.array([0, 3]), parent, np.array([0, 1, 1], np.int32), p, q,
+                                   V, 1.0, 0, 0, 2, uniforms=lambda b, i: uni[i],
+                                   draft_probs=True)
+    assert res["accept_nodes"][0, :2].tolist() == [0, 2]
+    assert int(res["mass_ties"][0]) == 1

@@ -73,6 +73,8 @@ def _declare(lib):
         "st_verify_stochastic_workspace": (S, [TP, I]),
         "st_verify_stochastic": (I, [TP, I, P, P, P, _c.c_float, _c.c_uint64, _c.c_uint64, P, P,
                                      P, P, P, S, P, P]),
+        "st_verify_stochastic_ex": (I, [TP, I, P, P, P, I, _c.c_float, _c.c_float, _c.c_uint64,
+                                        _c.c_uint64, P, P, P, P, P, S, P, P]),
         "st_kv_compact": (I, [I, I, I, I, P, P, I, P, P, P, I, P, P, P, P]),
         "st_status_str": (_c.c_char_p, [I]),
         "st_verification_step_workspace": (S, [TP, _c.POINTER(StStep)]),
@@ -255,6 +257,38 @@ def st_verify_stochastic(tree: Tree, tokens, target_logits, draft_logits, temper
         int(seed), int(offset), _ptr(accept_len), _ptr(accept_nodes), _ptr(out_tokens),
         _ptr(near_ties), _ptr(workspace), ws_bytes, _ptr(status), _stream()),
         "st_verify_stochastic")
+
+
+def st_verify_stochastic_ex(tree: Tree, tokens, target_logits, draft, temperature: float,
+                            seed: int, offset: int, accept_len, accept_nodes, out_tokens,
+                            workspace, near_ties=None, status=None, top_p: float = 1.0,
+                            draft_is_probs: bool = False):
+    """st_verify_stochastic with nucleus sampling (top_p < 1) and/or the draft
+    given as probabilities."""
+    T, V = target_logits.shape
+    _dev(tokens, "tokens", torch.int32, tree.T)
+    _dev(target_logits, "target_logits", torch.float32)
+    _dev(draft, "draft", torch.float32)
+    if draft.shape != target_logits.shape:
+        raise ValueError("draft must match target_logits")
+    _path_outputs(tree, accept_len, accept_nodes, out_tokens)
+    if near_ties is not None:
+        _dev(near_ties, "near_ties", torch.int32, tree.B)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().st_verify_stochastic_ex(
+        tree.ref, V, _ptr(tokens), _ptr(target_logits), _ptr(draft), int(bool(draft_is_probs)),
+        float(temperature), float(top_p), int(seed), int(offset), _ptr(accept_len),
+        _ptr(accept_nodes), _ptr(out_tokens), _ptr(near_ties), _ptr(workspace), ws_bytes,
+        _ptr(status), _stream()), "st_verify_stochastic_ex")
+
+
+def candidate_length(t: int, T_est: int, K_max: int) -> int:
+    """Draft length for the next step (explainer §3.3, dynamic candidate
+    length): K_t = max(1, round(K_max * (1 - t / T_est))) for t tokens
+    generated out of an estimated T_est.  Host policy; rounds half to even."""
+    if T_est <= 0 or K_max < 1:
+        raise ValueError("T_est must be positive and K_max at least 1")
+    return max(1, int(round(K_max * (1.0 - t / T_est))))
 
 
 def st_kv_compact(k_cache, v_cache, prefix_len, accept_len, accept_nodes, src_slot, new_len,

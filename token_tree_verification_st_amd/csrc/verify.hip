@@ -33,6 +33,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kTieEps = 1e-6;
+// A residual whose mass (as a fraction of the target row) is at most this is
+// taken to have none: where r and q agree, the fp32 terms max(0, P - c Q)
+// leave up to about 1e-7 of rounding residue, which must not be renormalised
+// into a distribution (a nucleus cut makes such agreement common: two
+// one-token nuclei on the same token).
+constexpr double kMassEps = 1e-6;
 
 // ---------------------------------------------------------------- reductions
 //
@@ -135,6 +141,18 @@ __device__ inline double block_sum(double v, double* lds, int set) {
   __syncthreads();
   return tree_fold<NW>(lds + set * NW, [](double a, double b) { return a + b; });
 }
+// A double moved to scalar registers (its value must be wave-uniform).
+__device__ __forceinline__ double uniform_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+}
+
 // Two reductions sharing one barrier: (x, y) -> (max x, max y) and sums.
 // They fill both slot sets of `lds`, so a barrier must separate them from
 // the previous reduction on that array and from the next one.
@@ -148,8 +166,9 @@ __device__ inline void block_max2(float& x, float& y, float* lds) {
     lds[NW + threadIdx.x / ST_WAVE] = y;
   }
   __syncthreads();
-  x = tree_fold<NW>(lds, [](float a, float b) { return fmaxf(a, b); });
-  y = tree_fold<NW>(lds + NW, [](float a, float b) { return fmaxf(a, b); });
+  // block-uniform results, kept in scalar registers
+  x = uniform_f32(tree_fold<NW>(lds, [](float a, float b) { return fmaxf(a, b); }));
+  y = uniform_f32(tree_fold<NW>(lds + NW, [](float a, float b) { return fmaxf(a, b); }));
 }
 template <int BLOCK>
 __device__ inline void block_sum2(double& x, double& y, double* lds) {
@@ -161,8 +180,36 @@ __device__ inline void block_sum2(double& x, double& y, double* lds) {
     lds[NW + threadIdx.x / ST_WAVE] = y;
   }
   __syncthreads();
-  x = tree_fold<NW>(lds, [](double a, double b) { return a + b; });
-  y = tree_fold<NW>(lds + NW, [](double a, double b) { return a + b; });
+  x = uniform_f64(tree_fold<NW>(lds, [](double a, double b) { return a + b; }));
+  y = uniform_f64(tree_fold<NW>(lds + NW, [](double a, double b) { return a + b; }));
+}
+
+// block_sum2 over one of two slot pairs of `lds` (4 * BLOCK / 64 doubles):
+// consecutive calls that alternate `set` need no barrier between them.  Each
+// lane of a 16-lane row reads one wavefront's partial and a butterfly adds
+// them (a + b and b + a round alike, so every lane gets the same bits); the
+// totals end in scalar registers.
+template <int BLOCK>
+__device__ inline void block_sum2_set(double& x, double& y, double* lds, int set) {
+  constexpr int NW = BLOCK / ST_WAVE;
+  static_assert(NW == 16, "one partial per lane of a 16-lane row");
+  double* l = lds + set * 2 * NW;
+  x = wave_sum(x);
+  y = wave_sum(y);
+  if (threadIdx.x % ST_WAVE == 0) {
+    l[threadIdx.x / ST_WAVE] = x;
+    l[NW + threadIdx.x / ST_WAVE] = y;
+  }
+  __syncthreads();
+  const int r = threadIdx.x & 15;
+  double a = l[r], b = l[NW + r];
+#pragma unroll
+  for (int k = 1; k < 16; k <<= 1) {
+    a += __shfl_xor(a, k, 16);
+    b += __shfl_xor(b, k, 16);
+  }
+  x = uniform_f64(a);
+  y = uniform_f64(b);
 }
 
 using st::argmax_merge;
@@ -255,6 +302,8 @@ struct StochArgs {
   float temperature;
   uint64_t seed, offset;
   int32_t* status;
+  int draft_probs;  // dl holds probabilities (used as given) rather than logits
+  float top_p;      // < 1: both rows restricted to their nucleus
 };
 
 constexpr int kStochMaxV = 32768;
@@ -342,6 +391,74 @@ __device__ __forceinline__ double resid_sum(const float (&P)[NPT], const float (
 #pragma unroll
   for (int k = 0; k < NPT / EPT; ++k) s += resid_group<EPT>(P, Q, c, k);
   return s;
+}
+
+// A thread's share of the mass at or above `cut` (fp32 within a group, fp64
+// from there on, as the row totals).
+template <bool VEC, int NPT>
+__device__ __forceinline__ double kept_sum(const float (&X)[NPT], float cut) {
+  constexpr int EPT = VEC ? 4 : 1;
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < NPT / EPT; ++k) {
+    float g = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) g += X[k * EPT + j] >= cut ? X[k * EPT + j] : 0.f;
+    s += (double)g;
+  }
+  return s;
+}
+
+// Nucleus (top-p) cuts of the target and draft weights P and Q (totals zt,
+// zd; largest entries at most pmax, qmax): the largest value `cut` whose mass
+// at or above it still reaches top_p of the total, found by bisection over
+// the bit patterns of non-negative floats (which order like the values), both
+// rows in one reduction per step.  The kept set {X >= cut} is the smallest
+// set of most likely tokens holding top_p of the mass, with every token tied
+// at the cut.  Entries below the cut are zeroed and zt, zd become the kept
+// mass.  Only P is cut when `both` is false.
+template <bool VEC, int NPT>
+__device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, float pmax,
+                                   float qmax, float top_p, double& zt, double& zd, double* lds,
+                                   float& cut_t, float& cut_d) {
+  // every bound and total below is block-uniform: kept in scalar registers
+  uint32_t lo_t = 0u, hi_t = __builtin_amdgcn_readfirstlane(__float_as_uint(pmax) + 1u);
+  uint32_t lo_d = 0u, hi_d = __builtin_amdgcn_readfirstlane(both ? __float_as_uint(qmax) + 1u : 1u);
+  const double want_t = uniform_f64((double)top_p * zt), want_d = uniform_f64((double)top_p * zd);
+  double kt = uniform_f64(zt), kd = uniform_f64(zd);  // kept mass at the lower bounds
+  int set = 0;
+  while ((hi_t - lo_t > 1u) | (hi_d - lo_d > 1u)) {  // block-uniform
+    const uint32_t mt = lo_t + (hi_t - lo_t) / 2u, md = lo_d + (hi_d - lo_d) / 2u;
+    double st = kept_sum<VEC, NPT>(P, __uint_as_float(mt));
+    double sd = both ? kept_sum<VEC, NPT>(Q, __uint_as_float(md)) : 0.0;
+    block_sum2_set<kNodeBlock>(st, sd, lds, set);
+    set ^= 1;
+    if (hi_t - lo_t > 1u) {
+      if (st >= want_t) {
+        lo_t = mt;
+        kt = st;
+      } else {
+        hi_t = mt;
+      }
+    }
+    if (hi_d - lo_d > 1u) {
+      if (sd >= want_d) {
+        lo_d = md;
+        kd = sd;
+      } else {
+        hi_d = md;
+      }
+    }
+  }
+  cut_t = __uint_as_float(lo_t);
+  cut_d = __uint_as_float(lo_d);
+#pragma unroll
+  for (int e = 0; e < NPT; ++e) {
+    P[e] = P[e] >= cut_t ? P[e] : 0.f;
+    if (both) Q[e] = Q[e] >= cut_d ? Q[e] : 0.f;
+  }
+  zt = kt;
+  if (both) zd = kd;
 }
 
 // v plus the partner lane's v at exchange stage S: the lanes l ^ 32, l ^ 16,
@@ -557,6 +674,7 @@ struct NodeLds {
   int ok[ST_MAX_NODES];                                           // token in range
   float redf[2 * kMaxWaves];
   double red[2 * kMaxWaves];
+  double red4[4 * kMaxWaves];
   double u_draw;
   DrawLds draw;
 };
@@ -570,7 +688,9 @@ struct NodeLds {
 // replacement token from r when no child is accepted (a leaf draws from p_u).
 // The tree is read before the rows' loads are issued, so that waiting for it
 // never waits for them.
-template <bool VEC>
+// EXT: the draft may be probabilities and the rows may be cut to their
+// nucleus (a separate instance, so the plain path keeps its registers).
+template <bool VEC, bool EXT>
 __global__ void __launch_bounds__(kNodeBlock)
 stoch_node_kernel(StochArgs g) {
   constexpr int NPT = kStochMaxV / kNodeBlock, EPT = VEC ? 4 : 1;
@@ -622,7 +742,8 @@ stoch_node_kernel(StochArgs g) {
   bool finite = true;
 #pragma unroll
   for (int e = 0; e < NPT; ++e) {
-    finite &= (bool)isfinite(P[e]) & (bool)isfinite(Q[e]);
+    finite &= (bool)isfinite(P[e]) & (bool)isfinite(Q[e]) &
+              (!EXT || !g.draft_probs || Q[e] >= 0.f);
     mt = fmaxf(mt, P[e]);
     md = fmaxf(md, Q[e]);
   }
@@ -647,7 +768,9 @@ stoch_node_kernel(StochArgs g) {
     if (nk) {
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
-        const float e = exp2_fast((Q[k * EPT + j] - md) * sc);
+        // a draft given as probabilities is used as it is
+        const float e =
+            EXT && g.draft_probs ? Q[k * EPT + j] : exp2_fast((Q[k * EPT + j] - md) * sc);
         Q[k * EPT + j] = in ? e : 0.f;
         sd_ += Q[k * EPT + j];
       }
@@ -656,6 +779,12 @@ stoch_node_kernel(StochArgs g) {
     zd += (double)sd_;
   }
   block_sum2<kNodeBlock>(zt, zd, s.red);
+  // nucleus sampling: both rows restricted to their top-p nucleus (the draft
+  // row only where it is used)
+  float cut_t = 0.f, cut_d = 0.f;
+  if (EXT && g.top_p < 1.f)
+    nucleus_cut<VEC, NPT>(P, Q, nk > 0, 1.f, g.draft_probs ? md : 1.f, g.top_p, zt, zd, s.red4,
+                          cut_t, cut_d);
   const double a = 1.0 / zt;
 
   if (nk == 0) {  // a leaf: the walk stops here with r = p_u
@@ -670,8 +799,11 @@ stoch_node_kernel(StochArgs g) {
     s.kids[rank] = tid;
     s.ok[rank] = ok;
     if (ok) {
-      s.px[rank] = (double)exp2_fast((lt - mt) * sc) * a;
-      s.qx[rank] = (double)exp2_fast((ld - md) * sc) * bq;
+      // the same fp32 weights as the registers hold, cut the same way
+      const float et = exp2_fast((lt - mt) * sc);
+      const float ed = EXT && g.draft_probs ? ld : exp2_fast((ld - md) * sc);
+      s.px[rank] = et >= cut_t ? (double)et * a : 0.0;
+      s.qx[rank] = ed >= cut_d ? (double)ed * bq : 0.0;
       double ua, us;
       node_uniforms(g.seed, g.offset, b, tid, ua, us);
       s.ua[rank] = ua;
@@ -699,7 +831,7 @@ stoch_node_kernel(StochArgs g) {
       const double cn = cc + D;
       const double Dn =
           a * block_sum<kNodeBlock>(resid_sum<VEC>(P, Q, (float)(cn * ratio)), s.red, k & 1);
-      if (Dn > 0.0) {
+      if (Dn > kMassEps) {
         cc = cn;
         D = Dn;
       }
@@ -708,7 +840,7 @@ stoch_node_kernel(StochArgs g) {
     if (accepted < 0) {  // every child rejected: draw from the final residual
       const double total =
           draw_residual<VEC>(P, Q, (float)((cc + D) * ratio), s.u_draw, s.draw, token, tie);
-      if (!(total > 0.0)) {  // the last rejection left no mass: r unchanged
+      if (!(total * a > kMassEps)) {  // the last rejection left no mass: r unchanged
         __syncthreads();
         draw_residual<VEC>(P, Q, (float)(cc * ratio), s.u_draw, s.draw, token, tie);
       }
@@ -793,18 +925,32 @@ int st::stochastic_prepare(const st_tree* tree, int V, const int32_t* tokens,
   return ST_OK;
 }
 
+namespace {
+int node_launch(const st::StochWalkArgs& w, const float* target_logits, const float* draft,
+                int draft_probs, float temperature, float top_p, uint64_t seed, uint64_t offset,
+                int B, void* stream) {
+  const StochArgs g{w.node_off,   w.parent, w.tokens, target_logits, draft,
+                    const_cast<NodeVerdict*>(w.verdict), B, w.T, w.V, w.max_nodes, temperature,
+                    seed,         offset,   w.status, draft_probs, top_p};
+  hipStream_t s = (hipStream_t)stream;
+  const bool vec = (w.V & 3) == 0, ext = draft_probs || top_p < 1.f;
+  if (vec && !ext)
+    hipLaunchKernelGGL((stoch_node_kernel<true, false>), dim3(w.T), dim3(kNodeBlock), 0, s, g);
+  else if (!ext)
+    hipLaunchKernelGGL((stoch_node_kernel<false, false>), dim3(w.T), dim3(kNodeBlock), 0, s, g);
+  else if (vec)
+    hipLaunchKernelGGL((stoch_node_kernel<true, true>), dim3(w.T), dim3(kNodeBlock), 0, s, g);
+  else
+    hipLaunchKernelGGL((stoch_node_kernel<false, true>), dim3(w.T), dim3(kNodeBlock), 0, s, g);
+  return st::check_launch();
+}
+}  // namespace
+
 int st::stochastic_node_launch(const st::StochWalkArgs& w, const float* target_logits,
                                const float* draft_logits, float temperature, uint64_t seed,
                                uint64_t offset, int B, void* stream) {
-  const StochArgs g{w.node_off, w.parent, w.tokens, target_logits, draft_logits,
-                    const_cast<NodeVerdict*>(w.verdict), B, w.T, w.V, w.max_nodes, temperature,
-                    seed, offset, w.status};
-  hipStream_t s = (hipStream_t)stream;
-  if ((w.V & 3) == 0)
-    hipLaunchKernelGGL(stoch_node_kernel<true>, dim3(w.T), dim3(kNodeBlock), 0, s, g);
-  else
-    hipLaunchKernelGGL(stoch_node_kernel<false>, dim3(w.T), dim3(kNodeBlock), 0, s, g);
-  return st::check_launch();
+  return node_launch(w, target_logits, draft_logits, 0, temperature, 1.f, seed, offset, B,
+                     stream);
 }
 
 extern "C" int st_verify_stochastic(const st_tree* tree, int V, const int32_t* tokens,
@@ -819,6 +965,26 @@ extern "C" int st_verify_stochastic(const st_tree* tree, int V, const int32_t* t
                                   ws_bytes, status, w);
   if (rc || (rc = st::stochastic_node_launch(w, target_logits, draft_logits, temperature, seed,
                                              offset, tree->B, stream)))
+    return rc;
+  hipLaunchKernelGGL(stoch_walk_kernel, dim3(tree->B), dim3(ST_WAVE), 0, (hipStream_t)stream, w);
+  return st::check_launch();
+}
+
+extern "C" int st_verify_stochastic_ex(const st_tree* tree, int V, const int32_t* tokens,
+                                       const float* target_logits, const float* draft,
+                                       int draft_is_probs, float temperature, float top_p,
+                                       uint64_t seed, uint64_t offset, int32_t* accept_len,
+                                       int32_t* accept_nodes, int32_t* out_tokens,
+                                       int32_t* near_ties, void* workspace, size_t ws_bytes,
+                                       int32_t* status, void* stream) {
+  if (!(top_p > 0.f && top_p <= 1.f) || (draft_is_probs != 0 && draft_is_probs != 1))
+    return ST_E_INVALID;
+  st::StochWalkArgs w;
+  int rc = st::stochastic_prepare(tree, V, tokens, target_logits, draft, temperature, accept_len,
+                                  accept_nodes, out_tokens, near_ties, workspace, ws_bytes,
+                                  status, w);
+  if (rc || (rc = node_launch(w, target_logits, draft, draft_is_probs, temperature, top_p, seed,
+                              offset, tree->B, stream)))
     return rc;
   hipLaunchKernelGGL(stoch_walk_kernel, dim3(tree->B), dim3(ST_WAVE), 0, (hipStream_t)stream, w);
   return st::check_launch();

@@ -7,7 +7,7 @@ of separate entry points, mask first.  Every call only enqueues kernels."""
 from __future__ import annotations
 
 from .binding import (st_kv_compact, st_tree_attention, st_tree_mask, st_verification_step,
-                      st_verify_greedy, st_verify_stochastic)
+                      st_verify_greedy, st_verify_stochastic, st_verify_stochastic_ex)
 from .device_io import DeviceWorkload
 
 
@@ -24,9 +24,16 @@ def run_attention(dw: DeviceWorkload, scale=None, derive_mask: bool = False):
                       scale=scale, status=b["status"])
 
 
-def run_verify(dw: DeviceWorkload, stochastic: bool):
+def run_verify(dw: DeviceWorkload, stochastic: bool, top_p: float = 1.0, draft=None):
+    """draft: probabilities [T][V] to use instead of the draft logits."""
     b = dw.buf
-    if stochastic:
+    if stochastic and (top_p < 1.0 or draft is not None):
+        st_verify_stochastic_ex(dw.tree, dw.tokens, dw.logits,
+                                dw.draft_logits if draft is None else draft, dw.temperature,
+                                dw.rng_seed, dw.rng_offset, b["accept_len"], b["accept_nodes"],
+                                b["out_tokens"], b["verify_ws"], b["near_ties"], b["status"],
+                                top_p=top_p, draft_is_probs=draft is not None)
+    elif stochastic:
         st_verify_stochastic(dw.tree, dw.tokens, dw.logits, dw.draft_logits, dw.temperature,
                              dw.rng_seed, dw.rng_offset, b["accept_len"], b["accept_nodes"],
                              b["out_tokens"], b["verify_ws"], b["near_ties"], b["status"])
