@@ -742,8 +742,7 @@ stoch_node_kernel(StochArgs g) {
   bool finite = true;
 #pragma unroll
   for (int e = 0; e < NPT; ++e) {
-    finite &= (bool)isfinite(P[e]) & (bool)isfinite(Q[e]) &
-              (!EXT || !g.draft_probs || Q[e] >= 0.f);
+    finite &= isfinite(P[e]) && isfinite(Q[e]) && (!EXT || !g.draft_probs || Q[e] >= 0.f);
     mt = fmaxf(mt, P[e]);
     md = fmaxf(md, Q[e]);
   }
