@@ -25,6 +25,9 @@ Sources (web pages, cited by title and section):
                     left-to-right check, replacement at the first rejection,
                     equal-distribution guarantee), §3.2 (single forward pass)
 
+Token-tree construction (build.py) merges candidate sequences into the tree
+that verification takes.
+
 Every function is pinned by tests marked ``not gpu`` (closed forms, brute
 force, invariants, library routines, hand-worked fixtures in tests/golden).
 The exact decision rule of the stochastic walk (order of siblings, residual
@@ -60,3 +63,4 @@ from .layer import (  # noqa: F401
     rope_angles,
     tree_layer,
 )
+from .build import build_tree, pack_trees  # noqa: F401,E402
