@@ -271,6 +271,38 @@ size_t st_verification_step_workspace(const st_tree* tree, const st_step* step);
 int st_verification_step(const st_tree* tree, const st_step* step, void* workspace,
                          size_t ws_bytes, int32_t* status, void* stream);
 
+/*
+ * st_tree_build -- merge candidate continuations into one token tree per
+ * request, the step before verification (SpecInfer news article, "研究現狀":
+ * the outputs of several small speculative models are merged into one
+ * speculated token tree; SpecInfer developer article §2.1-2.2: candidates that
+ * share a prefix share its nodes, and every node points to its parent).
+ * Request b's root is root_tokens[b] (the last token the target emitted);
+ * candidate k continues it with seqs[b][k][0 .. lens[b][k]-1].  The tree's
+ * nodes are the root and every distinct non-empty prefix of a candidate, the
+ * node of a prefix being the child of the node of that prefix minus its last
+ * token.  Nodes are numbered level by level (so parent < child); within a
+ * level by their parent's number, then by the smallest k whose candidate has
+ * the prefix.
+ *   root_tokens [B], seqs [B][K][Lmax], lens [B][K]   int32 inputs
+ *   n_nodes [B]          nodes of each tree, root included, at most cap
+ *   parent  [B][cap]     request-local parent index (root -1)   } -1 past
+ *   tokens  [B][cap]     token of each node (root: root_tokens)  } n_nodes[b]
+ *   depth   [B][cap]     edges to the root                       }
+ *   node_off [B+1], parent_packed [B*cap], tokens_packed [B*cap]: the same
+ *     trees concatenated in the st_tree layout (entries past node_off[B]
+ *     untouched); all three NULL to skip, written by a second kernel.
+ * A length outside [0, Lmax] counts as 0 and a token outside [0, V) ends its
+ * candidate before it, both setting ST_STATUS_BAD_TOKEN (the root token is
+ * not checked); a tree of more than cap nodes keeps its first cap and sets
+ * ST_STATUS_PATH_OVERFLOW.  Limits: 1 <= K <= 256, K * Lmax <= 8192,
+ * 1 <= cap <= ST_MAX_NODES (ST_E_UNSUPPORTED beyond them).
+ */
+int st_tree_build(int B, int K, int Lmax, int V, int cap, const int32_t* root_tokens,
+                  const int32_t* seqs, const int32_t* lens, int32_t* n_nodes, int32_t* parent,
+                  int32_t* tokens, int32_t* depth, int32_t* node_off, int32_t* parent_packed,
+                  int32_t* tokens_packed, int32_t* status, void* stream);
+
 /* ---------------------------------------------------------------------------
  * The target layer around verification.  The pages fix no architecture; the
  * calls below are the pieces one attention layer needs to run over a token

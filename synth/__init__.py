@@ -23,3 +23,4 @@ from .workloads import (  # noqa: F401
     tree_beam_plus_leaves,
 )
 from .model import model_config, model_weights  # noqa: F401,E402
+from .candidates import make_candidates, TREE_BUILD_CASE  # noqa: F401,E402

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("st_tree_mask", "st_tree_attention", "st_verify_greedy", "st_verify_stochastic",
               "st_kv_compact", "st_status_str", "st_embed", "st_tree_rope_append", "st_linear",
-              "st_linear_workspace", "st_verify_stochastic_ex"):
+              "st_linear_workspace", "st_verify_stochastic_ex", "st_tree_build"):
         assert n in names
 
 

@@ -4,7 +4,8 @@ The target model's side of tree-based speculative decoding for one attention
 layer, as hand-written HIP kernels behind a C ABI (include/st.h, libst.so):
 ancestor mask, tree-masked split-KV attention, greedy and rejection-sampling
 acceptance, KV compaction; and the layer pieces around them (embedding,
-skinny bf16 projections, rotary embedding with the tree-KV append).  This package is the thin Python binding; torch
+skinny bf16 projections, rotary embedding with the tree-KV append), and the
+merge of candidate continuations into a token tree.  This package is the thin Python binding; torch
 provides device memory and streams.
 """
 
@@ -24,6 +25,7 @@ from .binding import (  # noqa: F401
     st_status_str,
     st_tree_attention,
     st_tree_attention_workspace,
+    st_tree_build,
     st_tree_mask,
     st_tree_rope_append,
     st_verification_step,

@@ -83,6 +83,7 @@ def _declare(lib):
         "st_tree_rope_append": (I, [TP, I, I, I, _c.c_float, P, P, I, I, P, P, P, P, P]),
         "st_linear_workspace": (S, [I, I, I]),
         "st_linear": (I, [I, I, I, P, P, P, P, I, P, S, P]),
+        "st_tree_build": (I, [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -280,6 +281,32 @@ def st_verify_stochastic_ex(tree: Tree, tokens, target_logits, draft, temperatur
         float(temperature), float(top_p), int(seed), int(offset), _ptr(accept_len),
         _ptr(accept_nodes), _ptr(out_tokens), _ptr(near_ties), _ptr(workspace), ws_bytes,
         _ptr(status), _stream()), "st_verify_stochastic_ex")
+
+
+def st_tree_build(root_tokens, seqs, lens, V: int, cap: int, n_nodes, parent, tokens, depth,
+                  node_off=None, parent_packed=None, tokens_packed=None, status=None):
+    """Merge candidates seqs [B][K][Lmax] (lengths lens [B][K]) into one
+    token tree per request: padded outputs [B][cap] and n_nodes [B]; with
+    node_off [B+1] / parent_packed / tokens_packed [B*cap] also the
+    concatenated st_tree layout."""
+    B, K, Lmax = seqs.shape
+    _dev(root_tokens, "root_tokens", torch.int32, B)
+    _dev(seqs, "seqs", torch.int32)
+    _dev(lens, "lens", torch.int32, B * K)
+    _dev(n_nodes, "n_nodes", torch.int32, B)
+    for name, t in (("parent", parent), ("tokens", tokens), ("depth", depth)):
+        _dev(t, name, torch.int32, B * cap)
+    packed = [node_off, parent_packed, tokens_packed]
+    if any(t is not None for t in packed):
+        if any(t is None for t in packed):
+            raise ValueError("node_off, parent_packed and tokens_packed go together")
+        _dev(node_off, "node_off", torch.int32, B + 1)
+        _dev(parent_packed, "parent_packed", torch.int32, B * cap)
+        _dev(tokens_packed, "tokens_packed", torch.int32, B * cap)
+    _check(load_library().st_tree_build(
+        B, K, Lmax, int(V), int(cap), _ptr(root_tokens), _ptr(seqs), _ptr(lens), _ptr(n_nodes),
+        _ptr(parent), _ptr(tokens), _ptr(depth), _ptr(node_off), _ptr(parent_packed),
+        _ptr(tokens_packed), _ptr(status), _stream()), "st_tree_build")
 
 
 def candidate_length(t: int, T_est: int, K_max: int) -> int:
