@@ -305,6 +305,97 @@ def bench_layer(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_tree_build(args):
+    """Token-tree construction: 16 requests, 16 candidate continuations of up
+    to 8 tokens each (shared prefixes of random length), vocab 32000, trees of
+    at most 128 nodes, merged and packed into the st_tree layout per call."""
+    import numpy as np
+    import torch
+
+    from synth import TREE_BUILD_CASE, make_candidates
+    from token_tree_verification_st_amd import load_library, st_tree_build
+
+    load_library()
+    torch.cuda.set_device(0)
+    c = TREE_BUILD_CASE
+    B, K, Lmax, V, cap = c["B"], c["K"], c["Lmax"], c["V"], c["cap"]
+    R = 64   # input and output replicas, cycled (they are small; this spreads the launches)
+    cands = [make_candidates(args.seed + r, B, K, Lmax, V) for r in range(R)]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    ins = [tuple(dev(a) for a in cd) for cd in cands]
+    outs = [{k: torch.empty(n, dtype=torch.int32, device="cuda") for k, n in
+             (("n_nodes", B), ("parent", B * cap), ("tokens", B * cap), ("depth", B * cap),
+              ("node_off", B + 1), ("parent_packed", B * cap), ("tokens_packed", B * cap),
+              ("status", 1))} for _ in range(R)]
+
+    def call(i):
+        root, seqs, lens = ins[i % R]
+        o = outs[i % R]
+        st_tree_build(root, seqs, lens, V, cap, o["n_nodes"], o["parent"], o["tokens"],
+                      o["depth"], node_off=o["node_off"], parent_packed=o["parent_packed"],
+                      tokens_packed=o["tokens_packed"], status=o["status"])
+
+    for o in outs:
+        o["status"].zero_()
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    Ks = args.steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(Ks):
+            call(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t
+    us = e0.elapsed_time(e1) / Ks * 1e3
+    assert not any(int(o["status"].item()) for o in outs), "device status set"
+    nodes = int(outs[0]["node_off"][B].item())
+    in_bytes = (B * K * Lmax + B * K + B) * 4
+    out_bytes = (B * cap * 3 + B + (B + 1) + 2 * nodes) * 4
+    gbs = (in_bytes + out_bytes) / (us * 1e-6) / 1e9
+    line = {
+        "metric": "token trees built per second (16 requests x 16 candidates x 8 tokens)",
+        "value": round(B / (wall / Ks), 1), "unit": "trees/s", "n_gpus": 1, "steps": Ks,
+        "warmup": args.warmup, "ms_per_step": round(wall / Ks * 1e3, 5),
+        "gpu_ms_per_step": round(us * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic (seeded PCG64 candidates with shared prefixes of random length)",
+        "config": {"workload": "tree_build", **c, "nodes_first_replica": nodes,
+                   "launch": "hip graph"},
+        "per_call_us": {"tree_build": round(us, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": None,
+                     "kernel": "st_tree_build (latency-bound: two launches, a few barriers "
+                               "per level)", "algorithmic_bytes": in_bytes + out_bytes,
+                     "avg_launch_us": round(us, 3),
+                     "timing": f"HIP events around a graph of {Ks} back-to-back calls"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            root, seqs, lens = cands[runs % R]
+            r = oracle.build_tree(root, seqs, lens, V, cap)
+            oracle.pack_trees(r["n_nodes"], r["parent"], r["tokens"])
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_seconds, 5.0) or runs >= 10000:
+                break
+        line["cpu_baseline"] = {"value": round(B * runs / el, 1), "unit": "trees/s", "cores": 1,
+                                "kind": "oracle", "sample": f"{runs} oracle merges of the same "
+                                f"case (pure Python, one thread) in {el:.1f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -312,6 +403,9 @@ def main():
         sys.exit(2)
     if args.workload == "llama7b_layer":
         bench_layer(args)
+        return
+    if args.workload == "tree_build":
+        bench_tree_build(args)
         return
     import numpy as np
     import torch

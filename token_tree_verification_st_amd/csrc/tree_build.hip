@@ -9,8 +9,10 @@
 // within a level by the parent's number, then by the smallest candidate index
 // that has the prefix.
 //
-// One workgroup per request, one thread per candidate.  The candidates'
-// tokens sit in LDS.  Level j is done in three barrier-separated phases:
+// One workgroup per request (a single wavefront for up to 64 candidates, so
+// the barriers cost nothing), one thread per candidate.  The candidates'
+// tokens sit in LDS.  Level j is done in three barrier-separated phases, each
+// a branch-free pass over the candidates' LDS words:
 //   1. each candidate long enough finds its representative: the smallest
 //      candidate whose prefix node at level j-1 is the same and whose token
 //      at j is the same (equal parent node and equal token = equal prefix);
@@ -26,20 +28,46 @@
 // node_off / parent / tokens layout of st_tree.
 #include "st_internal.h"
 
+#include <limits.h>
+
 namespace {
 
 constexpr int kMaxCand = 256;    // candidates per request (one thread each)
 constexpr int kMaxCells = 8192;  // K * Lmax tokens staged in LDS (32 KB)
 
-__global__ void __launch_bounds__(256)
+// Barrier-and-reduce helpers: a workgroup of one wavefront needs no LDS
+// reduction, a ballot does.
+template <int NT>
+__device__ inline bool sync_or(bool p) {
+  if constexpr (NT == ST_WAVE) {
+    __syncthreads();
+    return __ballot(p) != 0ull;
+  } else {
+    return __syncthreads_or(p);
+  }
+}
+template <int NT>
+__device__ inline int sync_count(bool p) {
+  if constexpr (NT == ST_WAVE) {
+    __syncthreads();
+    return __popcll(__ballot(p));
+  } else {
+    return __syncthreads_count(p);
+  }
+}
+
+// NT threads (one wavefront when K <= 64, else 256).
+template <int NT>
+__global__ void __launch_bounds__(NT)
 tree_build_kernel(const int32_t* __restrict__ root_tokens, const int32_t* __restrict__ seqs,
                   const int32_t* __restrict__ lens, int K, int Lmax, int V, int cap,
                   int32_t* __restrict__ n_nodes, int32_t* __restrict__ parent,
                   int32_t* __restrict__ tokens, int32_t* __restrict__ depth, int32_t* status) {
   __shared__ int s_tok[kMaxCells];
-  __shared__ int s_use[kMaxCand];  // usable length of each candidate
-  __shared__ int s_cur[kMaxCand];  // node number of the candidate's prefix at the last level
-  __shared__ int s_rep[kMaxCand];  // representative at this level, -1 if too short
+  // per candidate: (node of its prefix at the last level, token at this
+  // level) packed in one word, all ones once the candidate is too short
+  __shared__ uint64_t s_kt[kMaxCand];
+  __shared__ int s_rk[kMaxCand];   // representatives' order key (parent * 256 + k), else INT_MAX
   __shared__ int s_new[kMaxCand];  // node number of each representative at this level
   const int b = blockIdx.x, tid = threadIdx.x;
   const int32_t* sq = seqs + (size_t)b * K * Lmax;
@@ -70,51 +98,50 @@ tree_build_kernel(const int32_t* __restrict__ root_tokens, const int32_t* __rest
       }
     }
     use = n;
-    s_use[tid] = n;
-    s_cur[tid] = 0;  // every candidate starts at the root
   }
+  // every candidate starts at the root (node 0)
+  s_kt[tid] = use > 0 ? (uint64_t)(uint32_t)s_tok[tid * Lmax] : ~0ull;
   __syncthreads();
   int total = 1;  // nodes numbered so far (the root)
   for (int j = 0; j < Lmax; ++j) {
-    // phase 1: representative of this candidate's prefix of length j + 1
-    const bool act = tid < K && use > j;
-    int rep = -1, x = 0, cur = 0;
-    if (act) {
-      cur = s_cur[tid];
-      x = s_tok[tid * Lmax + j];
-      rep = tid;
-      for (int k = 0; k < tid; ++k) {
-        if (s_use[k] > j && s_cur[k] == cur && s_tok[k * Lmax + j] == x) {
-          rep = k;
-          break;
-        }
-      }
+    // phase 1: representative of this candidate's prefix of length j + 1, the
+    // smallest candidate with the same parent node and token (no early exit:
+    // the LDS reads of the loop pipeline)
+    const bool act = use > j;
+    const uint64_t mine = s_kt[tid];
+    int rep = tid;
+#pragma unroll 8
+    for (int k = 0; k < K; ++k) {
+      const bool eq = s_kt[k] == mine;
+      rep = (eq && k < rep) ? k : rep;
     }
-    if (tid < K) s_rep[tid] = rep;
-    if (!__syncthreads_or(act)) break;  // no candidate reaches this level
+    const int cur = (int)(mine >> 32);
+    const bool is_rep = act && rep == tid;
+    s_rk[tid] = is_rep ? cur * kMaxCand + tid : INT_MAX;
+    if (!sync_or<NT>(act)) break;  // no candidate reaches this level
 
     // phase 2: number the representatives by (parent number, candidate)
-    const bool is_rep = act && rep == tid;
     if (is_rep) {
+      const int key = cur * kMaxCand + tid;
       int rank = 0;
-      for (int k = 0; k < K; ++k) {
-        if (s_rep[k] == k) {
-          const int ck = s_cur[k];
-          rank += (ck < cur) | ((ck == cur) & (k < tid));
-        }
-      }
+#pragma unroll 8
+      for (int k = 0; k < K; ++k) rank += s_rk[k] < key;
       const int num = total + rank;
       s_new[tid] = num;
       if (num < cap) {
         parent[ob + num] = cur;
-        tokens[ob + num] = x;
+        tokens[ob + num] = s_tok[tid * Lmax + j];
         depth[ob + num] = j + 1;
       }
     }
-    total += __syncthreads_count(is_rep);
+    total += sync_count<NT>(is_rep);
 
-    // phase 3: follow the representative to this level's node
-    if (act) s_cur[tid] = s_new[rep];
+    // phase 3: follow the representative to this level's node, with the
+    // token of the next level
+    const bool next = use > j + 1;
+    s_kt[tid] = next ? ((uint64_t)(uint32_t)s_new[rep] << 32) |
+                           (uint32_t)s_tok[tid * Lmax + j + 1]
+                     : ~0ull;
     __syncthreads();
   }
 
@@ -175,8 +202,12 @@ extern "C" int st_tree_build(int B, int K, int Lmax, int V, int cap, const int32
                      (tokens_packed != nullptr);
   if (packed != 0 && packed != 3) return ST_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(tree_build_kernel, dim3(B), dim3(256), 0, s, root_tokens, seqs, lens, K,
-                     Lmax, V, cap, n_nodes, parent, tokens, depth, status);
+  if (K <= ST_WAVE)
+    hipLaunchKernelGGL(tree_build_kernel<ST_WAVE>, dim3(B), dim3(ST_WAVE), 0, s, root_tokens, seqs,
+                       lens, K, Lmax, V, cap, n_nodes, parent, tokens, depth, status);
+  else
+    hipLaunchKernelGGL(tree_build_kernel<256>, dim3(B), dim3(256), 0, s, root_tokens, seqs, lens,
+                       K, Lmax, V, cap, n_nodes, parent, tokens, depth, status);
   int rc = st::check_launch();
   if (rc || !packed) return rc;
   hipLaunchKernelGGL(tree_pack_kernel, dim3(B), dim3(256), 0, s, n_nodes, parent, tokens, B, cap,
