@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--traffic", default=None,
                     help="traffic summary (default profiles/attention_<workload>_traffic.md); "
                          "used only if it was taken from the current attention sources")
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
+                    help="also time st_tree_attention_paged with this block size")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -496,10 +498,55 @@ def main():
         g_step = capture(step_fn)
         wall, gpu_span_ms = timed_replay(g_step)
     ms_per_step = wall / K * 1e3
+    spread = {}
+    if not args.eager:
+        # four more replays of the same graph: the spread of the per-step time
+        reps_ms = [gpu_span_ms / K] + [timed_replay(g_step)[1] / K for _ in range(4)]
+        q = np.percentile(reps_ms, [10, 50, 90])
+        spread = {"replays": len(reps_ms), "p10_us": round(q[0] * 1e3, 3),
+                  "p50_us": round(q[1] * 1e3, 3), "p90_us": round(q[2] * 1e3, 3)}
+    # one step after a 1 GiB write has pushed every input out of the caches,
+    # events around that step only (median of 5)
+    flush = torch.empty(REPLICA_BYTES // 4, dtype=torch.float32, device="cuda")
+    single = []
+    for i in range(5):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step_fn(reps[i % R])
+        e1.record()
+        torch.cuda.synchronize()
+        single.append(e0.elapsed_time(e1) * 1e3)
+    del flush
     per_call = {}
     for c in calls:
         _, ms = timed_replay(capture(fns[c]))
         per_call[c] = ms / K * 1e3  # us per launch
+    if args.paged:
+        # the same attention over a paged pool (blocks scattered by a seeded
+        # permutation), one pool per replica
+        from synth import make_paged
+        from token_tree_verification_st_amd import st_tree_attention_paged
+
+        def dev16(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+            return torch.from_numpy(a).cuda()
+
+        kp_h, vp_h, bt_h = make_paged(args.seed, wl.k_cache, wl.v_cache, args.paged)
+        pools = [(dev16(kp_h), dev16(vp_h)) for _ in range(R)]
+        bt = torch.from_numpy(bt_h).cuda()
+
+        def paged_call(d, i=[0]):
+            kp, vp = pools[i[0] % R]
+            i[0] += 1
+            st_tree_attention_paged(d.tree, d.q, kp, vp, bt, d.prefix_len, d.max_prefix,
+                                    d.buf["mask"], d.buf["out"], d.buf["lse"], d.buf["attn_ws"],
+                                    status=d.buf["status"])
+
+        _, ms = timed_replay(capture(paged_call))
+        per_call["attention_paged"] = ms / K * 1e3
+        del pools
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -550,9 +597,12 @@ def main():
                    "acceptance": "stochastic" if stochastic else "greedy",
                    **({"top_p": args.top_p, "draft": "probabilities" if args.draft_probs
                        else "logits"} if ext else {}),
-                   "replicas": R, "launch": "eager" if args.eager else "hip graph"},
+                   "replicas": R, "launch": "eager" if args.eager else "hip graph",
+                   **({"paged_block": args.paged} if args.paged else {})},
         "per_call_us": {c: round(v, 3) for c, v in per_call.items()},
         "hbm_frac_step": round(attn_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_spread": spread,
+        "single_step_us_after_flush": round(float(np.median(single)), 3),
         "accepted_tokens_per_step": int((al + 1).sum()),
         "roofline": roof,
     }

@@ -60,6 +60,7 @@ extern "C" {
 #define ST_STATUS_PATH_OVERFLOW 8 /* accepted path longer than max_depth        */
 #define ST_STATUS_BAD_PREFIX 16   /* prefix_len outside [0, max_prefix], or the
                                      request's slots run past S_max             */
+#define ST_STATUS_BAD_BLOCK 32    /* a block-table entry outside [0, n_blocks)  */
 
 #define ST_MAX_NODES 256          /* per request                                */
 
@@ -121,6 +122,33 @@ int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtyp
                       const int32_t* prefix_len, int max_prefix, const uint64_t* mask,
                       void* out, float* lse, void* workspace, size_t ws_bytes, int32_t* status,
                       void* stream);
+
+/*
+ * st_tree_attention_paged -- st_tree_attention over a paged KV pool: the
+ * keys and values of request b are not one contiguous [S_max][D] run per kv
+ * head but fixed-size blocks picked by a per-request block table (the paged
+ * KV memory that the SpecInfer news article and the vAttention notes contrast
+ * with contiguous per-request KV).  Logical slot k of request b (prefix keys
+ * k < prefix_len[b], node i at prefix_len[b] + i, as before) lives in row
+ * k % block_size of physical block block_table[b][k / block_size].
+ *   k_pool, v_pool  [n_blocks][Hkv][block_size][D] of `dtype`
+ *   block_table     [B][max_blocks] int32; the logical capacity is
+ *                   S_max = max_blocks * block_size; only the entries that
+ *                   cover slots below prefix_len[b] + N_b are read.  An entry
+ *                   outside [0, n_blocks) sets ST_STATUS_BAD_BLOCK and reads
+ *                   block 0 or n_blocks-1 instead (never outside the pool).
+ *   block_size      a power of two from 32 to 4096
+ * Everything else, including the workspace size (st_tree_attention_workspace
+ * with the same arguments), as for st_tree_attention; the arithmetic is the
+ * same, so the outputs equal those of st_tree_attention on the gathered
+ * contiguous caches bit for bit.
+ */
+int st_tree_attention_paged(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype,
+                            float scale, const void* q, const void* k_pool, const void* v_pool,
+                            int n_blocks, int block_size, const int32_t* block_table,
+                            int max_blocks, const int32_t* prefix_len, int max_prefix,
+                            const uint64_t* mask, void* out, float* lse, void* workspace,
+                            size_t ws_bytes, int32_t* status, void* stream);
 
 /* Bytes of workspace st_verify_greedy needs. */
 size_t st_verify_greedy_workspace(const st_tree* tree, int V);
@@ -223,6 +251,21 @@ int st_kv_compact(int B, int Hkv, int D, st_dtype dtype, void* k_cache, void* v_
                   const int32_t* prefix_len, const int32_t* accept_len,
                   const int32_t* accept_nodes, int max_path, int32_t* src_slot, int32_t* new_len,
                   int32_t* status, void* stream);
+
+/*
+ * st_kv_compact_paged -- st_kv_compact on a paged pool (layout and block
+ * table as for st_tree_attention_paged; block_size any power of two up to
+ * 4096): logical slot P + j takes what logical slot P + path[j] held, each
+ * translated through the request's block table.  The table entries of one
+ * request must name distinct blocks (the moves are in place).  src_slot and
+ * new_len hold logical slots.  An out-of-range entry sets
+ * ST_STATUS_BAD_BLOCK and is clamped into the pool.
+ */
+int st_kv_compact_paged(int B, int Hkv, int D, st_dtype dtype, void* k_pool, void* v_pool,
+                        int n_blocks, int block_size, const int32_t* block_table, int max_blocks,
+                        const int32_t* prefix_len, const int32_t* accept_len,
+                        const int32_t* accept_nodes, int max_path, int32_t* src_slot,
+                        int32_t* new_len, int32_t* status, void* stream);
 
 /*
  * st_verification_step -- one verification step of one layer in one call:

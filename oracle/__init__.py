@@ -64,3 +64,4 @@ from .layer import (  # noqa: F401
     tree_layer,
 )
 from .build import build_tree, pack_trees  # noqa: F401,E402
+from .paged import gather_paged, kv_compact_paged, scatter_paged  # noqa: F401,E402

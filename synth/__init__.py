@@ -24,3 +24,4 @@ from .workloads import (  # noqa: F401
 )
 from .model import model_config, model_weights  # noqa: F401,E402
 from .candidates import make_candidates, TREE_BUILD_CASE  # noqa: F401,E402
+from .paged import make_paged  # noqa: F401,E402

@@ -19,11 +19,13 @@ from .binding import (  # noqa: F401
     load_library,
     st_embed,
     st_kv_compact,
+    st_kv_compact_paged,
     st_linear,
     st_linear_workspace,
     st_mask_words,
     st_status_str,
     st_tree_attention,
+    st_tree_attention_paged,
     st_tree_attention_workspace,
     st_tree_build,
     st_tree_mask,

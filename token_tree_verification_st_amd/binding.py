@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libst.so")
 ST_F32, ST_BF16 = 0, 1
 ST_MAX_NODES = 256
 STATUS_BITS = {1: "bad parent", 2: "bad token", 4: "non-finite logit", 8: "path overflow",
-               16: "bad prefix length"}
+               16: "bad prefix length", 32: "block-table entry out of range"}
 
 
 class StTree(ctypes.Structure):
@@ -84,6 +84,9 @@ def _declare(lib):
         "st_linear_workspace": (S, [I, I, I]),
         "st_linear": (I, [I, I, I, P, P, P, P, I, P, S, P]),
         "st_tree_build": (I, [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "st_tree_attention_paged": (I, [TP, I, I, I, I, _c.c_float, P, P, P, I, I, P, I, P, I, P,
+                                        P, P, P, S, P, P]),
+        "st_kv_compact_paged": (I, [I, I, I, I, P, P, I, I, P, I, P, P, P, I, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -214,6 +217,38 @@ def st_tree_attention(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix: i
         _ptr(status), _stream()), "st_tree_attention")
 
 
+def st_tree_attention_paged(tree: Tree, q, k_pool, v_pool, block_table, prefix_len,
+                            max_prefix: int, mask, out, lse=None, workspace=None,
+                            scale: Optional[float] = None, status=None):
+    """Tree attention over a paged pool: k_pool / v_pool [n_blocks][Hkv][block][D],
+    block_table int32 [B][max_blocks]; other arguments as st_tree_attention."""
+    T, Hq, D = q.shape
+    n_blocks, Hkv, bs, D2 = k_pool.shape
+    B, max_blocks = block_table.shape
+    if D2 != D or tuple(v_pool.shape) != tuple(k_pool.shape) or T != tree.T or B != tree.B:
+        raise ValueError("shape mismatch between q, pools, block table and tree")
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("out", out)):
+        _dev(t, name, q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _dev(block_table, "block_table", torch.int32)
+    _dev(prefix_len, "prefix_len", torch.int32, B)
+    if mask is not None:
+        _dev(mask, "mask", torch.int64, tree.T * tree.W)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, T * Hq)
+    need = st_tree_attention_workspace(tree, Hq, Hkv, D, q.dtype, max_prefix)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        raise ValueError(f"workspace needs {need} bytes")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(load_library().st_tree_attention_paged(
+        tree.ref, Hq, Hkv, D, _dtype_code(q), scale, _ptr(q), _ptr(k_pool), _ptr(v_pool),
+        n_blocks, bs, _ptr(block_table), max_blocks, _ptr(prefix_len), max_prefix, _ptr(mask),
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _ptr(status), _stream()),
+        "st_tree_attention_paged")
+
+
 def st_verify_greedy_workspace(tree: Tree, V: int) -> int:
     return load_library().st_verify_greedy_workspace(tree.ref, V)
 
@@ -316,6 +351,29 @@ def candidate_length(t: int, T_est: int, K_max: int) -> int:
     if T_est <= 0 or K_max < 1:
         raise ValueError("T_est must be positive and K_max at least 1")
     return max(1, int(round(K_max * (1.0 - t / T_est))))
+
+
+def st_kv_compact_paged(k_pool, v_pool, block_table, prefix_len, accept_len, accept_nodes,
+                        src_slot, new_len, status=None):
+    """st_kv_compact on a paged pool [n_blocks][Hkv][block][D] (updated in
+    place) through block_table int32 [B][max_blocks]."""
+    n_blocks, Hkv, bs, D = k_pool.shape
+    B, max_blocks = block_table.shape
+    _dev(k_pool, "k_pool")
+    _dev(v_pool, "v_pool", k_pool.dtype)
+    if tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("v_pool must match k_pool")
+    _dev(block_table, "block_table", torch.int32)
+    max_path = accept_nodes.shape[-1]
+    _dev(prefix_len, "prefix_len", torch.int32, B)
+    _dev(accept_len, "accept_len", torch.int32, B)
+    _dev(accept_nodes, "accept_nodes", torch.int32, B * max_path)
+    _dev(src_slot, "src_slot", torch.int32, B * max_path)
+    _dev(new_len, "new_len", torch.int32, B)
+    _check(load_library().st_kv_compact_paged(
+        B, Hkv, D, _dtype_code(k_pool), _ptr(k_pool), _ptr(v_pool), n_blocks, bs,
+        _ptr(block_table), max_blocks, _ptr(prefix_len), _ptr(accept_len), _ptr(accept_nodes),
+        max_path, _ptr(src_slot), _ptr(new_len), _ptr(status), _stream()), "st_kv_compact_paged")
 
 
 def st_kv_compact(k_cache, v_cache, prefix_len, accept_len, accept_nodes, src_slot, new_len,

@@ -63,7 +63,35 @@ struct AttnArgs {
   int items;       // B * Hkv * NS * n_rblk
   int per_xcd;     // ceil(items / 8)
   float scale_log2;
+  st::KvPaging pg; // pg.bt null: contiguous caches
 };
+
+// First element of key row `key` of (request b, kv head g): contiguous
+// [B][Hkv][S_max][D], or through the block table into a paged pool
+// [n_blocks][Hkv][block][D] (an entry outside [0, n_blocks) is clamped and
+// flagged, so every address stays inside the pool).  Chunks start at
+// multiples of 32 keys and blocks hold a multiple of 32, so the rows of one
+// chunk never leave its block.
+__device__ inline int table_entry(const AttnArgs& a, int b, int key) {
+  const int e = a.pg.bt[(size_t)b * a.pg.bt_stride + (key >> a.pg.lbs)];
+  const int phys = min(max(e, 0), a.pg.n_blocks - 1);
+  if (phys != e) st::set_status(a.status, ST_STATUS_BAD_BLOCK);
+  return phys;
+}
+
+template <typename T>
+__device__ inline const T* kv_block_row(const AttnArgs& a, const void* cache, int phys, int g,
+                                        int key, int D) {
+  return (const T*)cache +
+         ((((size_t)phys * a.Hkv + g) << a.pg.lbs) + (key & ((1 << a.pg.lbs) - 1))) * D;
+}
+
+template <typename T>
+__device__ inline const T* kv_row(const AttnArgs& a, const void* cache, int b, int g, int key,
+                                  int D) {
+  if (!a.pg.bt) return (const T*)cache + (((size_t)b * a.Hkv + g) * a.S_max + key) * D;
+  return kv_block_row<T>(a, cache, table_entry(a, b, key), g, key, D);
+}
 
 struct Item {
   int w, b, g, split, rblk;
@@ -254,14 +282,18 @@ __device__ __forceinline__ void wait_chunks(int n) {
 // This wavefront's share (row group rw of RWV) of the direct loads of one
 // 32-key chunk starting at key kt; key rows past klast are clamped to it.  The
 // chunk base is wave-uniform, each lane adds a 32-bit offset.
-template <int D, int RWV>
-__device__ __forceinline__ void chunk_dma(uint16_t* sK, uint16_t* sV, const uint16_t* kg,
-                                          const uint16_t* vg, int kt, int klast, int rw,
-                                          int lane) {
+// (PAGED: `phys` is the block that holds the chunk, looked up beforehand.)
+template <int D, int RWV, bool PAGED>
+__device__ __forceinline__ void chunk_dma(uint16_t* sK, uint16_t* sV, const AttnArgs& a,
+                                          const Item& it, const uint16_t* kgp,
+                                          const uint16_t* vgp, int kt, int klast, int rw,
+                                          int lane, int phys = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass never runs this body
   constexpr int CH = D / 8, RPI = 64 / CH, INST = kCK / RPI, PER = INST / RWV;
-  const uint16_t* kb = kg + (size_t)kt * D;
-  const uint16_t* vb = vg + (size_t)kt * D;
+  const uint16_t* kb =
+      PAGED ? kv_block_row<uint16_t>(a, a.k, phys, it.g, kt, D) : kgp + (size_t)kt * D;
+  const uint16_t* vb =
+      PAGED ? kv_block_row<uint16_t>(a, a.v, phys, it.g, kt, D) : vgp + (size_t)kt * D;
   const int lim = klast - kt;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -408,7 +440,7 @@ __device__ __forceinline__ void write_row_out(const AttnArgs& a, int grow, int g
 // RWV row groups of RBW 16-row blocks; KWV = 4 / RWV key groups; MINB
 // workgroups per CU (two let one workgroup's softmax run while the other's
 // MFMAs do).
-template <int D, int NSTAGE, int RWV, int RBW, int MINB = 1>
+template <int D, int NSTAGE, int RWV, int RBW, int MINB = 1, bool PAGED = false>
 __global__ void __launch_bounds__(256, MINB)
 attn_stream_kernel(AttnArgs a) {
   constexpr int KWV = 4 / RWV;
@@ -441,6 +473,7 @@ attn_stream_kernel(AttnArgs a) {
   const int rw = wave % RWV, kg = wave / RWV;
   const int r16 = lane & 15, grp = lane >> 4;
   const int k0 = it.split * a.KS;
+  // contiguous caches: the (request, head) base, fixed for the workgroup
   const size_t head_off = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
   const uint16_t* kgp = (const uint16_t*)a.k + head_off;
   const uint16_t* vgp = (const uint16_t*)a.v + head_off;
@@ -470,7 +503,11 @@ attn_stream_kernel(AttnArgs a) {
   const int niter = (nch + KWV - 1) / KWV;       // the same for every wavefront
   const int want = min(PRIME, nmine);
   // the first chunk goes first, then Q and the masks, then the rest of the ring
-  if (nmine > 0) chunk_dma<D, RWV>(ring, ring + kCK * D, kgp, vgp, k0 + kg * kCK, klast, rw, lane);
+  // paged pool: the block of each chunk is looked up one refill ahead
+  auto entry = [&](int c) { return PAGED ? table_entry(a, it.b, k0 + c * kCK) : 0; };
+  if (nmine > 0)
+    chunk_dma<D, RWV, PAGED>(ring, ring + kCK * D, a, it, kgp, vgp, k0 + kg * kCK, klast, rw,
+                             lane, entry(kg));
 
   // Q of the workgroup's rows (rows past the end repeat the last): staged in
   // LDS once when several key groups share the rows, else loaded directly.
@@ -523,8 +560,8 @@ attn_stream_kernel(AttnArgs a) {
 #pragma unroll
   for (int s = 1; s < PRIME; ++s)
     if (s < nmine)
-      chunk_dma<D, RWV>(ring + s * STAGE, ring + s * STAGE + kCK * D, kgp, vgp,
-                        k0 + (s * KWV + kg) * kCK, klast, rw, lane);
+      chunk_dma<D, RWV, PAGED>(ring + s * STAGE, ring + s * STAGE + kCK * D, a, it, kgp, vgp,
+                               k0 + (s * KWV + kg) * kCK, klast, rw, lane, entry(s * KWV + kg));
   wait_chunks<PRIME - 1, DPC>(want - 1);  // the first chunk, Q and the masks are older
   if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
   if (need_mask) {
@@ -575,6 +612,7 @@ attn_stream_kernel(AttnArgs a) {
     // A ring of one's own: compute chunk r, then refill its stage with chunk
     // r + NSTAGE; no other wavefront reads it, so no barrier is needed.
     int stage = 0;
+    int next = NSTAGE < nmine ? entry(NSTAGE * KWV + kg) : 0;  // block of the next refill
     for (int r = 0; r < nmine; ++r) {
       wait_chunks<NSTAGE - 1, DPC>(min(NSTAGE - 1, nmine - r - 1));
       __builtin_amdgcn_sched_barrier(0);
@@ -584,8 +622,9 @@ attn_stream_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       if (r + NSTAGE < nmine) {
         uint16_t* sb = ring + stage * STAGE;
-        chunk_dma<D, RWV>(sb, sb + kCK * D, kgp, vgp, k0 + ((r + NSTAGE) * KWV + kg) * kCK,
-                          klast, rw, lane);
+        chunk_dma<D, RWV, PAGED>(sb, sb + kCK * D, a, it, kgp, vgp,
+                                 k0 + ((r + NSTAGE) * KWV + kg) * kCK, klast, rw, lane, next);
+        if (PAGED && r + NSTAGE + 1 < nmine) next = entry((r + NSTAGE + 1) * KWV + kg);
       }
       __builtin_amdgcn_sched_barrier(0);
       stage = stage + 1 == NSTAGE ? 0 : stage + 1;
@@ -595,14 +634,17 @@ attn_stream_kernel(AttnArgs a) {
     // (after the barrier, so every row group is done with chunk r - 1) refill
     // the stage chunk r - 1 used with chunk r + NSTAGE - 1.
     int stage = 0, refill = NSTAGE - 1;
+    int next = NSTAGE - 1 < nmine ? entry((NSTAGE - 1) * KWV + kg) : 0;  // next refill's block
     for (int r = 0; r < niter; ++r) {
       wait_chunks<NSTAGE - 2, DPC>(min(NSTAGE - 2, nmine - r - 1));
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
       if (r + NSTAGE - 1 < nmine) {
         uint16_t* sb = ring + refill * STAGE;
-        chunk_dma<D, RWV>(sb, sb + kCK * D, kgp, vgp, k0 + ((r + NSTAGE - 1) * KWV + kg) * kCK,
-                          klast, rw, lane);
+        chunk_dma<D, RWV, PAGED>(sb, sb + kCK * D, a, it, kgp, vgp,
+                                 k0 + ((r + NSTAGE - 1) * KWV + kg) * kCK, klast, rw, lane,
+                                 next);
+        if (PAGED && r + NSTAGE < nmine) next = entry((r + NSTAGE) * KWV + kg);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (r < nmine) {
@@ -764,9 +806,6 @@ attn_valu_kernel(AttnArgs a) {
     mw2 = sRow[r][2];
     mw3 = sRow[r][3];
   }
-  const size_t head_off = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
-  const Tin* kg = (const Tin*)a.k + head_off;
-  const Tin* vg = (const Tin*)a.v + head_off;
 
   float acc[DJ];
 #pragma unroll
@@ -780,8 +819,8 @@ attn_valu_kernel(AttnArgs a) {
     for (int e = tid; e < KT * D; e += 256) {
       const int kr = e / D, d = e % D;
       const bool ok = kr < nk;
-      sK[kr][d] = ok ? load_val(kg + (size_t)(kt + kr) * D + d) : 0.f;
-      sV[kr][d] = ok ? load_val(vg + (size_t)(kt + kr) * D + d) : 0.f;
+      sK[kr][d] = ok ? load_val(kv_row<Tin>(a, a.k, it.b, it.g, kt + kr, D) + d) : 0.f;
+      sV[kr][d] = ok ? load_val(kv_row<Tin>(a, a.v, it.b, it.g, kt + kr, D) + d) : 0.f;
     }
     __syncthreads();
     float dot[KJ];
@@ -1038,7 +1077,8 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
                             int S_max, const int32_t* prefix_len, int max_prefix,
                             const uint64_t* mask, void* out, float* lse, void* workspace,
                             size_t ws_bytes, int32_t* status, void* stream,
-                            const st::CompactArgs* compact, const st::ArgmaxJob* argmax) {
+                            const st::CompactArgs* compact, const st::ArgmaxJob* argmax,
+                            const st::KvPaging* paging) {
   Plan p;
   int rc = make_plan(tree, Hq, Hkv, D, dtype, max_prefix, p);
   if (rc) return rc;
@@ -1077,6 +1117,7 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
   a.items = p.items;
   a.per_xcd = p.per_xcd;
   a.scale_log2 = scale * kLog2e;
+  a.pg = paging ? *paging : st::KvPaging{nullptr, 0, 0, 0};
   a.am = st::ArgmaxJob{nullptr, nullptr, 0, 0, 0, nullptr};
   if (argmax && p.stream) a.am = *argmax;
   hipStream_t s = (hipStream_t)stream;
@@ -1084,14 +1125,20 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
   if (p.stream) {
     const dim3 sblock(256);
     const int shape = p.rwv * 8 + p.rbw;
-#define ST_LAUNCH_STREAM(RWV_, RBW_, NS128_, NS64_, MINB_)                                    \
+#define ST_LAUNCH_STREAM_P(RWV_, RBW_, NS128_, NS64_, MINB_, PG_)                              \
   if (shape == RWV_ * 8 + RBW_) {                                                              \
     if (D == 128)                                                                              \
-      hipLaunchKernelGGL((attn_stream_kernel<128, NS128_, RWV_, RBW_, MINB_>), grid, sblock, 0, \
-                         s, a);                                                                \
+      hipLaunchKernelGGL((attn_stream_kernel<128, NS128_, RWV_, RBW_, MINB_, PG_>), grid,      \
+                         sblock, 0, s, a);                                                     \
     else                                                                                       \
-      hipLaunchKernelGGL((attn_stream_kernel<64, NS64_, RWV_, RBW_, MINB_>), grid, sblock, 0,   \
-                         s, a);                                                                \
+      hipLaunchKernelGGL((attn_stream_kernel<64, NS64_, RWV_, RBW_, MINB_, PG_>), grid, sblock, \
+                         0, s, a);                                                             \
+  }
+#define ST_LAUNCH_STREAM(RWV_, RBW_, NS128_, NS64_, MINB_)                                    \
+  if (a.pg.bt) {                                                                               \
+    ST_LAUNCH_STREAM_P(RWV_, RBW_, NS128_, NS64_, MINB_, true)                                 \
+  } else {                                                                                     \
+    ST_LAUNCH_STREAM_P(RWV_, RBW_, NS128_, NS64_, MINB_, false)                                \
   }
     ST_LAUNCH_STREAM(1, 1, 2, 4, 1)
     ST_LAUNCH_STREAM(1, 2, 2, 4, 1)
@@ -1100,6 +1147,7 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
     ST_LAUNCH_STREAM(4, 4, 8, 16, 1)
     ST_LAUNCH_STREAM(2, 2, 2, 4, 2)
     ST_LAUNCH_STREAM(4, 2, 4, 8, 2)
+#undef ST_LAUNCH_STREAM_P
 #undef ST_LAUNCH_STREAM
   } else {
     if (D == 128) hipLaunchKernelGGL((attn_valu_kernel<float, 128>), grid, block, 0, s, a);
@@ -1135,6 +1183,25 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
       hipLaunchKernelGGL((attn_combine_compact_kernel<float, 64>), cg, block, 0, s, a, c, n_combine);
   }
   return st::check_launch();
+}
+
+extern "C" int st_tree_attention_paged(const st_tree* tree, int Hq, int Hkv, int D,
+                                       st_dtype dtype, float scale, const void* q,
+                                       const void* k_pool, const void* v_pool, int n_blocks,
+                                       int block_size, const int32_t* block_table,
+                                       int max_blocks, const int32_t* prefix_len,
+                                       int max_prefix, const uint64_t* mask, void* out,
+                                       float* lse, void* workspace, size_t ws_bytes,
+                                       int32_t* status, void* stream) {
+  if (!block_table || n_blocks < 1 || max_blocks < 1) return ST_E_INVALID;
+  if (block_size < 32 || block_size > 4096 || (block_size & (block_size - 1)))
+    return ST_E_UNSUPPORTED;
+  const long cap = (long)max_blocks * block_size;
+  if (cap > (1L << 30)) return ST_E_UNSUPPORTED;
+  const st::KvPaging pg{block_table, max_blocks, __builtin_ctz(block_size), n_blocks};
+  return st::tree_attention_impl(tree, Hq, Hkv, D, dtype, scale, q, k_pool, v_pool, (int)cap,
+                                 prefix_len, max_prefix, mask, out, lse, workspace, ws_bytes,
+                                 status, stream, nullptr, nullptr, &pg);
 }
 
 extern "C" int st_tree_attention(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype,

@@ -36,6 +36,7 @@ int fill_compact_args(int B, int Hkv, int D, st_dtype dtype, void* k_cache, void
   c.src_slot = src_slot;
   c.new_len = new_len;
   c.status = status;
+  c.pg = KvPaging{nullptr, 0, 0, 0};
   c.walk = kWalkNone;
   c.g = GreedyWalkArgs{};
   return ST_OK;
@@ -52,6 +53,27 @@ extern "C" int st_kv_compact(int B, int Hkv, int D, st_dtype dtype, void* k_cach
                                        accept_len, accept_nodes, max_path, src_slot, new_len,
                                        status, c);
   if (rc) return rc;
+  hipLaunchKernelGGL(kv_compact_kernel, dim3(B, 2 * Hkv), dim3(256), 0, (hipStream_t)stream, c);
+  return st::check_launch();
+}
+
+extern "C" int st_kv_compact_paged(int B, int Hkv, int D, st_dtype dtype, void* k_pool,
+                                   void* v_pool, int n_blocks, int block_size,
+                                   const int32_t* block_table, int max_blocks,
+                                   const int32_t* prefix_len, const int32_t* accept_len,
+                                   const int32_t* accept_nodes, int max_path, int32_t* src_slot,
+                                   int32_t* new_len, int32_t* status, void* stream) {
+  if (!block_table || n_blocks < 1 || max_blocks < 1) return ST_E_INVALID;
+  if (block_size < 1 || block_size > 4096 || (block_size & (block_size - 1)))
+    return ST_E_UNSUPPORTED;
+  const long cap = (long)max_blocks * block_size;
+  if (cap > (1L << 30)) return ST_E_UNSUPPORTED;
+  st::CompactArgs c;
+  const int rc = st::fill_compact_args(B, Hkv, D, dtype, k_pool, v_pool, (int)cap, prefix_len,
+                                       accept_len, accept_nodes, max_path, src_slot, new_len,
+                                       status, c);
+  if (rc) return rc;
+  c.pg = st::KvPaging{block_table, max_blocks, __builtin_ctz(block_size), n_blocks};
   hipLaunchKernelGGL(kv_compact_kernel, dim3(B, 2 * Hkv), dim3(256), 0, (hipStream_t)stream, c);
   return st::check_launch();
 }

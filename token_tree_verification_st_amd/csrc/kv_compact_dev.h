@@ -28,12 +28,25 @@ struct CompactArgs {
   int32_t* src_slot;
   int32_t* new_len;
   int32_t* status;
+  KvPaging pg;          // block table of a paged pool (pg.bt null: contiguous caches)
   int walk;             // 0: the path is in accept_len / accept_nodes; 1: run the
   GreedyWalkArgs g;     // greedy walk with these inputs (the argmax partials);
   StochWalkArgs sw;     // 2: the stochastic walk over these node verdicts
 };
 
 enum { kWalkNone = 0, kWalkGreedy = 1, kWalkStochastic = 2 };
+
+// Row `slot` of (request b, kv head) in 16-byte pieces: contiguous, or through
+// the block table (an entry outside the pool is clamped and flagged).
+__device__ inline uint4* kv_row_ptr(const CompactArgs& c, uint4* cache, int b, int head,
+                                    int slot) {
+  if (!c.pg.bt) return cache + (((size_t)b * c.Hkv + head) * c.S_max + slot) * c.chunks;
+  const int e = c.pg.bt[(size_t)b * c.pg.bt_stride + (slot >> c.pg.lbs)];
+  const int phys = min(max(e, 0), c.pg.n_blocks - 1);
+  if (phys != e) st::set_status(c.status, ST_STATUS_BAD_BLOCK);
+  return cache +
+         ((((size_t)phys * c.Hkv + head) << c.pg.lbs) + (slot & ((1 << c.pg.lbs) - 1))) * c.chunks;
+}
 
 // Moves of one workgroup (blockDim.x == 256): request b, cache row set y
 // (< Hkv: keys of head y, else values of head y - Hkv), path[0..L] of the
@@ -58,16 +71,16 @@ __device__ inline void kv_compact_rows(const CompactArgs& c, int b, int y, int L
   }
   if (bad) return;
   const int head = y % c.Hkv;
-  uint4* rows = (y < c.Hkv ? c.kc : c.vc) + ((size_t)b * c.Hkv + head) * (size_t)c.S_max * c.chunks;
+  uint4* cache = y < c.Hkv ? c.kc : c.vc;
   const int per_pass = 256 / c.chunks;
   const int col = threadIdx.x % c.chunks, jr = threadIdx.x / c.chunks;
   for (int j0 = 0; j0 <= L; j0 += per_pass) {
     const int j = j0 + jr;
     const bool move = jr < per_pass && j <= L && path[min(j, L)] != j;
     uint4 v;
-    if (move) v = rows[(size_t)(P + path[j]) * c.chunks + col];
+    if (move) v = kv_row_ptr(c, cache, b, head, P + path[j])[col];
     __syncthreads();
-    if (move) rows[(size_t)(P + j) * c.chunks + col] = v;
+    if (move) kv_row_ptr(c, cache, b, head, P + j)[col] = v;
     __syncthreads();
   }
 }

@@ -22,6 +22,15 @@ inline int check_tree_host(const st_tree* t) {
   return ST_OK;
 }
 
+// KV rows reached through a per-request block table instead of the
+// contiguous [B][Hkv][S_max][D] layout: logical slot k of request b lives in
+// physical block bt[b * bt_stride + (k >> lbs)] of a pool laid out
+// [n_blocks][Hkv][1 << lbs][D].  bt == nullptr: contiguous.
+struct KvPaging {
+  const int32_t* bt;
+  int bt_stride, lbs, n_blocks;
+};
+
 inline int mask_words(int max_nodes) { return (max_nodes + 63) / 64; }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

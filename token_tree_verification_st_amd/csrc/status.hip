@@ -13,6 +13,7 @@ extern "C" const char* st_status_str(int code) {
     case ST_STATUS_NONFINITE: return "non-finite logit";
     case ST_STATUS_PATH_OVERFLOW: return "accepted path longer than max_depth";
     case ST_STATUS_BAD_PREFIX: return "bad prefix length";
+    case ST_STATUS_BAD_BLOCK: return "block-table entry out of range";
     default: return "unknown code";
   }
 }

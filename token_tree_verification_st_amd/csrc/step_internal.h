@@ -52,7 +52,7 @@ int tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dt
                         const int32_t* prefix_len, int max_prefix, const uint64_t* mask,
                         void* out, float* lse, void* workspace, size_t ws_bytes, int32_t* status,
                         void* stream, const CompactArgs* compact,
-                        const ArgmaxJob* argmax = nullptr);
+                        const ArgmaxJob* argmax = nullptr, const KvPaging* paging = nullptr);
 
 // Work items (workgroups with work) of the attention plan for these sizes.
 int attention_workgroups(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype,
