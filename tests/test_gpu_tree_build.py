@@ -131,3 +131,67 @@ def test_host_errors():
         st_tree_build(d(root), d(long), z(2), 10, 8, z(1), z(8), z(8), z(8))
     with pytest.raises(ValueError):         # packed outputs go together
         st_tree_build(d(root), d(seqs), d(lens), 10, 8, z(1), z(8), z(8), z(8), node_off=z(2))
+
+
+def test_built_trees_feed_the_verification_step():
+    """Candidates -> st_tree_build -> one-call verification step (mask,
+    attention, greedy acceptance, compaction), against the oracle; the target
+    is planted to agree with one candidate of each request along its whole
+    length, so the accepted path is that candidate."""
+    from synth import build_workload
+    from token_tree_verification_st_amd import to_device
+    from token_tree_verification_st_amd import step as stp
+
+    B, K, Lmax, V = 4, 6, 5, 500
+    root, seqs, lens = make_candidates(21, B, K, Lmax, V)
+    g = _run(root, seqs, lens, V, 64)
+    assert g["status"] == 0
+    off = g["node_off"]
+    T = int(off[-1])
+    par_p, tok_p = g["parent_packed"][:T], g["tokens_packed"][:T]
+    trees = []
+    for b in range(B):
+        n = int(g["n_nodes"][b])
+        trees.append((g["parent"][b * 64:b * 64 + n].copy(), g["depth"][b * 64:b * 64 + n].copy()))
+    rng = np.random.default_rng(22)
+    wl = build_workload("built", rng, dtype="bf16", Hq=4, Hkv=4, D=128, V=V,
+                        prefix_lens=[37, 300, 129, 64], trees=trees, max_depth=Lmax)
+    assert np.array_equal(wl.node_off, off) and np.array_equal(wl.parent, par_p)
+    wl.tokens = tok_p.astype(np.int32).copy()
+    # plant: after each node on candidate k's path, the target's argmax is the
+    # candidate's next token (the tree holds that child); after its last node,
+    # token 7
+    want = {}
+    for b in range(B):
+        k = int(np.argmax(lens[b]))
+        node, path = 0, [0]
+        lo = int(off[b])
+        for j in range(int(lens[b, k])):
+            kids = [c for c in range(int(g["n_nodes"][b])) if g["parent"][b * 64 + c] == node]
+            node = next(c for c in kids if g["tokens"][b * 64 + c] == seqs[b, k, j])
+            path.append(node)
+        for u, nxt in zip(path, path[1:] + [None]):
+            wl.logits[lo + u, :] = -5.0
+            wl.logits[lo + u, int(seqs[b, k, len(path[:path.index(u)])]) if nxt is not None
+                      else 7] = 5.0
+        want[b] = path
+    dw = to_device(wl)
+    k0 = wl.k_cache.copy()
+    stp.verification_step(dw, stochastic=False)
+    torch.cuda.synchronize()
+    res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, wl.logits, V, wl.max_depth)
+    for key in ("accept_len", "accept_nodes", "out_tokens"):
+        assert np.array_equal(dw.buf[key].cpu().numpy(), res[key]), key
+    for b in range(B):
+        L = int(res["accept_len"][b])
+        assert res["accept_nodes"][b, :L + 1].tolist() == want[b]
+    kn, vn, src, new_len, st = oracle.kv_compact(k0, wl.v_cache, wl.prefix_len,
+                                                 res["accept_len"], res["accept_nodes"],
+                                                 wl.max_depth + 1)
+    assert np.array_equal(dw.k_cache.cpu().view(torch.int16).numpy().view(np.uint16), kn)
+    assert np.array_equal(dw.buf["new_len"].cpu().numpy(), new_len)
+    out = dw.buf["out"].float().cpu().numpy().astype(np.float64)
+    ref, _ = oracle.tree_attention(wl.q, k0, wl.v_cache, wl.dtype, wl.Hq, wl.Hkv, wl.node_off,
+                                   wl.parent, wl.prefix_len)
+    assert np.abs(out - ref).max() <= 1e-2
+    assert int(dw.buf["status"].item()) == 0

@@ -85,6 +85,34 @@ def grid_table(trace_csv: str, prefix: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def attention_calls_table(trace_csv: str) -> str:
+    """The streaming attention kernel's launches split by what follows them on
+    the stream: the split merge (a plain st_tree_attention call) or the
+    merge + compaction launch (the one-call step), with the plain calls'
+    duration from the streaming kernel's start to the merge's end."""
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    plain, step, call = [], [], []
+    for i, r in enumerate(rows[:-1]):
+        if not _short(r["Kernel_Name"]).startswith("attn_stream_kernel"):
+            continue
+        nxt = _short(rows[i + 1]["Kernel_Name"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if nxt.startswith("attn_combine_kernel"):
+            plain.append(dur)
+            call.append((int(rows[i + 1]["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        elif nxt.startswith("attn_combine_compact_kernel"):
+            step.append(dur)
+    out = ["", "attn_stream_kernel by caller (the launch that follows it):", "",
+           "| launches | count | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for name, v in (("st_tree_attention (then the split merge)", plain),
+                    ("verification step (then merge + compaction)", step),
+                    ("st_tree_attention call, stream start to merge end", call)):
+        if v:
+            out.append(f"| {name} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | "
+                       f"{max(v):.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def _per_grid(counter_csv: str, counter: str, prefix: str):
     """Per grid size of the kernels whose short name starts with ``prefix``:
     mean counter value (KiB) and dispatch count."""
@@ -200,6 +228,8 @@ def main(argv):
         text = stats_md(stats_csv, title, command)
         if len(argv) > 6:   # TRACE_CSV KERNEL_PREFIX: add a per-launch-shape table
             text += grid_table(argv[5], argv[6])
+            if argv[6] == "attn_stream_kernel":
+                text += attention_calls_table(argv[5])
         open(out, "w").write(text)
     elif argv[0] == "linear_traffic":
         fcsv, wcsv, copy_bytes, lm_grid, out, cmd_f, cmd_w = argv[1:8]
