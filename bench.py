@@ -559,6 +559,21 @@ def main():
     assert not any(st_words), f"device status {st_words}"
 
     attn_bytes = algorithmic_attention_bytes(wl)
+    # practical ceiling: a plain read-only pass over as many bytes as the
+    # attention's algorithmic traffic, cycled over cold buffers
+    from token_tree_verification_st_amd import st_stream_read
+    nbuf = max(2, math.ceil(REPLICA_BYTES / attn_bytes))
+    bufs = [torch.ones(attn_bytes // 4, dtype=torch.int32, device="cuda") for _ in range(nbuf)]
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    for i in range(3):
+        st_stream_read(bufs[i % nbuf], sink)
+    g_read = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_read):
+        for i in range(K):
+            st_stream_read(bufs[i % nbuf], sink)
+    _, ms = timed_replay(g_read)
+    ceiling_us = ms / K * 1e3
+    del g_read, bufs
     attn_us = per_call["attention"]
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     from token_tree_verification_st_amd.profiling import read_traffic
@@ -602,10 +617,17 @@ def main():
         "per_call_us": {c: round(v, 3) for c, v in per_call.items()},
         "hbm_frac_step": round(attn_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_spread": spread,
+        "stream_ceiling": {"kernel": "st_stream_read (read-only)", "bytes": attn_bytes,
+                           "us": round(ceiling_us, 3),
+                           "gbs": round(attn_bytes / (ceiling_us * 1e-6) / 1e9, 1)},
         "single_step_us_after_flush": round(float(np.median(single)), 3),
         "accepted_tokens_per_step": int((al + 1).sum()),
         "roofline": roof,
     }
+    if stochastic:
+        # comparisons on the taken paths within 1e-6 of the acceptance bound (and
+        # replacement draws within 1e-6 of a bin edge), summed over requests
+        line["near_ties_per_step"] = int(reps[0].buf["near_ties"].sum().item())
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, stochastic)
     print(json.dumps(line), flush=True)

@@ -395,6 +395,13 @@ size_t st_linear_workspace(int M, int N, int K);
 int st_linear(int M, int N, int K, const void* x, const void* w, const void* residual, void* y,
               st_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
 
+/* Measurement helper (not part of the method): one plain read-only pass over
+ * `bytes` of device memory at `src` (16-byte aligned, a multiple of 16), the
+ * practical HBM read ceiling the kernels above are compared with.  `sink`
+ * [sink_len] uint32 is written only on a data pattern that practically never
+ * occurs; at most sink_len workgroups are launched. */
+int st_stream_read(const void* src, size_t bytes, uint32_t* sink, int sink_len, void* stream);
+
 /* Text for a return code or for a status bit (host memory, static). */
 const char* st_status_str(int code);
 

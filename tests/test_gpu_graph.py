@@ -48,3 +48,21 @@ def test_graph_replays_equal_eager(name, stochastic):
         _ = (dw.buf["out"].float() * 2).sum().item()   # unrelated eager kernels
     assert int(dw.buf["status"].item()) == 0
     say(f"{name}: 4 graph replays equal the eager step")
+
+
+def test_stream_read_helper():
+    """The read-ceiling helper runs over any 16-byte multiple, leaves its sink
+    alone on ordinary data, and refuses a size that is not a multiple of 16."""
+    import ctypes
+    from token_tree_verification_st_amd import load_library, st_stream_read
+    require_gpu()
+    for n in (4, 1000, 1 << 22, (1 << 24) + 12):
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+        st_stream_read(src, sink)
+        torch.cuda.synchronize()
+        assert int(sink.abs().sum().item()) == 0
+    src = torch.ones(10, dtype=torch.int32, device="cuda")
+    rc = load_library().st_stream_read(ctypes.c_void_p(src.data_ptr()), 40, ctypes.c_void_p(
+        sink.data_ptr()), 64, None)
+    assert rc == -1

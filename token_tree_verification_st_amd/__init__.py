@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     st_linear_workspace,
     st_mask_words,
     st_status_str,
+    st_stream_read,
     st_tree_attention,
     st_tree_attention_paged,
     st_tree_attention_workspace,

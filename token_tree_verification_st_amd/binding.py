@@ -87,6 +87,7 @@ def _declare(lib):
         "st_tree_attention_paged": (I, [TP, I, I, I, I, _c.c_float, P, P, P, I, I, P, I, P, I, P,
                                         P, P, P, S, P, P]),
         "st_kv_compact_paged": (I, [I, I, I, I, P, P, I, I, P, I, P, P, P, I, P, P, P, P]),
+        "st_stream_read": (I, [P, S, P, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -342,6 +343,16 @@ def st_tree_build(root_tokens, seqs, lens, V: int, cap: int, n_nodes, parent, to
         B, K, Lmax, int(V), int(cap), _ptr(root_tokens), _ptr(seqs), _ptr(lens), _ptr(n_nodes),
         _ptr(parent), _ptr(tokens), _ptr(depth), _ptr(node_off), _ptr(parent_packed),
         _ptr(tokens_packed), _ptr(status), _stream()), "st_tree_build")
+
+
+def st_stream_read(src: torch.Tensor, sink: torch.Tensor):
+    """One read-only pass over src (the practical HBM read ceiling); sink is an
+    int32 scratch tensor (its length bounds the launch width)."""
+    _dev(src, "src")
+    _dev(sink, "sink", torch.int32)
+    nbytes = src.numel() * src.element_size()
+    _check(load_library().st_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink),
+                                         sink.numel(), _stream()), "st_stream_read")
 
 
 def candidate_length(t: int, T_est: int, K_max: int) -> int:
