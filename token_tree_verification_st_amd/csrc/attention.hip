@@ -775,6 +775,24 @@ attn_valu_kernel(AttnArgs a) {
   const int hq = it.g * a.G + (row_ok ? row % a.G : 0);
   const int grow = (rq.lo + node) * a.Hq + hq;
 
+  // the first K/V tile's loads go out before Q and the masks are read
+  static_assert(sizeof(Tin) == 4, "the VALU kernel serves fp32 inputs");
+  constexpr int V4 = D / 4, LPT = KT * V4 / 256;  // 16-byte loads per thread and tile
+  f32x4 rk[LPT], rv[LPT];
+  auto load_tile = [&](int kt) {
+    const int nk = min(KT, k1 - kt);
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int e = tid + 256 * j, kr = e / V4, d4 = 4 * (e % V4);
+      const bool ok = kr < nk;
+      rk[j] = ok ? *(const f32x4*)(kv_row<Tin>(a, a.k, it.b, it.g, kt + kr, D) + d4)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+      rv[j] = ok ? *(const f32x4*)(kv_row<Tin>(a, a.v, it.b, it.g, kt + kr, D) + d4)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_tile(k0);
+
   const Tin* qp = (const Tin*)a.q + (size_t)grow * D;
   for (int d = c; d < D; d += 16) sQ[r][d] = row_ok ? load_val(qp + d) : 0.f;
   uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
@@ -813,16 +831,18 @@ attn_valu_kernel(AttnArgs a) {
   float m = -INFINITY, lsum = 0.f;
 
   for (int kt = k0; kt < k1; kt += KT) {
-    const int nk = min(KT, k1 - kt);
-    __syncthreads();
-#pragma unroll 4
-    for (int e = tid; e < KT * D; e += 256) {
-      const int kr = e / D, d = e % D;
-      const bool ok = kr < nk;
-      sK[kr][d] = ok ? load_val(kv_row<Tin>(a, a.k, it.b, it.g, kt + kr, D) + d) : 0.f;
-      sV[kr][d] = ok ? load_val(kv_row<Tin>(a, a.v, it.b, it.g, kt + kr, D) + d) : 0.f;
+    __syncthreads();  // the previous tile's readers are done
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int e = tid + 256 * j, kr = e / V4, d4 = 4 * (e % V4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sK[kr][d4 + q] = rk[j][q];
+        sV[kr][d4 + q] = rv[j][q];
+      }
     }
     __syncthreads();
+    if (kt + KT < k1) load_tile(kt + KT);  // in flight while this tile is computed
     float dot[KJ];
 #pragma unroll
     for (int j = 0; j < KJ; ++j) dot[j] = 0.f;
@@ -1042,7 +1062,9 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
   const int forced_ks = env_int("ST_ATTN_SPLIT_KEYS", 0);
   if (forced_ks > 0) ks = (forced_ks + gran - 1) / gran * gran;
   const long kmax = (keys_max + gran - 1) / gran * gran;
-  if (ks < 64) ks = 64;
+  // the streaming kernel wants at least two chunks per wavefront; the fp32
+  // kernel, whose tiles are not prefetched, is fastest with one tile a split
+  if (ks < (p.stream ? 64 : gran)) ks = p.stream ? 64 : gran;
   if (ks > kmax) ks = kmax;
   p.KS = (int)ks;
   p.NS = (int)((keys_max + ks - 1) / ks);
