@@ -61,6 +61,23 @@ def test_greedy_random_planted_trees(seed):
     _assert_paths_equal(res, gpu)
 
 
+@pytest.mark.parametrize("V", [20000, 20001, 8193])
+def test_greedy_large_batches(V):
+    """A large batch (more than eight argmax slices per CU) with an odd slice
+    count, and a vocab that is not a multiple of 4 (scalar loads)."""
+    say(f"greedy large batch V={V}")
+    rng = np.random.default_rng(V)
+    trees = [tree_random_attach(rng, 150, 6) for _ in range(8)]
+    wl = build_workload("gl", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=V,
+                        prefix_lens=[16] * 8, trees=trees, max_depth=6,
+                        token_rule="plant_leaf_path")
+    assert wl.T * ((V + 8191) // 8192) > 8 * 256
+    res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.V, wl.max_depth)
+    dw, gpu = _greedy_gpu(wl)
+    _assert_paths_equal(res, gpu)
+    assert status_of(dw) == 0 and res["accept_len"].max() > 0
+
+
 def test_greedy_status_bits():
     rng = np.random.default_rng(7)
     wl = build_workload("s", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=50, prefix_lens=[1, 1],
