@@ -346,6 +346,20 @@ int st_tree_build(int B, int K, int Lmax, int V, int cap, const int32_t* root_to
                   int32_t* tokens, int32_t* depth, int32_t* node_off, int32_t* parent_packed,
                   int32_t* tokens_packed, int32_t* status, void* stream);
 
+/*
+ * st_verification_step_paged -- st_verification_step over a paged KV pool:
+ * step->k_cache / step->v_cache are pools [n_blocks][Hkv][block_size][D]
+ * addressed through block_table [B][max_blocks] as for
+ * st_tree_attention_paged (block_size a power of two from 32 to 4096);
+ * step->S_max is ignored (the logical capacity is max_blocks * block_size).
+ * Attention reads and compaction moves logical slots through the table; the
+ * workspace size is st_verification_step_workspace's.  Outputs equal those of
+ * st_verification_step on the contiguous caches the table describes.
+ */
+int st_verification_step_paged(const st_tree* tree, const st_step* step, int n_blocks,
+                               int block_size, const int32_t* block_table, int max_blocks,
+                               void* workspace, size_t ws_bytes, int32_t* status, void* stream);
+
 /* ---------------------------------------------------------------------------
  * The target layer around verification.  The pages fix no architecture; the
  * calls below are the pieces one attention layer needs to run over a token

@@ -137,3 +137,47 @@ def test_paged_compaction_bit_exact(bs, dtype):
     assert int(status.item()) == st_r == 8
     assert np.array_equal(_host(kp), k2) and np.array_equal(_host(vp), v2)
     assert np.array_equal(src.cpu().numpy(), src_r) and np.array_equal(nl.cpu().numpy(), nl_r)
+
+
+@pytest.mark.parametrize("name,bs,stochastic", [("tiny_fp32", 32, False), ("llama7b", 64, False),
+                                                ("ragged_batch", 128, False),
+                                                ("stochastic_tree", 32, True)])
+def test_paged_step_equals_contiguous_step(name, bs, stochastic):
+    """The one-call step over a paged pool gives the contiguous step's outputs
+    bit for bit, and its pools hold what the contiguous caches hold."""
+    from token_tree_verification_st_amd import st_verification_step_paged
+    say(f"paged step {name} block {bs}")
+    wl = make_workload(name, 0)
+    dw = to_device(wl)
+    kp_h, vp_h, bt_h = make_paged(13, wl.k_cache, wl.v_cache, bs)
+    stp.verification_step(dw, stochastic=stochastic)
+    torch.cuda.synchronize()
+    ref = {k: dw.buf[k].clone() for k in ("out", "lse", "accept_len", "accept_nodes",
+                                          "out_tokens", "src_slot", "new_len", "near_ties")}
+    kc, vc = _host(dw.k_cache), _host(dw.v_cache)
+    dw2 = to_device(wl)
+    b = dw2.buf
+    kp, vp, bt = _dev(kp_h), _dev(vp_h), _dev(bt_h)
+    st_verification_step_paged(dw2.tree, dw2.q, kp, vp, bt, dw2.prefix_len, dw2.max_prefix,
+                               b["out"], b["lse"], dw2.tokens, dw2.logits, b["accept_len"],
+                               b["accept_nodes"], b["out_tokens"], b["src_slot"], b["new_len"],
+                               b["step_ws"], draft_logits=dw2.draft_logits if stochastic else None,
+                               temperature=dw2.temperature, seed=dw2.rng_seed,
+                               offset=dw2.rng_offset,
+                               near_ties=b["near_ties"] if stochastic else None,
+                               status=b["status"])
+    torch.cuda.synchronize()
+    assert int(b["status"].item()) == 0
+    for k, v in ref.items():
+        got = b[k]
+        if got.dtype == torch.bfloat16:
+            assert torch.equal(got.view(torch.int16), v.view(torch.int16)), k
+        else:
+            assert torch.equal(got, v), k
+    S = wl.S_max
+    assert np.array_equal(oracle.gather_paged(_host(kp), bt_h, bs)[:, :, :S], kc)
+    assert np.array_equal(oracle.gather_paged(_host(vp), bt_h, bs)[:, :, :S], vc)
+    # blocks the table does not name are untouched
+    spares = sorted(set(range(kp_h.shape[0])) - set(bt_h.ravel().tolist()))
+    kph = _host(kp)
+    assert all(np.array_equal(kph[s], kp_h[s]) for s in spares)

@@ -88,6 +88,7 @@ def _declare(lib):
                                         P, P, P, S, P, P]),
         "st_kv_compact_paged": (I, [I, I, I, I, P, P, I, I, P, I, P, P, P, I, P, P, P, P]),
         "st_stream_read": (I, [P, S, P, I, P]),
+        "st_verification_step_paged": (I, [TP, _c.POINTER(StStep), I, I, P, I, P, S, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -408,9 +409,14 @@ def st_kv_compact(k_cache, v_cache, prefix_len, accept_len, accept_nodes, src_sl
 def _step_struct(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix: int, out, lse,
                  tokens, logits, draft_logits, temperature: float, seed: int, offset: int,
                  accept_len, accept_nodes, out_tokens, near_ties, src_slot, new_len,
-                 scale: Optional[float]) -> StStep:
+                 scale: Optional[float], block_table=None) -> StStep:
     T, Hq, D = q.shape
-    B, Hkv, S_max, D2 = k_cache.shape
+    if block_table is None:
+        B, Hkv, S_max, D2 = k_cache.shape
+    else:                        # paged pools [n_blocks][Hkv][block][D]
+        _, Hkv, bs, D2 = k_cache.shape
+        B, max_blocks = block_table.shape
+        S_max = max_blocks * bs
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or T != tree.T or B != tree.B:
         raise ValueError("shape mismatch between q, caches and tree")
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
@@ -463,6 +469,32 @@ def st_verification_step(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix
     _check(load_library().st_verification_step(
         tree.ref, ctypes.byref(step), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(status), _stream()), "st_verification_step")
+
+
+def st_verification_step_paged(tree: Tree, q, k_pool, v_pool, block_table, prefix_len,
+                               max_prefix: int, out, lse, tokens, logits, accept_len,
+                               accept_nodes, out_tokens, src_slot, new_len, workspace,
+                               draft_logits=None, temperature: float = 1.0, seed: int = 0,
+                               offset: int = 0, near_ties=None, scale: Optional[float] = None,
+                               status=None):
+    """st_verification_step over paged pools [n_blocks][Hkv][block][D] through
+    block_table int32 [B][max_blocks]; the pools are compacted in place."""
+    _dev(block_table, "block_table", torch.int32)
+    if tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("v_pool must match k_pool")
+    step = _step_struct(tree, q, k_pool, v_pool, prefix_len, max_prefix, out, lse, tokens,
+                        logits, draft_logits, temperature, seed, offset, accept_len, accept_nodes,
+                        out_tokens, near_ties, src_slot, new_len, scale, block_table=block_table)
+    need = st_verification_step_workspace(tree, step)
+    if need == 0:
+        raise ValueError("st_verification_step_paged: invalid arguments")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    n_blocks, _, bs, _ = k_pool.shape
+    _check(load_library().st_verification_step_paged(
+        tree.ref, ctypes.byref(step), n_blocks, bs, _ptr(block_table), block_table.shape[1],
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(status), _stream()),
+        "st_verification_step_paged")
 
 
 def st_embed(tokens, table, out, status=None):

@@ -31,8 +31,12 @@ extern "C" size_t st_verification_step_workspace(const st_tree* tree, const st_s
   return st::align_up(verify_ws(tree, s), 256) + a;
 }
 
-extern "C" int st_verification_step(const st_tree* tree, const st_step* s, void* workspace,
-                                    size_t ws_bytes, int32_t* status, void* stream) {
+namespace {
+
+// The step over contiguous caches (pg null) or a paged pool (pg: the block
+// table; s->S_max is then the logical capacity).
+int step_impl(const st_tree* tree, const st_step* s, void* workspace, size_t ws_bytes,
+              int32_t* status, void* stream, const st::KvPaging* pg) {
   int rc = st::check_tree_host(tree);
   if (rc) return rc;
   if (!step_fields_ok(s)) return ST_E_INVALID;
@@ -52,6 +56,7 @@ extern "C" int st_verification_step(const st_tree* tree, const st_step* s, void*
                              s->prefix_len, s->accept_len, s->accept_nodes, max_path,
                              s->src_slot, s->new_len, status, c);
   if (rc) return rc;
+  if (pg) c.pg = *pg;
 
   // Each compaction workgroup of the last launch walks its request's tree
   // itself (a few microseconds of latency-bound work that then needs no
@@ -87,5 +92,27 @@ extern "C" int st_verification_step(const st_tree* tree, const st_step* s, void*
   return st::tree_attention_impl(tree, s->Hq, s->Hkv, s->D, s->dtype, s->scale, s->q,
                                  s->k_cache, s->v_cache, s->S_max, s->prefix_len, s->max_prefix,
                                  nullptr, s->out, s->lse, (char*)workspace + off, aws, status,
-                                 stream, &c, fuse_argmax ? &job : nullptr);
+                                 stream, &c, fuse_argmax ? &job : nullptr, pg);
+}
+
+}  // namespace
+
+extern "C" int st_verification_step(const st_tree* tree, const st_step* s, void* workspace,
+                                    size_t ws_bytes, int32_t* status, void* stream) {
+  return step_impl(tree, s, workspace, ws_bytes, status, stream, nullptr);
+}
+
+extern "C" int st_verification_step_paged(const st_tree* tree, const st_step* s, int n_blocks,
+                                          int block_size, const int32_t* block_table,
+                                          int max_blocks, void* workspace, size_t ws_bytes,
+                                          int32_t* status, void* stream) {
+  if (!s || !block_table || n_blocks < 1 || max_blocks < 1) return ST_E_INVALID;
+  if (block_size < 32 || block_size > 4096 || (block_size & (block_size - 1)))
+    return ST_E_UNSUPPORTED;
+  const long cap = (long)max_blocks * block_size;
+  if (cap > (1L << 30)) return ST_E_UNSUPPORTED;
+  st_step sp = *s;
+  sp.S_max = (int32_t)cap;
+  const st::KvPaging pg{block_table, max_blocks, __builtin_ctz(block_size), n_blocks};
+  return step_impl(tree, &sp, workspace, ws_bytes, status, stream, &pg);
 }
