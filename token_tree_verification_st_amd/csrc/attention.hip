@@ -66,12 +66,9 @@ struct AttnArgs {
   st::KvPaging pg; // pg.bt null: contiguous caches
 };
 
-// First element of key row `key` of (request b, kv head g): contiguous
-// [B][Hkv][S_max][D], or through the block table into a paged pool
-// [n_blocks][Hkv][block][D] (an entry outside [0, n_blocks) is clamped and
-// flagged, so every address stays inside the pool).  Chunks start at
-// multiples of 32 keys and blocks hold a multiple of 32, so the rows of one
-// chunk never leave its block.
+// The physical block of key `key` of request b in a paged pool: its block-
+// table entry, clamped into [0, n_blocks) and flagged when it was outside, so
+// every address stays inside the pool.
 __device__ inline int table_entry(const AttnArgs& a, int b, int key) {
   const int e = a.pg.bt[(size_t)b * a.pg.bt_stride + (key >> a.pg.lbs)];
   const int phys = min(max(e, 0), a.pg.n_blocks - 1);
@@ -86,6 +83,10 @@ __device__ inline const T* kv_block_row(const AttnArgs& a, const void* cache, in
          ((((size_t)phys * a.Hkv + g) << a.pg.lbs) + (key & ((1 << a.pg.lbs) - 1))) * D;
 }
 
+// First element of key row `key` of (request b, kv head g): contiguous
+// [B][Hkv][S_max][D], or through the block table into a paged pool
+// [n_blocks][Hkv][block][D].  Chunks start at multiples of 32 keys and blocks
+// hold a multiple of 32, so the rows of one chunk never leave its block.
 template <typename T>
 __device__ inline const T* kv_row(const AttnArgs& a, const void* cache, int b, int g, int key,
                                   int D) {
@@ -282,12 +283,31 @@ __device__ __forceinline__ void wait_chunks(int n) {
 // This wavefront's share (row group rw of RWV) of the direct loads of one
 // 32-key chunk starting at key kt; key rows past klast are clamped to it.  The
 // chunk base is wave-uniform, each lane adds a 32-bit offset.
+// Byte offsets of this lane's direct loads within a whole chunk (swizzled
+// 16-byte pieces of its key rows), the same for every chunk: computed once,
+// so a whole chunk's loads take a uniform base plus a fixed 32-bit offset and
+// need no vector arithmetic.
+template <int D, int RWV>
+struct ChunkOff {
+  static constexpr int CH = D / 8, RPI = 64 / CH, INST = kCK / RPI, PER = INST / RWV;
+  uint32_t k[PER], v[PER];
+  __device__ ChunkOff(int rw, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int inst = rw * PER + i;
+      const int row = inst * RPI + lane / CH, pos = lane % CH;
+      k[i] = 2u * (uint32_t)(row * D + 8 * (pos ^ kswz<D>(row)));
+      v[i] = 2u * (uint32_t)(row * D + 8 * (pos ^ vswz<D>(row)));
+    }
+  }
+};
+
 // (PAGED: `phys` is the block that holds the chunk, looked up beforehand.)
 template <int D, int RWV, bool PAGED>
 __device__ __forceinline__ void chunk_dma(uint16_t* sK, uint16_t* sV, const AttnArgs& a,
                                           const Item& it, const uint16_t* kgp,
                                           const uint16_t* vgp, int kt, int klast, int rw,
-                                          int lane, int phys = 0) {
+                                          int lane, const ChunkOff<D, RWV>& off, int phys = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass never runs this body
   constexpr int CH = D / 8, RPI = 64 / CH, INST = kCK / RPI, PER = INST / RWV;
   const uint16_t* kb =
@@ -295,6 +315,17 @@ __device__ __forceinline__ void chunk_dma(uint16_t* sK, uint16_t* sV, const Attn
   const uint16_t* vb =
       PAGED ? kv_block_row<uint16_t>(a, a.v, phys, it.g, kt, D) : vgp + (size_t)kt * D;
   const int lim = klast - kt;
+  if (lim >= kCK - 1) {  // a whole chunk: no row is clamped
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int inst = rw * PER + i;
+      __builtin_amdgcn_global_load_lds((const char*)kb + off.k[i], ST_LDS_PTR(sK + inst * 512),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const char*)vb + off.v[i], ST_LDS_PTR(sV + inst * 512),
+                                       16, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int inst = rw * PER + i;
@@ -505,9 +536,10 @@ attn_stream_kernel(AttnArgs a) {
   // the first chunk goes first, then Q and the masks, then the rest of the ring
   // paged pool: the block of each chunk is looked up one refill ahead
   auto entry = [&](int c) { return PAGED ? table_entry(a, it.b, k0 + c * kCK) : 0; };
+  const ChunkOff<D, RWV> coff(rw, lane);
   if (nmine > 0)
     chunk_dma<D, RWV, PAGED>(ring, ring + kCK * D, a, it, kgp, vgp, k0 + kg * kCK, klast, rw,
-                             lane, entry(kg));
+                             lane, coff, entry(kg));
 
   // Q of the workgroup's rows (rows past the end repeat the last): staged in
   // LDS once when several key groups share the rows, else loaded directly.
@@ -561,7 +593,8 @@ attn_stream_kernel(AttnArgs a) {
   for (int s = 1; s < PRIME; ++s)
     if (s < nmine)
       chunk_dma<D, RWV, PAGED>(ring + s * STAGE, ring + s * STAGE + kCK * D, a, it, kgp, vgp,
-                               k0 + (s * KWV + kg) * kCK, klast, rw, lane, entry(s * KWV + kg));
+                               k0 + (s * KWV + kg) * kCK, klast, rw, lane, coff,
+                               entry(s * KWV + kg));
   wait_chunks<PRIME - 1, DPC>(want - 1);  // the first chunk, Q and the masks are older
   if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
   if (need_mask) {
@@ -623,7 +656,8 @@ attn_stream_kernel(AttnArgs a) {
       if (r + NSTAGE < nmine) {
         uint16_t* sb = ring + stage * STAGE;
         chunk_dma<D, RWV, PAGED>(sb, sb + kCK * D, a, it, kgp, vgp,
-                                 k0 + ((r + NSTAGE) * KWV + kg) * kCK, klast, rw, lane, next);
+                                 k0 + ((r + NSTAGE) * KWV + kg) * kCK, klast, rw, lane, coff,
+                                 next);
         if (PAGED && r + NSTAGE + 1 < nmine) next = entry((r + NSTAGE + 1) * KWV + kg);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -643,7 +677,7 @@ attn_stream_kernel(AttnArgs a) {
         uint16_t* sb = ring + refill * STAGE;
         chunk_dma<D, RWV, PAGED>(sb, sb + kCK * D, a, it, kgp, vgp,
                                  k0 + ((r + NSTAGE - 1) * KWV + kg) * kCK, klast, rw, lane,
-                                 next);
+                                 coff, next);
         if (PAGED && r + NSTAGE < nmine) next = entry((r + NSTAGE) * KWV + kg);
       }
       __builtin_amdgcn_sched_barrier(0);
