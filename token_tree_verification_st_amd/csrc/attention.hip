@@ -946,11 +946,10 @@ attn_valu_kernel(AttnArgs a) {
 // Merge the splits of every row: the partial (m, l) pairs and 4 dims of the
 // partial outputs of up to 8 splits are all loaded before any is used.  Block
 // `blk` covers 256 / (D/4) consecutive rows.
-template <typename Tout, int D>
-__device__ inline void combine_block(const AttnArgs& a, int blk) {
+template <typename Tout, int D, int CHUNK>
+__device__ inline void combine_block_n(const AttnArgs& a, int blk) {
   constexpr int LPR = D / 4;        // lanes per row, 4 dims each
   constexpr int RPB = 256 / LPR;    // rows per block
-  constexpr int CHUNK = 8;
   const int grow = blk * RPB + threadIdx.x / LPR;
   const int d = 4 * (threadIdx.x % LPR);
   const int TH = a.T * a.Hq;
@@ -1005,6 +1004,13 @@ __device__ inline void combine_block(const AttnArgs& a, int blk) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) store_val(op + j, o[j] * inv);
   if (a.lse && d == 0) a.lse[grow] = (M + log2f(L)) * kLn2;
+}
+
+// Splits loaded before the first use: as many as a request can have, up to 8.
+template <typename Tout, int D>
+__device__ inline void combine_block(const AttnArgs& a, int blk) {
+  if (a.NS <= 4) combine_block_n<Tout, D, 4>(a, blk);
+  else combine_block_n<Tout, D, 8>(a, blk);
 }
 
 template <typename Tout, int D>
