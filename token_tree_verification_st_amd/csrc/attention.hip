@@ -1001,8 +1001,17 @@ __device__ inline void combine_block_n(const AttnArgs& a, int blk) {
   }
   const float inv = 1.f / L;
   Tout* op = (Tout*)a.out + (size_t)grow * D + d;
+  if constexpr (sizeof(Tout) == 2) {  // bf16: the lane's four dims in one 8-byte store
+    uint2 w;
+    w.x = (uint32_t)st::f32_to_bf16_rne(o[0] * inv) |
+          ((uint32_t)st::f32_to_bf16_rne(o[1] * inv) << 16);
+    w.y = (uint32_t)st::f32_to_bf16_rne(o[2] * inv) |
+          ((uint32_t)st::f32_to_bf16_rne(o[3] * inv) << 16);
+    *(uint2*)op = w;
+  } else {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) store_val(op + j, o[j] * inv);
+    for (int j = 0; j < 4; ++j) store_val(op + j, o[j] * inv);
+  }
   if (a.lse && d == 0) a.lse[grow] = (M + log2f(L)) * kLn2;
 }
 
