@@ -26,7 +26,8 @@ Sources (web pages, cited by title and section):
                     equal-distribution guarantee), §3.2 (single forward pass)
 
 Token-tree construction (build.py) merges candidate sequences into the tree
-that verification takes.
+that verification takes; paged.py describes a paged KV pool by the contiguous
+caches its block table names.
 
 Every function is pinned by tests marked ``not gpu`` (closed forms, brute
 force, invariants, library routines, hand-worked fixtures in tests/golden).
