@@ -181,3 +181,32 @@ def test_paged_step_equals_contiguous_step(name, bs, stochastic):
     spares = sorted(set(range(kp_h.shape[0])) - set(bt_h.ravel().tolist()))
     kph = _host(kp)
     assert all(np.array_equal(kph[s], kp_h[s]) for s in spares)
+
+
+@pytest.mark.parametrize("dtype,bs", [("bf16", 32), ("bf16", 64), ("f32", 32)])
+def test_paged_block_boundaries(dtype, bs):
+    """Prefixes at and around block boundaries (0, 1, bs-1, bs, bs+1, 2bs) and
+    trees that straddle them: paged equals contiguous bit for bit."""
+    say(f"paged block boundaries {dtype} block {bs}")
+    rng = np.random.default_rng(bs + (dtype == "f32"))
+    prefixes = [0, 1, bs - 1, bs, bs + 1, 2 * bs]
+    trees = [tree_random_attach(rng, int(rng.integers(1, 50)), 6) for _ in prefixes]
+    D = 128 if dtype == "bf16" else 64
+    wl = build_workload("pb", rng, dtype=dtype, Hq=4, Hkv=2, D=D, V=0, prefix_lens=prefixes,
+                        trees=trees, max_depth=6)
+    dw = to_device(wl)
+    stp.run_mask(dw)
+    stp.run_attention(dw)
+    torch.cuda.synchronize()
+    kp_h, vp_h, bt_h = make_paged(17, wl.k_cache, wl.v_cache, bs)
+    out, lse, st = _paged_attention(dw, _dev(kp_h), _dev(vp_h), _dev(bt_h))
+    assert st == 0
+    if out.dtype == torch.bfloat16:
+        assert torch.equal(out.view(torch.int16), dw.buf["out"].view(torch.int16))
+    else:
+        assert torch.equal(out, dw.buf["out"])
+    assert torch.equal(lse, dw.buf["lse"])
+    ref, _ = oracle.tree_attention(wl.q, wl.k_cache, wl.v_cache, wl.dtype, wl.Hq, wl.Hkv,
+                                   wl.node_off, wl.parent, wl.prefix_len)
+    err = float(np.abs(out.float().cpu().numpy().astype(np.float64) - ref).max())
+    assert err <= (F32_TOL if dtype == "f32" else BF16_TOL)
