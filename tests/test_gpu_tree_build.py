@@ -195,3 +195,28 @@ def test_built_trees_feed_the_verification_step():
                                    wl.parent, wl.prefix_len)
     assert np.abs(out - ref).max() <= 1e-2
     assert int(dw.buf["status"].item()) == 0
+
+
+@pytest.mark.parametrize("K", [63, 64, 65, 128])
+def test_kernel_width_boundary(K):
+    """Around the switch from one wavefront (K <= 64) to 256 threads."""
+    root, seqs, lens = make_candidates(30 + K, 3, K, 6, 7)
+    _compare(root, seqs, lens, 7, 256)
+
+
+def test_degenerate_candidate_sets():
+    """Identical candidates (one chain), candidates differing in their first
+    token only (a star of chains), and no candidate tokens at all (the root
+    alone)."""
+    B, K, L = 3, 8, 5
+    seqs = np.zeros((B, K, L), np.int32)
+    lens = np.full((B, K), L, np.int32)
+    seqs[0] = np.arange(L)                                    # all the same
+    for k in range(K):
+        seqs[1, k] = [k] + [9] * (L - 1)                      # first tokens differ
+    lens[2] = 0                                               # nothing to merge
+    root = np.array([1, 2, 3], np.int32)
+    g, r = _compare(root, seqs, lens, 10, 64)
+    assert g["n_nodes"].tolist() == [1 + L, 1 + K * L, 1]
+    assert g["parent"][:1 + L].tolist() == [-1] + list(range(L))
+    assert g["status"] == 0
