@@ -447,11 +447,9 @@ def main():
            "compact": stp.run_compact}
 
     def one_step(d):
-        if ext:   # the options exist on the separate entry points only
-            stp.run_mask(d)
-            stp.run_attention(d)
-            verify(d)
-            stp.run_compact(d)
+        if ext:
+            stp.verification_step(d, stochastic=True, top_p=args.top_p,
+                                  draft=d.buf.get("draft_probs"))
         else:
             stp.verification_step(d, stochastic=stochastic)
 

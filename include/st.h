@@ -347,6 +347,18 @@ int st_tree_build(int B, int K, int Lmax, int V, int cap, const int32_t* root_to
                   int32_t* tokens_packed, int32_t* status, void* stream);
 
 /*
+ * st_verification_step_ex -- st_verification_step with the sampling options of
+ * st_verify_stochastic_ex: nucleus filtering (top_p in (0, 1]) and the draft
+ * given as probabilities (draft_is_probs 1: step->draft_logits holds
+ * probabilities).  Both need stochastic acceptance (step->draft_logits set);
+ * ST_E_INVALID otherwise or for values out of range.  top_p = 1 and
+ * draft_is_probs = 0 give st_verification_step.  Same workspace size.
+ */
+int st_verification_step_ex(const st_tree* tree, const st_step* step, int draft_is_probs,
+                            float top_p, void* workspace, size_t ws_bytes, int32_t* status,
+                            void* stream);
+
+/*
  * st_verification_step_paged -- st_verification_step over a paged KV pool:
  * step->k_cache / step->v_cache are pools [n_blocks][Hkv][block_size][D]
  * addressed through block_table [B][max_blocks] as for

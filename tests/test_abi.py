@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     for n in ("st_tree_mask", "st_tree_attention", "st_verify_greedy", "st_verify_stochastic",
               "st_kv_compact", "st_status_str", "st_embed", "st_tree_rope_append", "st_linear",
               "st_linear_workspace", "st_verify_stochastic_ex", "st_tree_build",
-              "st_tree_attention_paged", "st_kv_compact_paged", "st_verification_step_paged"):
+              "st_tree_attention_paged", "st_kv_compact_paged", "st_verification_step_paged",
+              "st_verification_step_ex"):
         assert n in names
 
 

@@ -111,3 +111,48 @@ def test_rejects_bad_arguments_and_flags_negative_probabilities():
     stp.run_verify(dw, stochastic=True, top_p=0.9, draft=torch.from_numpy(bad).cuda())
     torch.cuda.synchronize()
     assert status_of(dw) & 4
+
+
+@pytest.mark.parametrize("name", ["stochastic_tree", "stochastic_chain"])
+@pytest.mark.parametrize("top_p,probs", [(0.9, False), (1.0, True), (0.6, True)])
+def test_one_call_step_ex_equals_separate_calls(name, top_p, probs):
+    """st_verification_step_ex gives what mask -> attention ->
+    st_verify_stochastic_ex -> compaction give, bit for bit, and its
+    acceptance follows the oracle up to near ties."""
+    wl = make_workload(name, 0)
+    a, b = to_device(wl), to_device(wl)
+    draft = torch.from_numpy(_probs(wl)).cuda() if probs else None
+    stp.verification_step(a, stochastic=True, fused=False, top_p=top_p, draft=draft)
+    stp.verification_step(b, stochastic=True, fused=True, top_p=top_p, draft=draft)
+    torch.cuda.synchronize()
+    for k in ("accept_len", "accept_nodes", "out_tokens", "near_ties", "src_slot", "new_len",
+              "status"):
+        assert torch.equal(a.buf[k], b.buf[k]), k
+    assert torch.equal(a.buf["out"], b.buf["out"]) and torch.equal(a.buf["lse"], b.buf["lse"])
+    assert torch.equal(a.k_cache, b.k_cache) and torch.equal(a.v_cache, b.v_cache)
+    # the separate path's acceptance against the oracle (fresh copies of the
+    # workload: the step compacted a's caches, which acceptance does not read)
+    _check(wl, top_p, probs)
+    say(f"{name} top_p={top_p} probs={probs}: one-call step ex equals separate calls, "
+        f"accept_len {b.buf['accept_len'].tolist()[:4]}")
+
+
+def test_one_call_step_ex_plain_options_and_bad_arguments():
+    from token_tree_verification_st_amd import st_verification_step_ex
+    wl = make_workload("stochastic_tree", 2)
+    a, b = to_device(wl), to_device(wl)
+    stp.run_step(a, stochastic=True)
+    bb = b.buf
+    args = (b.tree, b.q, b.k_cache, b.v_cache, b.prefix_len, b.max_prefix, bb["out"], bb["lse"],
+            b.tokens, b.logits, bb["accept_len"], bb["accept_nodes"], bb["out_tokens"],
+            bb["src_slot"], bb["new_len"], bb["step_ws"], b.draft_logits)
+    kw = dict(temperature=b.temperature, seed=b.rng_seed, offset=b.rng_offset,
+              near_ties=bb["near_ties"], status=bb["status"])
+    st_verification_step_ex(*args, **kw, top_p=1.0, draft_is_probs=False)
+    torch.cuda.synchronize()
+    for k in ("accept_len", "accept_nodes", "out_tokens", "near_ties", "new_len", "out"):
+        assert torch.equal(a.buf[k], b.buf[k]), k
+    assert torch.equal(a.k_cache, b.k_cache)
+    for top_p in (0.0, -0.5, 1.5, float("nan")):
+        with pytest.raises(RuntimeError):
+            st_verification_step_ex(*args, **kw, top_p=top_p)

@@ -32,6 +32,7 @@ from .binding import (  # noqa: F401
     st_tree_mask,
     st_tree_rope_append,
     st_verification_step,
+    st_verification_step_ex,
     st_verification_step_paged,
     st_verification_step_workspace,
     st_verify_greedy,

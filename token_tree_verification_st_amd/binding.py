@@ -89,6 +89,7 @@ def _declare(lib):
         "st_kv_compact_paged": (I, [I, I, I, I, P, P, I, I, P, I, P, P, P, I, P, P, P, P]),
         "st_stream_read": (I, [P, S, P, I, P]),
         "st_verification_step_paged": (I, [TP, _c.POINTER(StStep), I, I, P, I, P, S, P, P]),
+        "st_verification_step_ex": (I, [TP, _c.POINTER(StStep), I, _c.c_float, P, S, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -469,6 +470,29 @@ def st_verification_step(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix
     _check(load_library().st_verification_step(
         tree.ref, ctypes.byref(step), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(status), _stream()), "st_verification_step")
+
+
+def st_verification_step_ex(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix: int, out,
+                            lse, tokens, logits, accept_len, accept_nodes, out_tokens, src_slot,
+                            new_len, workspace, draft, temperature: float = 1.0, seed: int = 0,
+                            offset: int = 0, near_ties=None, scale: Optional[float] = None,
+                            status=None, top_p: float = 1.0, draft_is_probs: bool = False):
+    """st_verification_step with stochastic acceptance under nucleus
+    filtering (top_p < 1) and/or the draft given as probabilities."""
+    if draft is None:
+        raise ValueError("st_verification_step_ex: draft is required")
+    step = _step_struct(tree, q, k_cache, v_cache, prefix_len, max_prefix, out, lse, tokens,
+                        logits, draft, temperature, seed, offset, accept_len, accept_nodes,
+                        out_tokens, near_ties, src_slot, new_len, scale)
+    need = st_verification_step_workspace(tree, step)
+    if need == 0:
+        raise ValueError("st_verification_step_ex: invalid arguments")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check(load_library().st_verification_step_ex(
+        tree.ref, ctypes.byref(step), int(bool(draft_is_probs)), float(top_p), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(status), _stream()),
+        "st_verification_step_ex")
 
 
 def st_verification_step_paged(tree: Tree, q, k_pool, v_pool, block_table, prefix_len,

@@ -36,7 +36,8 @@ namespace {
 // The step over contiguous caches (pg null) or a paged pool (pg: the block
 // table; s->S_max is then the logical capacity).
 int step_impl(const st_tree* tree, const st_step* s, void* workspace, size_t ws_bytes,
-              int32_t* status, void* stream, const st::KvPaging* pg) {
+              int32_t* status, void* stream, const st::KvPaging* pg, int draft_probs = 0,
+              float top_p = 1.f) {
   int rc = st::check_tree_host(tree);
   if (rc) return rc;
   if (!step_fields_ok(s)) return ST_E_INVALID;
@@ -74,7 +75,7 @@ int step_impl(const st_tree* tree, const st_step* s, void* workspace, size_t ws_
   if (rc) return rc;
   if (s->draft_logits &&
       (rc = st::stochastic_node_launch(c.sw, s->logits, s->draft_logits, s->temperature, s->seed,
-                                       s->offset, tree->B, stream)))
+                                       s->offset, tree->B, stream, draft_probs, top_p)))
     return rc;
   // Greedy with bf16 attention: when there is at most one argmax slice per
   // attention workgroup (and V is a multiple of 4), the workgroups reduce them
@@ -115,4 +116,13 @@ extern "C" int st_verification_step_paged(const st_tree* tree, const st_step* s,
   sp.S_max = (int32_t)cap;
   const st::KvPaging pg{block_table, max_blocks, __builtin_ctz(block_size), n_blocks};
   return step_impl(tree, &sp, workspace, ws_bytes, status, stream, &pg);
+}
+
+extern "C" int st_verification_step_ex(const st_tree* tree, const st_step* s, int draft_is_probs,
+                                       float top_p, void* workspace, size_t ws_bytes,
+                                       int32_t* status, void* stream) {
+  if (!s || !(top_p > 0.f && top_p <= 1.f) || (draft_is_probs != 0 && draft_is_probs != 1))
+    return ST_E_INVALID;
+  if ((draft_is_probs || top_p < 1.f) && !s->draft_logits) return ST_E_INVALID;
+  return step_impl(tree, s, workspace, ws_bytes, status, stream, nullptr, draft_is_probs, top_p);
 }

@@ -24,7 +24,8 @@ int stochastic_prepare(const st_tree* tree, int V, const int32_t* tokens,
                        StochWalkArgs& walk);
 int stochastic_node_launch(const StochWalkArgs& walk, const float* target_logits,
                            const float* draft_logits, float temperature, uint64_t seed,
-                           uint64_t offset, int B, void* stream);
+                           uint64_t offset, int B, void* stream,
+                           int draft_probs = 0, float top_p = 1.f);
 
 // Vocab argmax slices handed to the attention launch: its workgroups load them
 // while their first K/V chunk is in flight and reduce them before their loop.

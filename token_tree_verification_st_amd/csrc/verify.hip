@@ -184,32 +184,36 @@ __device__ inline void block_sum2(double& x, double& y, double* lds) {
   y = uniform_f64(tree_fold<NW>(lds + NW, [](double a, double b) { return a + b; }));
 }
 
-// block_sum2 over one of two slot pairs of `lds` (4 * BLOCK / 64 doubles):
+// Three sums over one of two slot sets of `lds` (6 * BLOCK / 64 doubles):
 // consecutive calls that alternate `set` need no barrier between them.  Each
 // lane of a 16-lane row reads one wavefront's partial and a butterfly adds
 // them (a + b and b + a round alike, so every lane gets the same bits); the
 // totals end in scalar registers.
 template <int BLOCK>
-__device__ inline void block_sum2_set(double& x, double& y, double* lds, int set) {
+__device__ inline void block_sum3_set(double& x, double& y, double& z, double* lds, int set) {
   constexpr int NW = BLOCK / ST_WAVE;
   static_assert(NW == 16, "one partial per lane of a 16-lane row");
-  double* l = lds + set * 2 * NW;
+  double* l = lds + set * 3 * NW;
   x = wave_sum(x);
   y = wave_sum(y);
+  z = wave_sum(z);
   if (threadIdx.x % ST_WAVE == 0) {
     l[threadIdx.x / ST_WAVE] = x;
     l[NW + threadIdx.x / ST_WAVE] = y;
+    l[2 * NW + threadIdx.x / ST_WAVE] = z;
   }
   __syncthreads();
   const int r = threadIdx.x & 15;
-  double a = l[r], b = l[NW + r];
+  double a = l[r], b = l[NW + r], c = l[2 * NW + r];
 #pragma unroll
   for (int k = 1; k < 16; k <<= 1) {
     a += __shfl_xor(a, k, 16);
     b += __shfl_xor(b, k, 16);
+    c += __shfl_xor(c, k, 16);
   }
   x = uniform_f64(a);
   y = uniform_f64(b);
+  z = uniform_f64(c);
 }
 
 using st::argmax_merge;
@@ -394,71 +398,236 @@ __device__ __forceinline__ double resid_sum(const float (&P)[NPT], const float (
 }
 
 // A thread's share of the mass at or above `cut` (fp32 within a group, fp64
-// from there on, as the row totals).
+// from there on, as the row totals), and how many entries that is.
 template <bool VEC, int NPT>
-__device__ __forceinline__ double kept_sum(const float (&X)[NPT], float cut) {
+__device__ __forceinline__ double kept_sum(const float (&X)[NPT], float cut, int& n) {
   constexpr int EPT = VEC ? 4 : 1;
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < NPT / EPT; ++k) {
     float g = 0.f;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) g += X[k * EPT + j] >= cut ? X[k * EPT + j] : 0.f;
+    for (int j = 0; j < EPT; ++j) {
+      const bool in = X[k * EPT + j] >= cut;
+      g += in ? X[k * EPT + j] : 0.f;
+      n += in;
+    }
     s += (double)g;
   }
   return s;
 }
 
+// The search's last phase: one wavefront, at most kCutLane candidates a lane.
+constexpr int kCutLane = 8;
+constexpr int kCutCand = kCutLane * ST_WAVE;  // per row
+struct CutLds {
+  double red[6 * kMaxWaves];  // two slot sets of three sums
+  float cand[2][kCutCand];    // the entries still between the bounds
+  int wtot[kMaxWaves];
+  uint32_t cut[2];
+  double kept[2];
+};
+
+// One row's bisection state over fp32 bit patterns: `want` is top_p of the
+// row's total; the mass at or above lo reaches it, the mass at or above hi
+// does not.  Masses and entry counts at both bounds are kept (the count at
+// lo is unknown, so large, until lo first moves).
+struct CutRow {
+  uint32_t lo, hi;
+  double want, m_lo, m_hi;
+  int n_lo, n_hi;
+  __device__ bool open() const { return hi - lo > 1u; }
+  __device__ uint32_t mid() const { return lo + (hi - lo) / 2u; }
+  __device__ int between() const { return n_lo - n_hi; }  // entries in [lo, hi)
+  __device__ void take(uint32_t m, double mass, int n) {
+    if (!open()) return;
+    if (mass >= want) {
+      lo = m;
+      m_lo = mass;
+      n_lo = n;
+    } else {
+      hi = m;
+      m_hi = mass;
+      n_hi = n;
+    }
+  }
+};
+
 // Nucleus (top-p) cuts of the target and draft weights P and Q (totals zt,
 // zd; largest entries at most pmax, qmax): the largest value `cut` whose mass
 // at or above it still reaches top_p of the total, found by bisection over
-// the bit patterns of non-negative floats (which order like the values), both
-// rows in one reduction per step.  The kept set {X >= cut} is the smallest
-// set of most likely tokens holding top_p of the mass, with every token tied
-// at the cut.  Entries below the cut are zeroed and zt, zd become the kept
-// mass.  Only P is cut when `both` is false.
+// the bit patterns of non-negative floats (which order like the values).  The
+// kept set {X >= cut} is the smallest set of most likely tokens holding top_p
+// of the mass, with every token tied at the cut.  Entries below the cut are
+// zeroed and zt, zd become the kept mass.  Only P is cut when `both` is false.
+//
+// While many entries lie between a row's bounds, each step is a pass over
+// every entry of both rows with one block reduction (masses and counts).
+// Once at most kCutCand entries of each open row remain between its bounds
+// they are gathered into LDS (in thread and entry order) and wavefront 0
+// finishes both searches alone: the mass at or above a trial cut is then the
+// mass at or above the upper bound at the gathering plus the candidates at or
+// above the cut.
+//
+// The search starts from a lower bound that is always inside the nucleus:
+// entries below (1 - top_p) Z / (2 V) hold at most half of the mass the
+// nucleus may leave out, so the mass at or above it exceeds top_p Z.  (Its
+// own mass is then unknown until the lower bound first moves.)
+__device__ inline uint32_t nucleus_floor(double z, float top_p, int V, float xmax) {
+  const float f = __double2float_rd((1.0 - (double)top_p) * z / (2.0 * V));
+  return (f > 0.f && f < xmax) ? __float_as_uint(f) : 0u;
+}
+
 template <bool VEC, int NPT>
 __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, float pmax,
-                                   float qmax, float top_p, double& zt, double& zd, double* lds,
-                                   float& cut_t, float& cut_d) {
-  // every bound and total below is block-uniform: kept in scalar registers
-  uint32_t lo_t = 0u, hi_t = __builtin_amdgcn_readfirstlane(__float_as_uint(pmax) + 1u);
-  uint32_t lo_d = 0u, hi_d = __builtin_amdgcn_readfirstlane(both ? __float_as_uint(qmax) + 1u : 1u);
-  const double want_t = uniform_f64((double)top_p * zt), want_d = uniform_f64((double)top_p * zd);
-  double kt = uniform_f64(zt), kd = uniform_f64(zd);  // kept mass at the lower bounds
-  int set = 0;
-  while ((hi_t - lo_t > 1u) | (hi_d - lo_d > 1u)) {  // block-uniform
-    const uint32_t mt = lo_t + (hi_t - lo_t) / 2u, md = lo_d + (hi_d - lo_d) / 2u;
-    double st = kept_sum<VEC, NPT>(P, __uint_as_float(mt));
-    double sd = both ? kept_sum<VEC, NPT>(Q, __uint_as_float(md)) : 0.0;
-    block_sum2_set<kNodeBlock>(st, sd, lds, set);
-    set ^= 1;
-    if (hi_t - lo_t > 1u) {
-      if (st >= want_t) {
-        lo_t = mt;
-        kt = st;
-      } else {
-        hi_t = mt;
-      }
-    }
-    if (hi_d - lo_d > 1u) {
-      if (sd >= want_d) {
-        lo_d = md;
-        kd = sd;
-      } else {
-        hi_d = md;
-      }
-    }
+                                   float qmax, float top_p, int V, double& zt, double& zd,
+                                   CutLds& c, float& cut_t, float& cut_d) {
+  constexpr int kUnknown = 1 << 30;
+  const int tid = threadIdx.x, lane = tid % ST_WAVE;
+  // one register per entry from here on (otherwise the compiler may keep a
+  // row value and its masked copy both live through the search and spill)
+#pragma unroll
+  for (int e = 0; e < NPT; ++e) {
+    asm volatile("" : "+v"(P[e]));
+    asm volatile("" : "+v"(Q[e]));
   }
-  cut_t = __uint_as_float(lo_t);
-  cut_d = __uint_as_float(lo_d);
+  // every bound and total below is block-uniform: kept in scalar registers
+  zt = uniform_f64(zt);
+  zd = uniform_f64(zd);
+  const uint32_t ft = nucleus_floor(zt, top_p, V, pmax);
+  const uint32_t fd = both ? nucleus_floor(zd, top_p, V, qmax) : 0u;
+  CutRow rt{ft, (uint32_t)__builtin_amdgcn_readfirstlane(__float_as_uint(pmax) + 1u),
+            (double)top_p * zt, ft ? -1.0 : zt, 0.0, kUnknown, 0};
+  CutRow rd{fd, (uint32_t)__builtin_amdgcn_readfirstlane(both ? __float_as_uint(qmax) + 1u : 1u),
+            (double)top_p * zd, fd ? -1.0 : zd, 0.0, kUnknown, 0};
+  int set = 0;
+  bool few = false;
+  while (rt.open() | rd.open()) {  // block-uniform
+    const uint32_t mt = rt.mid(), md = rd.mid();
+    int nt = 0, nd = 0;
+    double st = kept_sum<VEC, NPT>(P, __uint_as_float(mt), nt);
+    double sd = both ? kept_sum<VEC, NPT>(Q, __uint_as_float(md), nd) : 0.0;
+    // both counts (each at most 32768) in one exactly summed double
+    double sn = (double)(nt * 65536 + nd);
+    block_sum3_set<kNodeBlock>(st, sd, sn, c.red, set);
+    set ^= 1;
+    const long long n = (long long)sn;
+    rt.take(mt, st, (int)(n >> 16));
+    rd.take(md, sd, (int)(n & 0xFFFF));
+    few = (!rt.open() || rt.between() <= kCutCand) && (!rd.open() || rd.between() <= kCutCand);
+    if (few) break;
+  }
+  if (few && (rt.open() | rd.open())) {
+    // gather the candidates: a thread's entries in [lo, hi), placed after
+    // those of the threads before it (counts packed as in the search)
+    const float lt = __uint_as_float(rt.lo), ht = __uint_as_float(rt.hi);
+    const float ld = __uint_as_float(rd.lo), hd = __uint_as_float(rd.hi);
+    const bool ot = rt.open(), od = rd.open();
+    int mine = 0;
+#pragma unroll
+    for (int e = 0; e < NPT; ++e) {
+      mine += (ot && P[e] >= lt && P[e] < ht) ? 1 : 0;
+      mine += (od && Q[e] >= ld && Q[e] < hd) ? 65536 : 0;
+    }
+    int inc = mine;
+#pragma unroll
+    for (int o = 1; o < ST_WAVE; o <<= 1) {
+      const int v = __shfl_up(inc, o, ST_WAVE);
+      inc += lane >= o ? v : 0;
+    }
+    if (lane == ST_WAVE - 1) c.wtot[tid / ST_WAVE] = inc;
+    __syncthreads();
+    int off = inc - mine;
+    for (int w = 0; w < tid / ST_WAVE; ++w) off += c.wtot[w];
+    int pt = off & 0xFFFF, pd = off >> 16;
+#pragma unroll
+    for (int e = 0; e < NPT; ++e) {
+      if (ot && P[e] >= lt && P[e] < ht) {
+        if (pt < kCutCand) c.cand[0][pt] = P[e];
+        ++pt;
+      }
+      if (od && Q[e] >= ld && Q[e] < hd) {
+        if (pd < kCutCand) c.cand[1][pd] = Q[e];
+        ++pd;
+      }
+    }
+    __syncthreads();
+    if (tid < ST_WAVE) {
+      const int ct = ot ? rt.between() : 0, cd = od ? rd.between() : 0;
+      float xt[kCutLane], xd[kCutLane];
+#pragma unroll
+      for (int j = 0; j < kCutLane; ++j) {
+        const int q = j * ST_WAVE + lane;
+        xt[j] = q < ct ? c.cand[0][q] : 0.f;
+        xd[j] = q < cd ? c.cand[1][q] : 0.f;
+      }
+      // every candidate lies below the upper bounds of the gathering, so the
+      // masses above those bounds are the base of every trial sum
+      const double base_t = rt.m_hi, base_d = rd.m_hi;
+      while (true) {
+        // a row with no candidate strictly between its bounds is decided:
+        // every trial cut in there keeps only the mass above the upper bound
+        const float lt_ = __uint_as_float(rt.lo), ht_ = __uint_as_float(rt.hi);
+        const float ld_ = __uint_as_float(rd.lo), hd_ = __uint_as_float(rd.hi);
+        bool it = false, id = false;
+#pragma unroll
+        for (int j = 0; j < kCutLane; ++j) {
+          it |= xt[j] > lt_ && xt[j] < ht_;
+          id |= xd[j] > ld_ && xd[j] < hd_;
+        }
+        if (__ballot(it) == 0ull) rt.hi = rt.lo + 1u;
+        if (__ballot(id) == 0ull) rd.hi = rd.lo + 1u;
+        if (!(rt.open() | rd.open())) break;  // wave-uniform
+        const uint32_t mt = rt.mid(), md = rd.mid();
+        const float ft = __uint_as_float(mt), fd = __uint_as_float(md);
+        double gt = 0.0, gd = 0.0;
+#pragma unroll
+        for (int j = 0; j < kCutLane; j += 4) {
+          float a = 0.f, b = 0.f;
+#pragma unroll
+          for (int i = j; i < j + 4; ++i) {
+            a += xt[i] >= ft ? xt[i] : 0.f;
+            b += xd[i] >= fd ? xd[i] : 0.f;
+          }
+          gt += (double)a;
+          gd += (double)b;
+        }
+        const double st = uniform_f64(base_t + wave_sum(gt));
+        const double sd = uniform_f64(base_d + wave_sum(gd));
+        rt.take(mt, st, 0);
+        rd.take(md, sd, 0);
+      }
+      if (tid == 0) {
+        c.cut[0] = rt.lo;
+        c.cut[1] = rd.lo;
+        c.kept[0] = rt.m_lo;
+        c.kept[1] = rd.m_lo;
+      }
+    }
+    __syncthreads();
+    rt.lo = (uint32_t)__builtin_amdgcn_readfirstlane(c.cut[0]);
+    rd.lo = (uint32_t)__builtin_amdgcn_readfirstlane(c.cut[1]);
+    rt.m_lo = uniform_f64(c.kept[0]);
+    rd.m_lo = uniform_f64(c.kept[1]);
+  }
+  if ((rt.m_lo < 0.0) | (rd.m_lo < 0.0)) {  // a cut at the starting bound
+    int nt = 0, nd = 0;
+    double st = kept_sum<VEC, NPT>(P, __uint_as_float(rt.lo), nt);
+    double sd = both ? kept_sum<VEC, NPT>(Q, __uint_as_float(rd.lo), nd) : 0.0;
+    double sn = 0.0;
+    block_sum3_set<kNodeBlock>(st, sd, sn, c.red, set);
+    if (rt.m_lo < 0.0) rt.m_lo = st;
+    if (rd.m_lo < 0.0) rd.m_lo = sd;
+  }
+  cut_t = __uint_as_float(rt.lo);
+  cut_d = __uint_as_float(rd.lo);
 #pragma unroll
   for (int e = 0; e < NPT; ++e) {
     P[e] = P[e] >= cut_t ? P[e] : 0.f;
     if (both) Q[e] = Q[e] >= cut_d ? Q[e] : 0.f;
   }
-  zt = kt;
-  if (both) zd = kd;
+  zt = rt.m_lo;
+  if (both) zd = rd.m_lo;
 }
 
 // v plus the partner lane's v at exchange stage S: the lanes l ^ 32, l ^ 16,
@@ -674,7 +843,7 @@ struct NodeLds {
   int ok[ST_MAX_NODES];                                           // token in range
   float redf[2 * kMaxWaves];
   double red[2 * kMaxWaves];
-  double red4[4 * kMaxWaves];
+  CutLds cut;
   double u_draw;
   DrawLds draw;
 };
@@ -782,8 +951,8 @@ stoch_node_kernel(StochArgs g) {
   // row only where it is used)
   float cut_t = 0.f, cut_d = 0.f;
   if (EXT && g.top_p < 1.f)
-    nucleus_cut<VEC, NPT>(P, Q, nk > 0, 1.f, g.draft_probs ? md : 1.f, g.top_p, zt, zd, s.red4,
-                          cut_t, cut_d);
+    nucleus_cut<VEC, NPT>(P, Q, nk > 0, 1.f, g.draft_probs ? md : 1.f, g.top_p, g.V, zt, zd,
+                          s.cut, cut_t, cut_d);
   const double a = 1.0 / zt;
 
   if (nk == 0) {  // a leaf: the walk stops here with r = p_u
@@ -947,9 +1116,10 @@ int node_launch(const st::StochWalkArgs& w, const float* target_logits, const fl
 
 int st::stochastic_node_launch(const st::StochWalkArgs& w, const float* target_logits,
                                const float* draft_logits, float temperature, uint64_t seed,
-                               uint64_t offset, int B, void* stream) {
-  return node_launch(w, target_logits, draft_logits, 0, temperature, 1.f, seed, offset, B,
-                     stream);
+                               uint64_t offset, int B, void* stream, int draft_probs,
+                               float top_p) {
+  return node_launch(w, target_logits, draft_logits, draft_probs, temperature, top_p, seed,
+                     offset, B, stream);
 }
 
 extern "C" int st_verify_stochastic(const st_tree* tree, int V, const int32_t* tokens,

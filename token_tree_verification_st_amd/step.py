@@ -7,7 +7,8 @@ of separate entry points, mask first.  Every call only enqueues kernels."""
 from __future__ import annotations
 
 from .binding import (st_kv_compact, st_tree_attention, st_tree_mask, st_verification_step,
-                      st_verify_greedy, st_verify_stochastic, st_verify_stochastic_ex)
+                      st_verification_step_ex, st_verify_greedy, st_verify_stochastic,
+                      st_verify_stochastic_ex)
 from .device_io import DeviceWorkload
 
 
@@ -48,9 +49,21 @@ def run_compact(dw: DeviceWorkload):
                   b["src_slot"], b["new_len"], b["status"])
 
 
-def run_step(dw: DeviceWorkload, stochastic: bool):
-    """The whole step in one C-ABI call."""
+def run_step(dw: DeviceWorkload, stochastic: bool, top_p: float = 1.0, draft=None):
+    """The whole step in one C-ABI call (draft: probabilities [T][V] to use
+    instead of the draft logits)."""
     b = dw.buf
+    if stochastic and (top_p < 1.0 or draft is not None):
+        st_verification_step_ex(dw.tree, dw.q, dw.k_cache, dw.v_cache, dw.prefix_len,
+                                dw.max_prefix, b["out"], b["lse"], dw.tokens, dw.logits,
+                                b["accept_len"], b["accept_nodes"], b["out_tokens"], b["src_slot"],
+                                b["new_len"], b["step_ws"],
+                                dw.draft_logits if draft is None else draft,
+                                temperature=dw.temperature, seed=dw.rng_seed,
+                                offset=dw.rng_offset, near_ties=b["near_ties"],
+                                status=b["status"], top_p=top_p,
+                                draft_is_probs=draft is not None)
+        return
     st_verification_step(dw.tree, dw.q, dw.k_cache, dw.v_cache, dw.prefix_len, dw.max_prefix,
                          b["out"], b["lse"], dw.tokens, dw.logits, b["accept_len"],
                          b["accept_nodes"], b["out_tokens"], b["src_slot"], b["new_len"],
@@ -60,15 +73,15 @@ def run_step(dw: DeviceWorkload, stochastic: bool):
 
 
 def verification_step(dw: DeviceWorkload, stochastic: bool = False, verify: bool = True,
-                      compact: bool = True, fused: bool = True):
+                      compact: bool = True, fused: bool = True, top_p: float = 1.0, draft=None):
     """One step: the one-call path when it applies (logits present, acceptance
     and compaction wanted), else mask -> attention -> acceptance -> compaction."""
     if fused and verify and compact and dw.V > 0:
-        run_step(dw, stochastic)
+        run_step(dw, stochastic, top_p=top_p, draft=draft)
         return
     run_mask(dw)
     run_attention(dw)
     if verify and dw.V > 0:
-        run_verify(dw, stochastic)
+        run_verify(dw, stochastic, top_p=top_p, draft=draft)
         if compact:
             run_compact(dw)
