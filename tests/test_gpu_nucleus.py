@@ -156,3 +156,48 @@ def test_one_call_step_ex_plain_options_and_bad_arguments():
     for top_p in (0.0, -0.5, 1.5, float("nan")):
         with pytest.raises(RuntimeError):
             st_verification_step_ex(*args, **kw, top_p=top_p)
+
+
+def _levels(rng, T, V, n):
+    """Logits on n integer levels 0, -1, ..., -(n-1): thousands of exactly
+    tied weights on every level."""
+    return -rng.integers(0, n, size=(T, V)).astype(np.float32)
+
+
+@pytest.mark.parametrize("pattern,top_p", [("plateaus", 0.9), ("flat", 0.90001),
+                                           ("near_total", 0.99999), ("spike", 0.9),
+                                           ("plateaus_draft_probs", 0.7)])
+def test_nucleus_search_paths(pattern, top_p):
+    """Rows that drive the nucleus search down each of its paths at full
+    vocabulary: plateaus (thousands of weights tied at the cut, so the bounds
+    never hold few enough entries to gather), a flat row (every token kept),
+    a nucleus holding all but 1e-5 of the mass (the search may end at its
+    starting bound), one dominant token (a one-token nucleus)."""
+    rng = np.random.default_rng(500 + len(pattern))
+    B = 4
+    trees = [tree_random_attach(rng, 24, 5) for _ in range(B)]
+    # near_total at 4000 tokens: the running sums near the cut then move by
+    # about 2.5e-4 a token, so few nodes land in the oracle's 1e-6 tie band
+    wl = build_workload("paths", rng, dtype="bf16", Hq=1, Hkv=1, D=64,
+                        V=4000 if pattern == "near_total" else 32000,
+                        prefix_lens=[1] * B, trees=trees, max_depth=5, token_rule="uniform",
+                        logit_sigma=1.0, draft_noise_sigma=0.5, temperature=1.0)
+    T, V = wl.logits.shape
+    if pattern.startswith("plateaus"):
+        wl.logits[:] = _levels(rng, T, V, 6)
+        wl.draft_logits[:] = _levels(rng, T, V, 4)
+    elif pattern == "flat":
+        wl.logits[:] = 0.0
+        wl.draft_logits[:] = 0.0
+    elif pattern == "near_total":
+        wl.logits[:] = rng.normal(0.0, 0.5, (T, V)).astype(np.float32)
+        wl.draft_logits[:] = rng.normal(0.0, 0.5, (T, V)).astype(np.float32)
+    else:   # spike: the node's own token dominates both rows
+        wl.logits[:] = rng.normal(0.0, 1.0, (T, V)).astype(np.float32)
+        wl.draft_logits[:] = rng.normal(0.0, 1.0, (T, V)).astype(np.float32)
+        hot = rng.integers(0, V, size=T)
+        wl.logits[np.arange(T), hot] += 30.0
+        wl.draft_logits[np.arange(T), hot] += 30.0
+    al, excused = _check(wl, top_p, probs=pattern.endswith("draft_probs"))
+    say(f"{pattern} top_p={top_p}: accept_len {al.tolist()}, near ties excused {excused}")
+    assert excused < B
