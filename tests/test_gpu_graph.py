@@ -14,16 +14,24 @@ from tests.gpu_util import require_gpu, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,stochastic", [("tiny_fp32", False), ("ragged_batch", False),
-                                             ("stochastic_chain", True)])
-def test_graph_replays_equal_eager(name, stochastic):
+@pytest.mark.parametrize("name,stochastic,top_p,probs",
+                         [("tiny_fp32", False, 1.0, False), ("ragged_batch", False, 1.0, False),
+                          ("stochastic_chain", True, 1.0, False),
+                          ("stochastic_tree", True, 0.9, True)])
+def test_graph_replays_equal_eager(name, stochastic, top_p, probs):
     require_gpu()
     wl = make_workload(name, 0)
     dw = to_device(wl)
+    draft = None
+    if probs:   # the draft as probabilities (one-call step with the sampling options)
+        z = wl.draft_logits.astype(np.float64) / wl.temperature
+        pr = np.exp(z - z.max(axis=1, keepdims=True))
+        draft = torch.from_numpy((pr / pr.sum(axis=1, keepdims=True)).astype(np.float32)).cuda()
+    opts = dict(stochastic=stochastic, top_p=top_p, draft=draft)
     k0, v0 = dw.k_cache.clone(), dw.v_cache.clone()
     keys = ["mask", "depth", "out", "lse", "accept_len", "accept_nodes", "out_tokens", "src_slot",
             "new_len"]
-    stp.verification_step(dw, stochastic=stochastic)
+    stp.verification_step(dw, **opts)
     torch.cuda.synchronize()
     eager = {k: dw.buf[k].clone() for k in keys}
     k_eager, v_eager = dw.k_cache.clone(), dw.v_cache.clone()
@@ -33,7 +41,7 @@ def test_graph_replays_equal_eager(name, stochastic):
     dw.v_cache.copy_(v0)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        stp.verification_step(dw, stochastic=stochastic)
+        stp.verification_step(dw, **opts)
     for rep in range(4):
         for k in keys:                      # eager work between replays
             dw.buf[k].zero_()
@@ -47,7 +55,7 @@ def test_graph_replays_equal_eager(name, stochastic):
         assert torch.equal(dw.k_cache, k_eager) and torch.equal(dw.v_cache, v_eager)
         _ = (dw.buf["out"].float() * 2).sum().item()   # unrelated eager kernels
     assert int(dw.buf["status"].item()) == 0
-    say(f"{name}: 4 graph replays equal the eager step")
+    say(f"{name} top_p={top_p} probs={probs}: 4 graph replays equal the eager step")
 
 
 def test_stream_read_helper():
