@@ -69,11 +69,13 @@ struct AttnArgs {
 // The physical block of key `key` of request b in a paged pool: its block-
 // table entry, clamped into [0, n_blocks) and flagged when it was outside, so
 // every address stays inside the pool.
-__device__ inline int table_entry(const AttnArgs& a, int b, int key) {
-  const int e = a.pg.bt[(size_t)b * a.pg.bt_stride + (key >> a.pg.lbs)];
+__device__ inline int table_phys(const AttnArgs& a, int e) {
   const int phys = min(max(e, 0), a.pg.n_blocks - 1);
   if (phys != e) st::set_status(a.status, ST_STATUS_BAD_BLOCK);
   return phys;
+}
+__device__ inline int table_entry(const AttnArgs& a, int b, int key) {
+  return table_phys(a, a.pg.bt[(size_t)b * a.pg.bt_stride + (key >> a.pg.lbs)]);
 }
 
 template <typename T>
@@ -513,6 +515,17 @@ attn_stream_kernel(AttnArgs a) {
   // masks are built; a second LDS object would cost the ring's prefetch: the
   // compiler then waits for every direct load before each LDS read)
   int* am_scratch = sPar;
+  // paged pool: the raw table entries of the first chunks, read before the
+  // request's size is known (a chunk's key depends on the split alone; the
+  // index is clamped into the table row, and an entry is checked where it is
+  // used, for a chunk inside the request's keys)
+  int e_first[PRIME];
+#pragma unroll
+  for (int s = 0; s < PRIME; ++s)
+    e_first[s] = PAGED ? a.pg.bt[(size_t)it.b * a.pg.bt_stride +
+                                 min((k0 + (s * KWV + kg) * kCK) >> a.pg.lbs,
+                                     a.pg.bt_stride - 1)]
+                       : 0;
   const bool am = a.am.logits != nullptr && it.w < a.am.units;
   st::ArgmaxRegs amr;
   if (am) st::argmax_slice_load<true>(a.am.logits, a.am.V, it.w / a.am.nslices, it.w % a.am.nslices, amr);
@@ -539,7 +552,7 @@ attn_stream_kernel(AttnArgs a) {
   const ChunkOff<D, RWV> coff(rw, lane);
   if (nmine > 0)
     chunk_dma<D, RWV, PAGED>(ring, ring + kCK * D, a, it, kgp, vgp, k0 + kg * kCK, klast, rw,
-                             lane, coff, entry(kg));
+                             lane, coff, PAGED ? table_phys(a, e_first[0]) : 0);
 
   // Q of the workgroup's rows (rows past the end repeat the last): staged in
   // LDS once when several key groups share the rows, else loaded directly.
@@ -594,7 +607,7 @@ attn_stream_kernel(AttnArgs a) {
     if (s < nmine)
       chunk_dma<D, RWV, PAGED>(ring + s * STAGE, ring + s * STAGE + kCK * D, a, it, kgp, vgp,
                                k0 + (s * KWV + kg) * kCK, klast, rw, lane, coff,
-                               entry(s * KWV + kg));
+                               PAGED ? table_phys(a, e_first[s]) : 0);
   wait_chunks<PRIME - 1, DPC>(want - 1);  // the first chunk, Q and the masks are older
   if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
   if (need_mask) {
