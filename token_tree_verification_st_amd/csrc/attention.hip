@@ -530,6 +530,18 @@ attn_stream_kernel(AttnArgs a) {
   st::ArgmaxRegs amr;
   if (am) st::argmax_slice_load<true>(a.am.logits, a.am.V, it.w / a.am.nslices, it.w % a.am.nslices, amr);
 
+  // contiguous caches: this wavefront's first chunk is issued before the
+  // request's sizes arrive when its 32 rows lie inside the (request, head)
+  // cache.  It is kept when the chunk lies wholly inside the request's keys;
+  // otherwise it is waited for (no direct load may still be writing LDS when
+  // the slot is reloaded or the workgroup ends) and replaced.
+  const int key0 = k0 + kg * kCK;
+  const bool spec = !PAGED && key0 + kCK <= a.S_max;
+  const ChunkOff<D, RWV> coff(rw, lane);
+  if (spec)
+    chunk_dma<D, RWV, false>(ring, ring + kCK * D, a, it, kgp, vgp, key0, key0 + kCK - 1, rw,
+                             lane, coff);
+
   const ReqInfo rq = request_info(a, it.b);
   const int rows_b = rq.n * a.G;
   const int row0 = it.rblk * ROWS;
@@ -537,6 +549,7 @@ attn_stream_kernel(AttnArgs a) {
     if (!rq.ok && threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
       st::set_status(a.status, ST_STATUS_BAD_PREFIX);
     if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
+    if (spec) ST_WAIT_VMCNT(0);
     return;
   }
   const int k1 = min(k0 + a.KS, rq.key_end);
@@ -549,10 +562,11 @@ attn_stream_kernel(AttnArgs a) {
   // the first chunk goes first, then Q and the masks, then the rest of the ring
   // paged pool: the block of each chunk is looked up one refill ahead
   auto entry = [&](int c) { return PAGED ? table_entry(a, it.b, k0 + c * kCK) : 0; };
-  const ChunkOff<D, RWV> coff(rw, lane);
-  if (nmine > 0)
-    chunk_dma<D, RWV, PAGED>(ring, ring + kCK * D, a, it, kgp, vgp, k0 + kg * kCK, klast, rw,
-                             lane, coff, PAGED ? table_phys(a, e_first[0]) : 0);
+  const bool keep = spec && nmine > 0 && klast - key0 >= kCK - 1;
+  if (spec && !keep) ST_WAIT_VMCNT(0);
+  if (nmine > 0 && !keep)
+    chunk_dma<D, RWV, PAGED>(ring, ring + kCK * D, a, it, kgp, vgp, key0, klast, rw, lane, coff,
+                             PAGED ? table_phys(a, e_first[0]) : 0);
 
   // Q of the workgroup's rows (rows past the end repeat the last): staged in
   // LDS once when several key groups share the rows, else loaded directly.
