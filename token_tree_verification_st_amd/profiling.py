@@ -222,6 +222,36 @@ def read_traffic(path: str):
     return int(b.group(1))
 
 
+def sq_md(csvs, kernel: str, title: str, commands) -> str:
+    """SQ counters of one kernel from rocprofv3 --pmc passes: the average per
+    dispatch over the kernel's dispatches, and per wavefront (SQ_WAVES)."""
+    sums, counts = {}, {}
+    for path in csvs:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if _short(r["Kernel_Name"]) != kernel:
+                    continue
+                c = r["Counter_Name"]
+                sums[c] = sums.get(c, 0.0) + float(r["Counter_Value"])
+                counts[c] = counts.get(c, 0) + 1
+    avg = {c: sums[c] / counts[c] for c in sums}
+    waves = avg.get("SQ_WAVES", 1.0) or 1.0
+    n = max(counts.values()) if counts else 0
+    out = [f"# {title}", "", "Commands (run from /tmp with TMPDIR=/tmp; $R = repository root), "
+           "one pass each:", "", "```", *commands, "```", "",
+           f"Average per dispatch over the {n} dispatches of `{kernel}` "
+           f"({waves:.0f} wavefronts each):", "", "| counter | per dispatch | per wavefront |",
+           "|---|---|---|"]
+    for c in sorted(avg):
+        out.append(f"| {c} | {avg[c]:.0f} | {avg[c] / waves:.1f} |")
+    if "SQ_WAVE_CYCLES" in avg:
+        wc = avg["SQ_WAVE_CYCLES"]
+        parts = [f"{k} / SQ_WAVE_CYCLES = {100 * avg[k] / wc:.0f}%"
+                 for k in ("SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY") if k in avg]
+        out += ["", "Shares of wavefront time: " + ", ".join(parts) + "."]
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if argv[0] == "stats":
         stats_csv, out, title, command = argv[1:5]
@@ -235,6 +265,10 @@ def main(argv):
         fcsv, wcsv, copy_bytes, lm_grid, out, cmd_f, cmd_w = argv[1:8]
         open(out, "w").write(linear_traffic_md(fcsv, wcsv, int(copy_bytes), int(lm_grid), cmd_f,
                                                cmd_w))
+    elif argv[0] == "sq":   # OUT KERNEL TITLE CSV... -- COMMAND...
+        out, kernel, title = argv[1:4]
+        i = argv.index("--")
+        open(out, "w").write(sq_md(argv[4:i], kernel, title, argv[i + 1:]))
     elif argv[0] == "traffic":
         fcsv, wcsv, copy_bytes, workload, out, cmd_f, cmd_w = argv[1:8]
         open(out, "w").write(traffic_md(fcsv, wcsv, int(copy_bytes), workload, cmd_f, cmd_w))
