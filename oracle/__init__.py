@@ -52,7 +52,8 @@ from .tree import (  # noqa: F401
 )
 from .attention import decode_values, tree_attention  # noqa: F401
 from .philox import philox4x64_10, uniforms_for_node  # noqa: F401
-from .verify import nucleus, verify_greedy, verify_stochastic  # noqa: F401
+from .verify import (nucleus, nucleus_variants, stochastic_outcomes,  # noqa: F401
+                     verify_greedy, verify_stochastic)
 from .compact import kv_compact  # noqa: F401
 from .layer import (  # noqa: F401
     ROPE_THETA,

@@ -18,13 +18,16 @@ Readings used here (the pages leave them open):
     node u with residual r (initially p_u), test the children in ascending
     index: child c with token x is accepted iff u_acc(c) * q_u[x] < r[x]
     (that is u < min(1, r/q) without a division); after a rejection
-    r <- max(0, r - q_u) renormalised, kept as it was if its mass is at most
-    1e-6 (a residual of the rounding of nearly equal r and q, which must not
-    be renormalised into a distribution: two one-token nuclei on the same
-    token leave exactly such a residual); when
-    no child is accepted the replacement token is drawn from r by inverse CDF
-    with u_smp(u), summing r in ascending vocab order.  The residual draw is
-    what makes the equal-distribution guarantee hold;
+    r <- max(0, r - q_u) renormalised whenever that residual has any mass,
+    and kept as it was only when its mass is exactly 0 (r <= q_u everywhere:
+    the rejected token's distribution is then unchanged); when no child is
+    accepted the replacement token is drawn from r by inverse CDF with
+    u_smp(u), summing r in ascending vocab order.  The residual draw is what
+    makes the equal-distribution guarantee hold;
+  * near ties: a comparison |r[x] - u q[x]| < 1e-6, a residual mass in
+    (0, 2e-6], a nucleus cut whose running sum lies within 1e-6 of top_p and a
+    draw within 1e-6 of a bin edge are decided by rounding in any finite
+    precision; stochastic_outcomes lists what each may lead to;
   * accept_len L counts accepted non-root nodes; out_tokens holds their tokens
     followed by the replacement token, so L + 1 tokens are emitted;
   * if an accepted path would grow past ``max_depth`` nodes below the root the
@@ -111,29 +114,56 @@ def softmax_with_temperature(row, temperature: float) -> np.ndarray:
     return e / e.sum()
 
 
+def _at_or_above(prob, thr):
+    """prob restricted to the entries at least thr, renormalised."""
+    kept = np.where(prob >= thr, prob, 0.0)
+    return kept / kept.sum()
+
+
+def nucleus_variants(prob, top_p: float):
+    """prob restricted to its top-p nucleus and renormalised (first entry):
+    sorted descending, the first rank whose running sum reaches top_p of the
+    total sets the cut, and every token at least as likely as that rank's is
+    kept.  Whether a set of tokens holds top_p of the mass is decided by its
+    sum, and the candidate sets are the value levels: all tokens at or above
+    some probability.  When the level chosen holds a mass within NEAR_TIE_EPS
+    of top_p, the next lower level (one more level of tokens) follows as a
+    variant; when the next higher level does, that level follows.  Also
+    returns whether the cut is a near tie."""
+    prob = np.asarray(prob, dtype=np.float64)
+    if top_p >= 1.0:
+        return [prob], False
+    total = float(prob.sum())
+    sp = prob[np.argsort(-prob, kind="stable")]
+    csum = np.cumsum(sp)
+    target = top_p * total
+    k = int(np.nonzero(csum >= target)[0][0])
+    start = int(np.nonzero(sp == sp[k])[0][0])       # the level of rank k, in rank order
+    end = int(np.nonzero(sp == sp[k])[0][-1])
+    out = [_at_or_above(prob, sp[k])]
+    near_at = abs(csum[end] - target) < NEAR_TIE_EPS * total
+    near_before = start > 0 and abs(csum[start - 1] - target) < NEAR_TIE_EPS * total
+    if near_before:
+        out.append(_at_or_above(prob, sp[start - 1]))
+    if near_at and end + 1 < len(sp) and sp[end + 1] > 0:
+        out.append(_at_or_above(prob, sp[end + 1]))
+    return out, bool(near_at or near_before)
+
+
 def nucleus(prob, top_p: float):
     """prob restricted to its top-p nucleus and renormalised, and whether the
     cut is a near tie (the running sum at the cut, or just before it, within
     NEAR_TIE_EPS of top_p)."""
-    prob = np.asarray(prob, dtype=np.float64)
-    if top_p >= 1.0:
-        return prob, False
-    total = float(prob.sum())
-    order = np.argsort(-prob, kind="stable")
-    csum = np.cumsum(prob[order])
-    target = top_p * total
-    k = int(np.nonzero(csum >= target)[0][0])
-    thr = prob[order[k]]
-    kept = np.where(prob >= thr, prob, 0.0)
-    tie = abs(csum[k] - target) < NEAR_TIE_EPS * total or \
-        (k > 0 and abs(csum[k - 1] - target) < NEAR_TIE_EPS * total)
-    return kept / kept.sum(), bool(tie)
+    variants, tie = nucleus_variants(prob, top_p)
+    return variants[0], tie
 
 
-def inverse_cdf(r: np.ndarray, u: float):
+def inverse_cdf_variants(r: np.ndarray, u: float):
     """Smallest v whose running sum (ascending v) exceeds u * sum(r); if
-    rounding leaves none, the last v with r[v] > 0.  Also reports whether the
-    threshold falls within NEAR_TIE_EPS * sum(r) of the chosen bin's edges."""
+    rounding leaves none, the last v with r[v] > 0 (first entry of the list).
+    When the threshold falls within NEAR_TIE_EPS * sum(r) of that bin's lower
+    edge, the previous bin with mass follows; within it of the upper edge, the
+    next one.  Also returns whether the draw is a near tie."""
     total = float(r.sum())
     thr = u * total
     csum = np.cumsum(r)
@@ -143,20 +173,146 @@ def inverse_cdf(r: np.ndarray, u: float):
     else:
         v = int(np.nonzero(r > 0)[0][-1])
     lo_edge = float(csum[v - 1]) if v > 0 else 0.0
-    tie = abs(float(csum[v]) - thr) < NEAR_TIE_EPS * total or \
-        (v > 0 and abs(lo_edge - thr) < NEAR_TIE_EPS * total)
-    return v, bool(tie)
+    near_hi = abs(float(csum[v]) - thr) < NEAR_TIE_EPS * total
+    near_lo = v > 0 and abs(lo_edge - thr) < NEAR_TIE_EPS * total
+    out = [v]
+    if near_lo:
+        before = np.nonzero(r[:v] > 0)[0]
+        if len(before):
+            out.append(int(before[-1]))
+    if near_hi:
+        after = np.nonzero(r[v + 1:] > 0)[0]
+        if len(after):
+            out.append(v + 1 + int(after[0]))
+    return out, bool(near_hi or near_lo)
+
+
+def inverse_cdf(r: np.ndarray, u: float):
+    """Smallest v whose running sum (ascending v) exceeds u * sum(r); if
+    rounding leaves none, the last v with r[v] > 0.  Also reports whether the
+    threshold falls within NEAR_TIE_EPS * sum(r) of the chosen bin's edges."""
+    variants, tie = inverse_cdf_variants(r, u)
+    return variants[0], tie
+
+
+class _Choices:
+    """The decisions a walk takes at its near ties.  The k-th near tie met
+    takes option script[k] (0 = the exact rule's own decision) when the
+    script reaches that far, else option 0; the number of options of every
+    tie met is recorded, so that all combinations can be enumerated."""
+
+    def __init__(self, script=()):
+        self.script = list(script)
+        self.options = []
+
+    def pick(self, n_options: int) -> int:
+        k = len(self.options)
+        self.options.append(int(n_options))
+        return self.script[k] if k < len(self.script) else 0
+
+
+def _stochastic_walk(b, lo, hi, parent, tokens, V, target_dist, draft_dist, uniforms,
+                     max_depth, choices):
+    """Rejection sampling down request b's tree (nodes lo..hi-1).
+
+    target_dist(t) / draft_dist(t) return the list of the row's possible
+    distributions (first entry: the exact one; more only at a near-tie nucleus
+    cut).  Every near tie consults ``choices``.  Returns the walk's outcome."""
+    par = [int(x) for x in parent[lo:hi]]
+    path = [0]
+    u = 0
+    tally = dict(near_ties=0, nucleus_ties=0, mass_ties=0, comparison_ties=0, bonus_tie=False)
+
+    def dist(fn, t):
+        variants = fn(t)
+        if len(variants) > 1:
+            tally["nucleus_ties"] += 1
+            return variants[choices.pick(len(variants))]
+        return variants[0]
+
+    r = dist(target_dist, lo)
+    overflow = False
+    while True:
+        kids = children_of(par, u)
+        q_u = dist(draft_dist, lo + u) if kids else None
+        accepted = None
+        for c in kids:
+            x = int(tokens[lo + c])
+            u_acc, _ = uniforms(b, c)
+            lhs = u_acc * q_u[x]
+            rhs = r[x]
+            take = lhs < rhs
+            if abs(rhs - lhs) < NEAR_TIE_EPS:            # decided by rounding either way
+                tally["near_ties"] += 1
+                tally["comparison_ties"] += 1
+                if choices.pick(2):
+                    take = not take
+            if take:
+                accepted = c
+                break
+            # r <- max(0, r - q_u) renormalised; with no mass left r stays as it was
+            resid = np.maximum(0.0, r - q_u)
+            mass = resid.sum()
+            renorm = mass > 0.0
+            if 0.0 < mass <= 2 * NEAR_TIE_EPS:           # no mass up to rounding
+                tally["mass_ties"] += 1
+                if choices.pick(2):
+                    renorm = False
+            if renorm:
+                r = resid / mass
+        if accepted is None:
+            break
+        if len(path) - 1 == max_depth:
+            overflow = True
+            break
+        path.append(accepted)
+        u = accepted
+        r = dist(target_dist, lo + u)
+    L = len(path) - 1
+    out_tokens = [int(tokens[lo + c]) for c in path[1:]]
+    if overflow:
+        out_tokens.append(-1)
+    else:
+        _, u_smp = uniforms(b, u)
+        variants, tie = inverse_cdf_variants(r, u_smp)
+        tally["bonus_tie"] = tie
+        tally["near_ties"] += int(tie)
+        out_tokens.append(variants[choices.pick(len(variants))] if len(variants) > 1
+                          else variants[0])
+    return dict(accept_len=L, accept_nodes=path, out_tokens=out_tokens, overflow=overflow,
+                **tally)
+
+
+def _stochastic_setup(node_off, parent, tokens, target_logits, draft_logits, V, temperature,
+                      seed, offset, uniforms, top_p, draft_probs):
+    if uniforms is None:
+        def uniforms(req, node):
+            return uniforms_for_node(seed, offset, req, node)
+    status = _input_status(node_off, parent, tokens, V, [target_logits, draft_logits])
+    if draft_probs:
+        for t in range(int(node_off[-1])):
+            row = np.asarray(draft_logits[t], dtype=np.float64)
+            if np.any(row < 0) or not row.sum() > 0:
+                status |= STATUS_NONFINITE
+
+    def target_dist(t):
+        return nucleus_variants(softmax_with_temperature(target_logits[t], temperature), top_p)[0]
+
+    def draft_dist(t):
+        if draft_probs:
+            row = np.asarray(draft_logits[t], dtype=np.float64)
+            row = row / row.sum()
+        else:
+            row = softmax_with_temperature(draft_logits[t], temperature)
+        return nucleus_variants(row, top_p)[0]
+
+    return uniforms, status, target_dist, draft_dist
 
 
 def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: int,
                       temperature: float, seed: int, offset: int, max_depth: int,
-                      follow=None, uniforms=None, top_p: float = 1.0, draft_probs: bool = False):
-    """Multi-step rejection sampling down the tree.
-
-    ``follow`` (optional) maps request -> accepted path observed elsewhere.  The
-    walk then takes that path's decision wherever it differs from its own and
-    records the difference in ``divergences`` with whether its own comparison
-    was a near tie (|r[x] - u*q[x]| < 1e-6).
+                      uniforms=None, top_p: float = 1.0, draft_probs: bool = False):
+    """Multi-step rejection sampling down the tree, by the exact rule.
 
     ``uniforms`` (optional) replaces the Philox draws: a callable
     (request, local_node) -> (u_acc, u_smp), for hand-worked examples.
@@ -165,102 +321,76 @@ def verify_stochastic(node_off, parent, tokens, target_logits, draft_logits, V: 
     draft_logits as probabilities (rows of q as given).
 
     Returns dict(accept_len, accept_nodes, out_tokens, near_ties [B], status,
-    divergences [B] (list of (node, child, near_tie)), bonus_tie [B],
-    nucleus_ties [B] (near-tie nucleus cuts met on the walk), mass_ties [B]
-    (residual masses within 2e-6 of zero after a rejection, where the
-    no-mass rule below is decided by rounding)).
+    bonus_tie [B], nucleus_ties [B] (near-tie nucleus cuts met on the walk),
+    mass_ties [B] (residual masses in (0, 2e-6] after a rejection, which the
+    exact rule renormalises but which rounding could have left at zero)).
     """
     B = len(node_off) - 1
-    if uniforms is None:
-        def uniforms(req, node):
-            return uniforms_for_node(seed, offset, req, node)
-    status = _input_status(node_off, parent, tokens, V, [target_logits, draft_logits])
+    uniforms, status, target_dist, draft_dist = _stochastic_setup(
+        node_off, parent, tokens, target_logits, draft_logits, V, temperature, seed, offset,
+        uniforms, top_p, draft_probs)
     accept_len = np.zeros(B, dtype=np.int32)
     accept_nodes = np.full((B, max_depth + 1), -1, dtype=np.int32)
     out_tokens = np.full((B, max_depth + 2), -1, dtype=np.int32)
     near_ties = np.zeros(B, dtype=np.int32)
-    divergences = [[] for _ in range(B)]
     bonus_tie = np.zeros(B, dtype=bool)
     nucleus_ties = np.zeros(B, dtype=np.int32)
     mass_ties = np.zeros(B, dtype=np.int32)
-    if draft_probs:
-        T = int(node_off[-1])
-        for t in range(T):
-            row = np.asarray(draft_logits[t], dtype=np.float64)
-            if np.any(row < 0) or not row.sum() > 0:
-                status |= STATUS_NONFINITE
-
-    def target_dist(b, t):
-        d, tie = nucleus(softmax_with_temperature(target_logits[t], temperature), top_p)
-        nucleus_ties[b] += int(tie)
-        return d
-
-    def draft_dist(b, t):
-        if draft_probs:
-            row = np.asarray(draft_logits[t], dtype=np.float64)
-            row = row / row.sum()
-        else:
-            row = softmax_with_temperature(draft_logits[t], temperature)
-        d, tie = nucleus(row, top_p)
-        nucleus_ties[b] += int(tie)
-        return d
-
     for b in range(B):
         lo, hi = int(node_off[b]), int(node_off[b + 1])
-        par = [int(x) for x in parent[lo:hi]]
-        path = [0]
-        u = 0
-        r = target_dist(b, lo)
-        overflow = False
-        forced = None if follow is None else [int(x) for x in follow[b]]
-        while True:
-            kids = children_of(par, u)
-            q_u = draft_dist(b, lo + u) if kids else None
-            accepted = None
-            for c in kids:
-                x = int(tokens[lo + c])
-                u_acc, _ = uniforms(b, c)
-                lhs = u_acc * q_u[x]
-                rhs = r[x]
-                tie = abs(rhs - lhs) < NEAR_TIE_EPS
-                near_ties[b] += int(tie)
-                take = lhs < rhs
-                if forced is not None:
-                    k = len(path)
-                    want = k < len(forced) and forced[k] == c
-                    if want != take:
-                        divergences[b].append((u, c, bool(tie)))
-                        take = want
-                if take:
-                    accepted = c
-                    break
-                resid = np.maximum(0.0, r - q_u)
-                mass = resid.sum()
-                if mass > NEAR_TIE_EPS:
-                    r = resid / mass
-                if 0.0 < mass <= 2 * NEAR_TIE_EPS:
-                    mass_ties[b] += 1
-            if accepted is None:
-                break
-            if len(path) - 1 == max_depth:
-                overflow = True
-                break
-            path.append(accepted)
-            u = accepted
-            r = target_dist(b, lo + u)
-        L = len(path) - 1
+        w = _stochastic_walk(b, lo, hi, parent, tokens, V, target_dist, draft_dist, uniforms,
+                             max_depth, _Choices())
+        L = w["accept_len"]
         accept_len[b] = L
-        accept_nodes[b, :L + 1] = path
-        out_tokens[b, :L] = [int(tokens[lo + c]) for c in path[1:]]
-        if overflow:
+        accept_nodes[b, :L + 1] = w["accept_nodes"]
+        out_tokens[b, :L + 1] = w["out_tokens"]
+        near_ties[b] = w["near_ties"]
+        bonus_tie[b] = w["bonus_tie"]
+        nucleus_ties[b] = w["nucleus_ties"]
+        mass_ties[b] = w["mass_ties"]
+        if w["overflow"]:
             status |= STATUS_PATH_OVERFLOW
-            out_tokens[b, L] = -1
-        else:
-            _, u_smp = uniforms(b, u)
-            v, tie = inverse_cdf(r, u_smp)
-            out_tokens[b, L] = v
-            bonus_tie[b] = tie
-            near_ties[b] += int(tie)
     return dict(accept_len=accept_len, accept_nodes=accept_nodes, out_tokens=out_tokens,
-                near_ties=near_ties, status=status, divergences=divergences,
-                bonus_tie=bonus_tie, nucleus_ties=nucleus_ties, mass_ties=mass_ties)
+                near_ties=near_ties, status=status, bonus_tie=bonus_tie,
+                nucleus_ties=nucleus_ties, mass_ties=mass_ties)
+
+
+def stochastic_outcomes(node_off, parent, tokens, target_logits, draft_logits, V: int,
+                        temperature: float, seed: int, offset: int, max_depth: int,
+                        uniforms=None, top_p: float = 1.0, draft_probs: bool = False,
+                        limit: int = 256):
+    """Every outcome of the walk of each request when each near tie it meets
+    may go either way: a comparison within NEAR_TIE_EPS (accept or reject), a
+    residual mass in (0, 2e-6] (renormalised or none), a nucleus cut near top_p
+    (one rank smaller or larger) and a draw on a bin edge (the neighbouring
+    bin).  Between ties every decision is the exact rule's.
+
+    Returns a list over requests; entry b is a list of dicts (accept_len,
+    accept_nodes, out_tokens, near_ties, ties_flipped), the first being the
+    exact rule's own outcome (ties_flipped 0).  At most ``limit`` outcomes per
+    request are enumerated (more raises)."""
+    B = len(node_off) - 1
+    uniforms, _, target_dist, draft_dist = _stochastic_setup(
+        node_off, parent, tokens, target_logits, draft_logits, V, temperature, seed, offset,
+        uniforms, top_p, draft_probs)
+    result = []
+    for b in range(B):
+        lo, hi = int(node_off[b]), int(node_off[b + 1])
+        outs = []
+        pending = [[]]
+        while pending:
+            script = pending.pop()
+            ch = _Choices(script)
+            w = _stochastic_walk(b, lo, hi, parent, tokens, V, target_dist, draft_dist,
+                                 uniforms, max_depth, ch)
+            outs.append(dict(accept_len=w["accept_len"], accept_nodes=list(w["accept_nodes"]),
+                             out_tokens=list(w["out_tokens"]), near_ties=w["near_ties"],
+                             ties_flipped=sum(1 for s in script if s)))
+            if len(outs) > limit:
+                raise RuntimeError(f"request {b}: more than {limit} near-tie outcomes")
+            # every later tie (beyond the script) may take each of its other options
+            for k in range(len(script), len(ch.options)):
+                for opt in range(1, ch.options[k]):
+                    pending.append(script + [0] * (k - len(script)) + [opt])
+        result.append(outs)
+    return result

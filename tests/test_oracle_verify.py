@@ -280,21 +280,84 @@ def test_one_hot_target_reduces_to_greedy(seed):
         assert np.array_equal(st[k], gr[k]), k
 
 
-def test_follow_mode_records_divergences():
-    wl = make_workload("stochastic_chain", 0)
-    sl = slice(0, int(wl.node_off[2]))
-    args = (wl.node_off[:3], wl.parent[sl], wl.tokens[sl], wl.logits[sl], wl.draft_logits[sl],
-            wl.V, wl.temperature, wl.rng_seed, wl.rng_offset, wl.max_depth)
-    own = oracle.verify_stochastic(*args)
-    same = oracle.verify_stochastic(*args, follow=[own["accept_nodes"][b][own["accept_nodes"][b] >= 0]
-                                                   for b in range(2)])
-    assert all(len(d) == 0 for d in same["divergences"])
-    assert np.array_equal(same["out_tokens"], own["out_tokens"])
-    other = [[0, 1, 2, 3, 4, 5], [0, 1, 2, 3, 4, 5]]
-    forced = oracle.verify_stochastic(*args, follow=other)
-    assert forced["accept_nodes"][:, :6].tolist() == other
-    changed = [b for b in range(2) if int(own["accept_len"][b]) != 5]
-    assert all(len(forced["divergences"][b]) >= 1 for b in changed)
+def test_outcomes_without_ties_are_the_exact_walk():
+    """On the named stochastic workloads (no near ties at seed 0) the tie
+    enumeration yields one outcome per request: the exact rule's."""
+    for name in ("stochastic_chain", "stochastic_tree"):
+        wl = make_workload(name, 0)
+        sl = slice(0, int(wl.node_off[4]))
+        args = (wl.node_off[:5], wl.parent[sl], wl.tokens[sl], wl.logits[sl],
+                wl.draft_logits[sl], wl.V, wl.temperature, wl.rng_seed, wl.rng_offset,
+                wl.max_depth)
+        own = oracle.verify_stochastic(*args)
+        outs = oracle.stochastic_outcomes(*args)
+        for b in range(4):
+            first = outs[b][0]
+            L = int(own["accept_len"][b])
+            assert first["ties_flipped"] == 0
+            assert first["accept_len"] == L
+            assert first["accept_nodes"] == own["accept_nodes"][b, :L + 1].tolist()
+            assert first["out_tokens"] == own["out_tokens"][b, :L + 1].tolist()
+            assert first["near_ties"] == int(own["near_ties"][b])
+            ties = own["near_ties"][b] + own["mass_ties"][b] + own["nucleus_ties"][b]
+            assert len(outs[b]) == 1 or ties > 0
+
+
+def _one_node(p, q, tokens, uni, top_p=1.0):
+    """A root whose children carry `tokens`, target probabilities p (as
+    logits, T = 1) and draft probabilities q, with the given uniforms."""
+    n = len(tokens) + 1
+    parent = np.array([-1] + [0] * (n - 1), np.int32)
+    tok = np.array([0] + list(tokens), np.int32)
+    tl = np.log(np.array([p] * n, np.float64))
+    dl = np.array([q] * n, np.float64)
+    args = (np.array([0, n]), parent, tok, tl, dl, len(p), 1.0, 0, 0, 2)
+    kw = dict(uniforms=lambda b, i: uni[i], draft_probs=True, top_p=top_p)
+    return oracle.verify_stochastic(*args, **kw), oracle.stochastic_outcomes(*args, **kw)[0]
+
+
+def test_outcomes_comparison_tie_takes_both_decisions():
+    """u q[x] within 1e-7 below r[x]: the exact rule accepts child 1; the
+    other decision rejects it, leaves r = max(0, p - q)/0.1 = (1, 0), rejects
+    child 2 (token 1, r = 0) and draws token 0 from (1, 0)."""
+    p, q = [0.6, 0.4], [0.5, 0.5]
+    uni = {1: ((0.6 - 1e-7) / 0.5, 0.3), 2: (0.2, 0.3), 0: (0.5, 0.7)}
+    res, outs = _one_node(p, q, [0, 1], uni)
+    assert res["accept_nodes"][0, :2].tolist() == [0, 1]
+    got = {(o["accept_len"], tuple(o["out_tokens"])) for o in outs}
+    assert (1, (0, int(res["out_tokens"][0, 1]))) in got
+    assert (0, (0,)) in got
+    assert outs[0]["ties_flipped"] == 0 and outs[0]["near_ties"] >= 1
+
+
+def test_outcomes_draw_on_a_bin_edge_takes_both_bins():
+    """A leaf root with r = (0.5, 0.5) and u_smp 1e-7 above one half: the
+    threshold passes bin 0's upper edge by 1e-7, so token 1 is drawn and
+    token 0 is the other outcome."""
+    parent = np.array([-1], np.int32)
+    tl = np.log(np.array([[0.5, 0.5]]))
+    args = (np.array([0, 1]), parent, np.array([0], np.int32), tl, tl, 2, 1.0, 0, 0, 2)
+    kw = dict(uniforms=lambda b, i: (0.5, 0.5 + 1e-7))
+    res = oracle.verify_stochastic(*args, **kw)
+    outs = oracle.stochastic_outcomes(*args, **kw)[0]
+    assert res["out_tokens"][0, 0] == 1 and res["bonus_tie"][0]
+    assert sorted(o["out_tokens"][0] for o in outs) == [0, 1]
+
+
+def test_outcomes_nucleus_tie_takes_both_cuts():
+    """Sorted target (0.5, 0.3, 0.2) with top_p 0.8 + 1e-8: the running sum
+    0.8 sits at the cut, so the nucleus holds three tokens by the exact rule
+    and two (0.625, 0.375) by the other rounding.  A leaf root with
+    u_smp = 0.9 draws token 2 from the three-token nucleus and token 1 from
+    the two-token one."""
+    parent = np.array([-1], np.int32)
+    tl = np.log(np.array([[0.5, 0.3, 0.2]]))
+    args = (np.array([0, 1]), parent, np.array([0], np.int32), tl, tl, 3, 1.0, 0, 0, 2)
+    kw = dict(uniforms=lambda b, i: (0.5, 0.9), top_p=0.8 + 1e-8)
+    res = oracle.verify_stochastic(*args, **kw)
+    outs = oracle.stochastic_outcomes(*args, **kw)[0]
+    assert res["nucleus_ties"][0] == 1 and res["out_tokens"][0, 0] == 2
+    assert sorted(o["out_tokens"][0] for o in outs) == [1, 2]
 
 
 # ---------------------------------------------------------------- nucleus and draft probabilities
@@ -314,8 +377,16 @@ def test_nucleus_hand_worked():
     # tokens as likely as the last one needed are all kept
     d, _ = oracle.nucleus(np.array([0.4, 0.2, 0.2, 0.2]), 0.5)
     np.testing.assert_allclose(d, [0.4, 0.2, 0.2, 0.2], atol=1e-15)
-    _, tie = oracle.nucleus(np.array([0.5, 0.25, 0.25]), 0.75)   # the cut lands on 0.75
-    assert tie
+    # the cut lands on 0.75: the two-token set holds exactly top_p, and the
+    # three-token set is what a rounding of that sum below 0.75 would keep
+    vs, tie = oracle.nucleus_variants(np.array([0.5, 0.25, 0.2, 0.05]), 0.75)
+    assert tie and len(vs) == 2
+    np.testing.assert_allclose(vs[0], [0.5 / 0.75, 0.25 / 0.75, 0.0, 0.0], atol=1e-15)
+    np.testing.assert_allclose(vs[1], [0.5 / 0.95, 0.25 / 0.95, 0.2 / 0.95, 0.0], atol=1e-15)
+    # a level of equal tokens is kept or dropped whole: with (0.5, 0.25, 0.25)
+    # the sets are {0.5} (0.5) and everything (1.0), neither near 0.75
+    vs, tie = oracle.nucleus_variants(np.array([0.5, 0.25, 0.25]), 0.75)
+    assert not tie and len(vs) == 1
 
 
 def test_draft_probabilities_equal_draft_logits():
@@ -395,25 +466,48 @@ def test_tiny_nucleus_reduces_to_greedy(seed):
         assert np.array_equal(st[k], gr[k]), k
 
 
-def test_rounding_residue_is_no_residual_mass():
-    """After a rejection a residual of at most 1e-6 is kept as no mass: r
-    stays as it was (and a mass that small is reported as a near tie)."""
+def test_residual_mass_rule_is_exact():
+    """After a rejection the residual max(0, r - q) is renormalised whenever
+    it has any mass, however small (the explainer §2.2 residual: anything
+    else changes the output distribution), and r is kept only when that mass
+    is exactly 0.  Masses in (0, 2e-6] are reported as mass ties."""
     V = 2
     parent = np.array([-1, 0, 0], np.int32)
+    # equal one-hot rows: child 1 (token 1, q = 0) is rejected and leaves no
+    # residual at all (p <= q everywhere), so r stays p and child 2 (token 0)
+    # is accepted
     uni = {1: (0.999, 0.5), 2: (0.9, 0.5), 0: (0.5, 0.5)}
-    # equal one-token rows: child 1 (token 1) is rejected, child 2 (token 0) accepted
     tl = np.array([[0.0, -1000.0]] * 3, np.float32)     # exp(-1000) is 0 in fp64
     res = oracle.verify_stochastic(np.array([0, 3]), parent, np.array([0, 1, 0], np.int32), tl,
                                    tl, V, 1.0, 0, 0, 2, uniforms=lambda b, i: uni[i])
     assert res["accept_nodes"][0, :2].tolist() == [0, 2]
-    # p exceeds q by 5e-7 on token 0: after child 1 (token 1) is rejected that
-    # residue is not a distribution, r stays p, and child 2 (token 1) is
-    # accepted (renormalising the residue would have put all of r on token 0)
-    p = np.log(np.array([[0.5 + 5e-7, 0.5 - 5e-7]] * 3))
-    q = np.array([[0.5, 0.5]] * 3)
-    uni = {1: (0.9999999, 0.5), 2: (0.9, 0.5), 0: (0.5, 0.5)}
-    res = oracle.verify_stochastic(np.array([0, 3]), parent, np.array([0, 1, 1], np.int32), p, q,
-                                   V, 1.0, 0, 0, 2, uniforms=lambda b, i: uni[i],
-                                   draft_probs=True)
-    assert res["accept_nodes"][0, :2].tolist() == [0, 2]
+    assert int(res["mass_ties"][0]) == 0
+    # p exceeds q by 5e-7 on token 0.  Child 1 (token 1): u q = 0.49999995 is
+    # not below r = 0.4999995, rejected; the residual (5e-7, 0) is
+    # renormalised to (1, 0).  Child 2 (token 1): r = 0, rejected; the
+    # residual of (1, 0) against q is (0.5, 0) -> (1, 0); the draw gives 0.
+    res, outs = _one_node([0.5 + 5e-7, 0.5 - 5e-7], [0.5, 0.5], [1, 1],
+                          {1: (0.9999999, 0.5), 2: (0.9, 0.5), 0: (0.5, 0.5)})
+    assert int(res["accept_len"][0]) == 0
+    assert res["out_tokens"][0, 0] == 0
     assert int(res["mass_ties"][0]) == 1
+    # keeping r instead (what rounding to no mass would do) accepts child 2
+    assert {(o["accept_len"], tuple(o["out_tokens"])) for o in outs} == {(0, (0,)), (1, (1, 0)),
+                                                                          (1, (1, 1))}
+
+
+def test_residual_mass_is_relative_to_the_current_residual():
+    """Two rejections at one node.  p = (.6000605, .3960395, .0039) and
+    q = (.6, .396, .004), both children token 2, u_acc .999999, u_smp .9.
+    Child 1: u q = .003999996 > .0039, rejected; residual (6.05e-5, 3.95e-5, 0)
+    of mass 1e-4 -> r = (.605, .395, 0).  Child 2: r = 0, rejected; residual
+    max(0, r - q) = (.005, 0, 0) of mass .005 (of r) -> (1, 0, 0); the draw
+    gives token 0.  As a fraction of p that second mass is only 5e-7, which
+    must not count as none."""
+    p = [0.6000605, 0.3960395, 0.0039]
+    q = [0.6, 0.396, 0.004]
+    res, outs = _one_node(p, q, [2, 2], {1: (0.999999, 0.9), 2: (0.999999, 0.9), 0: (0.5, 0.9)})
+    assert int(res["accept_len"][0]) == 0
+    assert res["out_tokens"][0, 0] == 0
+    assert int(res["mass_ties"][0]) == 0 and int(res["near_ties"][0]) == 0
+    assert len(outs) == 1
