@@ -68,11 +68,14 @@ def tree_attention(q, k_cache, v_cache, dtype, Hq, Hkv, node_off, parent, prefix
         P = int(prefix_len[b])
         n = hi - lo
         mask = request_mask([int(x) for x in parent[lo:hi]], P)[[t - lo for t in rows]]
+        kv = {}
         for h in head_list:
             g = h // G
+            if g not in kv:                                            # decoded once per kv-head
+                kv = {g: (decode_values(k_cache[b, g, :P + n, :], dtype),      # [P+N, D]
+                          decode_values(v_cache[b, g, :P + n, :], dtype))}
+            K, Vv = kv[g]
             Q = decode_values(q[rows, h, :], dtype)                    # [r, D]
-            K = decode_values(k_cache[b, g, :P + n, :], dtype)         # [P+N, D]
-            Vv = decode_values(v_cache[b, g, :P + n, :], dtype)
             S = (Q @ K.T) * scale
             S = np.where(mask, S, -np.inf)
             mx = S.max(axis=1, keepdims=True)
