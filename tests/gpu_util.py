@@ -1,6 +1,7 @@
 """Helpers for the GPU parity tests: run the HIP path through the C ABI on a
 seeded workload and compare with the oracle on the same host bytes."""
 
+import contextlib
 import sys
 
 import numpy as np
@@ -9,6 +10,7 @@ import torch
 
 import oracle
 from token_tree_verification_st_amd import load_library, to_device
+from token_tree_verification_st_amd.binding import st_testing_set_plan
 from token_tree_verification_st_amd import step as stp
 
 BF16_TOL = 1e-2   # max-abs error, bf16 inputs with fp32 accumulation
@@ -19,6 +21,17 @@ def require_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     load_library()  # raises if libst.so is missing
+
+
+@contextlib.contextmanager
+def plan_override(**fields):
+    """Planner overrides (st_testing_plan fields) for the calls inside the
+    block, workspace queries included."""
+    st_testing_set_plan(fields)
+    try:
+        yield
+    finally:
+        st_testing_set_plan(None)
 
 
 def say(msg):
@@ -36,20 +49,6 @@ def gpu_mask(dw):
     W = dw.tree.W
     mask = dw.buf["mask"].cpu().numpy().view(np.uint64).reshape(dw.T, W)
     return mask, dw.buf["depth"].cpu().numpy()
-
-
-def sample_rows(wl, per_req=4, heads=3, seed=0):
-    """A few nodes per request (root, last, random) and a few q-heads."""
-    rng = np.random.default_rng(seed)
-    nodes = []
-    for b in range(wl.B):
-        lo, hi = int(wl.node_off[b]), int(wl.node_off[b + 1])
-        pick = {lo, hi - 1}
-        while len(pick) < min(per_req, hi - lo):
-            pick.add(int(rng.integers(lo, hi)))
-        nodes += sorted(pick)
-    hs = sorted({0, wl.Hq - 1} | {int(x) for x in rng.integers(0, wl.Hq, heads)})
-    return nodes, hs
 
 
 def attention_errors(wl, dw, nodes=None, heads=None, derive_mask=False):
@@ -80,3 +79,30 @@ def device_paths(dw):
     an = dw.buf["accept_nodes"].cpu().numpy()
     ot = dw.buf["out_tokens"].cpu().numpy()
     return al, an, ot
+
+
+def stochastic_parity(wl, dw, draft_host=None, top_p=1.0, probs=False, label=""):
+    """The GPU's stochastic acceptance (already run on dw) against the
+    oracle, request by request and exactly: accept_len, the accepted nodes,
+    the emitted tokens (bonus included), the -1 padding and the near-tie
+    count must equal one of the outcomes the oracle's walk can reach when the
+    near ties it meets go either way (the first outcome is the exact rule's;
+    every decision between ties is the exact rule's).  Returns how many
+    requests matched only an outcome with a tie decided the other way."""
+    al, an, ot = device_paths(dw)
+    ties_gpu = dw.buf["near_ties"].cpu().numpy()
+    draft = wl.draft_logits if draft_host is None else draft_host
+    outs = oracle.stochastic_outcomes(wl.node_off, wl.parent, wl.tokens, wl.logits, draft, wl.V,
+                                      wl.temperature, wl.rng_seed, wl.rng_offset, wl.max_depth,
+                                      top_p=top_p, draft_probs=probs)
+    followed = 0
+    for b in range(wl.B):
+        L = int(al[b])
+        assert (an[b, L + 1:] == -1).all() and (ot[b, L + 1:] == -1).all(), f"request {b}"
+        got = (L, an[b, :L + 1].tolist(), ot[b, :L + 1].tolist(), int(ties_gpu[b]))
+        match = [o for o in outs[b]
+                 if (o["accept_len"], o["accept_nodes"], o["out_tokens"], o["near_ties"]) == got]
+        assert match, (f"{label} request {b}: GPU (L, path, tokens, near ties) {got} is none of "
+                       f"the oracle's {[(o['accept_len'], o['accept_nodes'], o['out_tokens'], o['near_ties']) for o in outs[b]]}")
+        followed += min(o["ties_flipped"] for o in match) > 0
+    return followed

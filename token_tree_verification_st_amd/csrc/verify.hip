@@ -10,14 +10,17 @@
 // min(1, p/q), check left to right, resample from the residual at the first
 // rejection).  The residual after k rejected children of node u has a closed
 // form: r_k = max(0, p_u - c_k q_u) / D_k with c_0 = 0, D_0 = 1,
-// c_{k+1} = c_k + D_k and D_{k+1} = sum_v max(0, p_u - c_{k+1} q_u)
-// (unchanged when that sum is 0).  A first kernel reduces every logit row to
-// its softmax statistics (max, sum of exponentials), one workgroup per row;
-// with those, testing the first child of any node needs two logits only.  A
-// second kernel walks each request's tree with one workgroup: the children's
-// tests read precomputed values, and only the nodes where the walk rejects a
-// child or stops have their two rows read again, for the residual masses and
-// the inverse-CDF draw of the replacement token.
+// c_{k+1} = c_k + D_k and D_{k+1} = sum_v max(0, p_u - c_{k+1} q_u).  One
+// workgroup per node reads the node's target and draft rows once into
+// registers, reduces them to their softmax statistics and decides the node
+// as the walk would on reaching it: its children are tested in order (after
+// each rejection one residual-mass reduction), and where none is accepted
+// the replacement token is drawn from the final residual by inverse CDF.  A
+// rejection that leaves a residual mass of at most 1e-6 of the current one
+// (D_{k+1} <= 1e-6 D_k: the fp32 rounding residue of r <= q) keeps r as it
+// was.  The node's verdict (first accepted child, near ties, drawn token) is
+// 16 bytes; one wavefront per request then follows the verdicts from the
+// root.
 #include "step_internal.h"
 
 #include <float.h>
@@ -33,11 +36,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kTieEps = 1e-6;
-// A residual whose mass (as a fraction of the target row) is at most this is
-// taken to have none: where r and q agree, the fp32 terms max(0, P - c Q)
-// leave up to about 1e-7 of rounding residue, which must not be renormalised
-// into a distribution (a nucleus cut makes such agreement common: two
-// one-token nuclei on the same token).
+// A rejection whose residual mass, as a fraction of the current residual's
+// (D_{k+1} / D_k, the mass of max(0, r - q) for the normalised r), is at most
+// this leaves r as it was: where r <= q everywhere the exact mass is 0, and
+// the fp32 terms max(0, P - c Q) leave up to about 1e-7 of rounding residue,
+// which must not be renormalised into a distribution (a nucleus cut makes
+// such agreement common: two one-token nuclei on the same token).
 constexpr double kMassEps = 1e-6;
 
 // ---------------------------------------------------------------- reductions
@@ -502,7 +506,7 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
             (double)top_p * zd, fd ? -1.0 : zd, 0.0, kUnknown, 0};
   int set = 0;
   bool few = false;
-  while (rt.open() | rd.open()) {  // block-uniform
+  while (rt.open() || rd.open()) {  // block-uniform
     const uint32_t mt = rt.mid(), md = rd.mid();
     int nt = 0, nd = 0;
     double st = kept_sum<VEC, NPT>(P, __uint_as_float(mt), nt);
@@ -517,7 +521,7 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
     few = (!rt.open() || rt.between() <= kCutCand) && (!rd.open() || rd.between() <= kCutCand);
     if (few) break;
   }
-  if (few && (rt.open() | rd.open())) {
+  if (few && (rt.open() || rd.open())) {
     // gather the candidates: a thread's entries in [lo, hi), placed after
     // those of the threads before it (counts packed as in the search)
     const float lt = __uint_as_float(rt.lo), ht = __uint_as_float(rt.hi);
@@ -577,7 +581,7 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
         }
         if (__ballot(it) == 0ull) rt.hi = rt.lo + 1u;
         if (__ballot(id) == 0ull) rd.hi = rd.lo + 1u;
-        if (!(rt.open() | rd.open())) break;  // wave-uniform
+        if (!(rt.open() || rd.open())) break;  // wave-uniform
         const uint32_t mt = rt.mid(), md = rd.mid();
         const float ft = __uint_as_float(mt), fd = __uint_as_float(md);
         double gt = 0.0, gd = 0.0;
@@ -999,7 +1003,7 @@ stoch_node_kernel(StochArgs g) {
       const double cn = cc + D;
       const double Dn =
           a * block_sum<kNodeBlock>(resid_sum<VEC>(P, Q, (float)(cn * ratio)), s.red, k & 1);
-      if (Dn > kMassEps) {
+      if (Dn > kMassEps * D) {
         cc = cn;
         D = Dn;
       }
@@ -1008,7 +1012,7 @@ stoch_node_kernel(StochArgs g) {
     if (accepted < 0) {  // every child rejected: draw from the final residual
       const double total =
           draw_residual<VEC>(P, Q, (float)((cc + D) * ratio), s.u_draw, s.draw, token, tie);
-      if (!(total * a > kMassEps)) {  // the last rejection left no mass: r unchanged
+      if (!(total * a > kMassEps * D)) {  // the last rejection left no mass: r unchanged
         __syncthreads();
         draw_residual<VEC>(P, Q, (float)(cc * ratio), s.u_draw, s.draw, token, tie);
       }
