@@ -1,7 +1,6 @@
 """GPU parity: ancestor mask (bit-exact) and tree attention (max-abs error) of the
 HIP path against the oracle, through the C ABI."""
 
-import os
 
 import numpy as np
 import pytest
@@ -11,8 +10,9 @@ import oracle
 from synth import (build_workload, make_workload, tree_beam_plus_leaves, tree_chain,
                    tree_complete_binary, tree_random_attach)
 from token_tree_verification_st_amd import to_device
-from tests.gpu_util import BF16_TOL, F32_TOL, attention_errors, gpu_mask, require_gpu, \
-    sample_rows, say, status_of
+from tests.gpu_util import BF16_TOL, F32_TOL, attention_errors, gpu_mask, plan_override, \
+    require_gpu, \
+    say, status_of
 
 pytestmark = pytest.mark.gpu
 
@@ -93,11 +93,11 @@ def test_attention_bf16_small_full(seed, D, Hq, Hkv):
 
 
 @pytest.mark.parametrize("split_keys", [64, 128, 320])
-def test_attention_forced_splits_and_combine(split_keys, monkeypatch):
-    monkeypatch.setenv("ST_ATTN_SPLIT_KEYS", str(split_keys))
+def test_attention_forced_splits_and_combine(split_keys):
     for dtype in ("bf16", "f32"):
         wl = _small_case(10 + split_keys, dtype=dtype, D=64 if dtype == "f32" else 128)
-        err, lerr = attention_errors(wl, to_device(wl))
+        with plan_override(attn_split_keys=split_keys):
+            err, lerr = attention_errors(wl, to_device(wl))
         say(f"split {split_keys} {dtype}: max-abs {err:.2e} lse {lerr:.2e}")
         tol = F32_TOL if dtype == "f32" else BF16_TOL
         assert err <= tol and lerr <= (F32_TOL if dtype == "f32" else 1e-3)
@@ -108,18 +108,18 @@ def test_attention_forced_splits_and_combine(split_keys, monkeypatch):
 # workgroups per CU: (2,2) (4,2) for shapes 5, 6
 @pytest.mark.parametrize("derive", [False, True])
 @pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6])
-def test_attention_every_kernel_shape(shape, derive, monkeypatch):
+def test_attention_every_kernel_shape(shape, derive):
     """derive: no mask is passed, the kernel builds it from the parent array."""
-    monkeypatch.setenv("ST_ATTN_SHAPE", str(shape))
     for i, (D, Hq, Hkv, nmax) in enumerate([(128, 4, 4, 90), (64, 6, 3, 40), (128, 16, 2, 25)]):
         wl = _small_case(70 + i, D=D, Hq=Hq, Hkv=Hkv, nmax=nmax)
-        err, lerr = attention_errors(wl, to_device(wl), derive_mask=derive)
+        with plan_override(attn_shape=shape):
+            err, lerr = attention_errors(wl, to_device(wl), derive_mask=derive)
         say(f"shape {shape} D {D} Hq {Hq} Hkv {Hkv}: max-abs {err:.2e} lse {lerr:.2e}")
         assert err <= BF16_TOL and lerr <= 1e-3
     # forced short splits: some key groups get no chunk, tails are partial chunks
-    monkeypatch.setenv("ST_ATTN_SPLIT_KEYS", "80")
     wl = _small_case(79, D=128, Hq=8, Hkv=2, nmax=70)
-    err, lerr = attention_errors(wl, to_device(wl), derive_mask=derive)
+    with plan_override(attn_shape=shape, attn_split_keys=80):
+        err, lerr = attention_errors(wl, to_device(wl), derive_mask=derive)
     say(f"shape {shape} split 80: max-abs {err:.2e} lse {lerr:.2e}")
     assert err <= BF16_TOL and lerr <= 1e-3
 
@@ -158,16 +158,16 @@ def test_attention_derived_mask_bad_parent_sets_status():
         assert status_of(dw) & 1
 
 
-def test_attention_workspace_reused_across_calls(monkeypatch):
+def test_attention_workspace_reused_across_calls():
     """One workspace serves calls with different trees and split counts."""
     ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
-    for i, sk in enumerate(["96", "64", "200", "96"]):
-        monkeypatch.setenv("ST_ATTN_SPLIT_KEYS", sk)
+    for i, sk in enumerate([96, 64, 200, 96]):
         wl = _small_case(90 + i, D=128, Hq=4, Hkv=2, nmax=60)
         dw = to_device(wl)
         dw.buf["attn_ws"] = ws
         for _ in range(2):
-            err, lerr = attention_errors(wl, dw)
+            with plan_override(attn_split_keys=sk):
+                err, lerr = attention_errors(wl, dw)
             assert err <= BF16_TOL and lerr <= 1e-3
         assert status_of(dw) == 0
 
@@ -210,12 +210,13 @@ def test_attention_bad_prefix_sets_status():
 
 @pytest.mark.parametrize("name", ["llama7b", "ragged_batch", "llama70b_gqa", "stochastic_tree",
                                   "stochastic_chain"])
-def test_attention_full_size_sampled_rows(name):
+def test_attention_full_size_every_row(name):
+    """Every (node, q-head) of the named workloads at full size, in the launch
+    configuration the benchmark times, against the oracle."""
     wl = make_workload(name, 0)
-    nodes, heads = sample_rows(wl)
-    err, lerr = attention_errors(wl, to_device(wl), nodes=nodes, heads=heads,
+    err, lerr = attention_errors(wl, to_device(wl),
                                  derive_mask=name in ("llama7b", "stochastic_tree"))
-    say(f"{name}: {len(nodes)} nodes x {len(heads)} heads, max-abs {err:.2e} lse {lerr:.2e}")
+    say(f"{name}: all {wl.T} nodes x {wl.Hq} heads, max-abs {err:.2e} lse {lerr:.2e}")
     assert err <= BF16_TOL and lerr <= 1e-3
 
 

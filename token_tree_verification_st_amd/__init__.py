@@ -39,7 +39,7 @@ from .binding import (  # noqa: F401
     st_verify_greedy_workspace,
     st_verify_stochastic,
     st_verify_stochastic_ex,
-    candidate_length,
     st_verify_stochastic_workspace,
 )
 from .device_io import DeviceWorkload, to_device  # noqa: F401
+from .policy import candidate_length  # noqa: F401

@@ -53,6 +53,13 @@ class StStep(ctypes.Structure):
     ]
 
 
+class StTestingPlan(ctypes.Structure):
+    """Mirror of st_testing_plan (include/st_testing.h)."""
+    _fields_ = [("attn_shape", ctypes.c_int32), ("attn_target_wg", ctypes.c_int32),
+                ("attn_split_keys", ctypes.c_int32), ("linear_ksplit", ctypes.c_int32),
+                ("linear_stages", ctypes.c_int32)]
+
+
 _lib = None
 _c = ctypes
 
@@ -90,6 +97,7 @@ def _declare(lib):
         "st_stream_read": (I, [P, S, P, I, P]),
         "st_verification_step_paged": (I, [TP, _c.POINTER(StStep), I, I, P, I, P, S, P, P]),
         "st_verification_step_ex": (I, [TP, _c.POINTER(StStep), I, _c.c_float, P, S, P, P]),
+        "st_testing_set_plan": (I, [_c.POINTER(StTestingPlan)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -357,15 +365,6 @@ def st_stream_read(src: torch.Tensor, sink: torch.Tensor):
                                          sink.numel(), _stream()), "st_stream_read")
 
 
-def candidate_length(t: int, T_est: int, K_max: int) -> int:
-    """Draft length for the next step (explainer §3.3, dynamic candidate
-    length): K_t = max(1, round(K_max * (1 - t / T_est))) for t tokens
-    generated out of an estimated T_est.  Host policy; rounds half to even."""
-    if T_est <= 0 or K_max < 1:
-        raise ValueError("T_est must be positive and K_max at least 1")
-    return max(1, int(round(K_max * (1.0 - t / T_est))))
-
-
 def st_kv_compact_paged(k_pool, v_pool, block_table, prefix_len, accept_len, accept_nodes,
                         src_slot, new_len, status=None):
     """st_kv_compact on a paged pool [n_blocks][Hkv][block][D] (updated in
@@ -576,3 +575,16 @@ def st_linear(x, w, y, residual=None, workspace=None):
 
 def st_status_str(code: int) -> str:
     return load_library().st_status_str(code).decode()
+
+
+def st_testing_set_plan(plan: Optional[dict]):
+    """Test-only (include/st_testing.h): install planner overrides for every
+    later call in the process, given as st_testing_plan fields; None restores
+    the planners' own choices."""
+    if plan is None:
+        _check(load_library().st_testing_set_plan(None), "st_testing_set_plan")
+        return
+    p = StTestingPlan(attn_shape=-1)
+    for k, v in plan.items():
+        setattr(p, k, int(v))
+    _check(load_library().st_testing_set_plan(ctypes.byref(p)), "st_testing_set_plan")

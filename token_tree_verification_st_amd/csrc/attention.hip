@@ -29,7 +29,6 @@
 #include "step_internal.h"
 
 #include <math.h>
-#include <stdlib.h>
 
 namespace {
 
@@ -1079,13 +1078,8 @@ struct Plan {
   size_t ml_bytes, ws_bytes;
 };
 
-int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  if (!s || !*s) return dflt;
-  return atoi(s);
-}
-
 int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_prefix, Plan& p) {
+  const st::TestingPlan& ovr = st::testing_plan();
   int rc = st::check_tree_host(t);
   if (rc) return rc;
   if (Hq < 1 || Hkv < 1 || max_prefix < 0) return ST_E_INVALID;
@@ -1114,7 +1108,7 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
     // wavefront, half the registers), whose softmax and MFMA phases overlap.
     if (rows_max > 64) p.rbw = 2;
     // 0..6: (1,1) (1,2) (1,4) (2,4) (4,4), then two workgroups per CU: (2,2) (4,2)
-    const int forced = env_int("ST_ATTN_SHAPE", -1);
+    const int forced = ovr.attn_shape;
     if (forced >= 0 && forced <= 6) {
       static const int kRwv[7] = {1, 1, 1, 2, 4, 2, 4}, kRbw[7] = {1, 2, 4, 4, 4, 2, 2};
       p.rwv = kRwv[forced];
@@ -1130,12 +1124,13 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
   // the streaming kernel, two for its two-per-CU shapes); splits are even, in
   // multiples of `gran` keys
   const bool two_per_cu = p.stream && p.rbw == 2 && p.rwv > 1;
-  const long target = env_int("ST_ATTN_TARGET_WG", !p.stream ? 512 : two_per_cu ? 512 : 256);
+  const long target =
+      ovr.attn_target_wg > 0 ? ovr.attn_target_wg : !p.stream ? 512 : two_per_cu ? 512 : 256;
   long ns = (target + base - 1) / base;
   if (ns < 1) ns = 1;
   long ks = (keys_max + ns - 1) / ns;
   ks = (ks + gran - 1) / gran * gran;
-  const int forced_ks = env_int("ST_ATTN_SPLIT_KEYS", 0);
+  const int forced_ks = ovr.attn_split_keys;
   if (forced_ks > 0) ks = (forced_ks + gran - 1) / gran * gran;
   const long kmax = (keys_max + gran - 1) / gran * gran;
   // the streaming kernel wants at least two chunks per wavefront; the fp32

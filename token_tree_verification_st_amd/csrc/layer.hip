@@ -22,7 +22,6 @@
 #include "st_internal.h"
 
 #include <math.h>
-#include <stdlib.h>
 
 namespace {
 
@@ -347,12 +346,6 @@ struct LinPlan {
   int mblk_rows, n_mblk, n_ntile, KSPLIT, KSL, items;
 };
 
-int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  if (!s || !*s) return dflt;
-  return atoi(s);
-}
-
 // Rows per workgroup 32 (M <= 32) or 64.  The reduction is split only when
 // one pass over the features and row blocks would leave more than a quarter of
 // the CUs idle: the smallest divisor of the stage count that fills 3/4 of
@@ -367,7 +360,7 @@ int linear_plan(int M, int N, int K, LinPlan& p) {
   const int nk = K / kKC;
   const int cus = st::device_cus();
   int ks = 1;
-  const int forced = env_int("ST_LINEAR_KSPLIT", 0);
+  const int forced = st::testing_plan().linear_ksplit;
   if (forced > 0 && nk % forced == 0) {
     ks = forced;
   } else {
@@ -470,7 +463,7 @@ extern "C" int st_linear(int M, int N, int K, const void* x, const void* w, cons
   const dim3 grid(8 * a.per_xcd);
   // 4 stages (64 KB of LDS at 64 rows: two workgroups per CU) measured
   // faster than 8 (one per CU) on the 7B-shaped projections
-  const bool deep = env_int("ST_LINEAR_STAGES", 4) == 8;
+  const bool deep = st::testing_plan().linear_stages == 8;
   if (p.mblk_rows == 32) {
     if (deep)
       hipLaunchKernelGGL((linear_kernel<2, 8>), grid, dim3(256), 0, (hipStream_t)stream, a);

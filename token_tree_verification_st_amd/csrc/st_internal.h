@@ -31,6 +31,14 @@ struct KvPaging {
   int bt_stride, lbs, n_blocks;
 };
 
+// Planner overrides installed by st_testing_set_plan (include/st_testing.h);
+// the defaults leave every choice to the planners.
+struct TestingPlan {
+  int attn_shape = -1, attn_target_wg = 0, attn_split_keys = 0;
+  int linear_ksplit = 0, linear_stages = 0;
+};
+const TestingPlan& testing_plan();
+
 inline int mask_words(int max_nodes) { return (max_nodes + 63) / 64; }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
