@@ -13,7 +13,7 @@ from synth import build_workload, make_paged, make_workload, tree_random_attach
 from token_tree_verification_st_amd import (st_kv_compact_paged, st_tree_attention_paged,
                                             to_device)
 from token_tree_verification_st_amd import step as stp
-from tests.gpu_util import BF16_TOL, F32_TOL, require_gpu, sample_rows, say
+from tests.gpu_util import BF16_TOL, F32_TOL, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -65,20 +65,17 @@ def test_paged_attention_equals_contiguous(name, bs, derive):
                        dw.buf["out"].view(torch.int16) if out.dtype == torch.bfloat16
                        else dw.buf["out"])
     assert torch.equal(lse, dw.buf["lse"])
-    if name == "llama70b_gqa":
-        return
-    # the oracle on the caches the pool and table describe
+    # the oracle on the caches the pool and table describe, every row
     kc = oracle.gather_paged(kp_h, bt_h, bs)[:, :, :wl.S_max]
     vc = oracle.gather_paged(vp_h, bt_h, bs)[:, :, :wl.S_max]
-    nodes, heads = (None, None) if wl.T * wl.Hq <= 4096 else sample_rows(wl)
     ref, ref_lse = oracle.tree_attention(wl.q, kc, vc, wl.dtype, wl.Hq, wl.Hkv, wl.node_off,
-                                         wl.parent, wl.prefix_len, nodes=nodes, heads=heads)
-    sel = ~np.isnan(ref_lse)
+                                         wl.parent, wl.prefix_len)
     got = out.float().cpu().numpy().astype(np.float64)
-    err = float(np.abs(got[sel] - ref[sel]).max())
+    err = float(np.abs(got - ref).max())
+    lerr = float(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse).max())
     tol = F32_TOL if wl.dtype == "f32" else BF16_TOL
-    say(f"  max-abs error {err:.2e}")
-    assert err <= tol
+    say(f"  every row: max-abs error {err:.2e}, lse {lerr:.2e}")
+    assert err <= tol and lerr <= (F32_TOL if wl.dtype == "f32" else 1e-3)
 
 
 def test_paged_bad_entries_are_flagged_and_clamped():
