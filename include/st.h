@@ -359,6 +359,24 @@ int st_verification_step_ex(const st_tree* tree, const st_step* step, int draft_
                             void* stream);
 
 /*
+ * st_verification_step_noalloc -- st_verification_step for callers that
+ * cannot allocate memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc).  It takes no workspace: the library's own
+ * static device buffer of 16 MiB per GPU (ST_NOALLOC_SCRATCH_BYTES), reserved
+ * when the library is loaded and held until the process ends, serves as the
+ * step's workspace.  The call allocates and frees nothing.  Outputs equal
+ * st_verification_step's for the same arguments.  Returns ST_E_WORKSPACE when
+ * st_verification_step_workspace(tree, step) exceeds the buffer (nothing is
+ * enqueued), ST_E_LAUNCH if the buffer's device address cannot be obtained,
+ * otherwise as st_verification_step.  Every call on one GPU uses that GPU's
+ * one buffer: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller; calls on one stream are ordered.
+ */
+#define ST_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int st_verification_step_noalloc(const st_tree* tree, const st_step* step, int32_t* status,
+                                 void* stream);
+
+/*
  * st_verification_step_paged -- st_verification_step over a paged KV pool:
  * step->k_cache / step->v_cache are pools [n_blocks][Hkv][block_size][D]
  * addressed through block_table [B][max_blocks] as for

@@ -98,6 +98,7 @@ def _declare(lib):
         "st_verification_step_paged": (I, [TP, _c.POINTER(StStep), I, I, P, I, P, S, P, P]),
         "st_verification_step_ex": (I, [TP, _c.POINTER(StStep), I, _c.c_float, P, S, P, P]),
         "st_testing_set_plan": (I, [_c.POINTER(StTestingPlan)]),
+        "st_verification_step_noalloc": (I, [TP, _c.POINTER(StStep), P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -469,6 +470,21 @@ def st_verification_step(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix
     _check(load_library().st_verification_step(
         tree.ref, ctypes.byref(step), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(status), _stream()), "st_verification_step")
+
+
+def st_verification_step_noalloc(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix: int,
+                                 out, lse, tokens, logits, accept_len, accept_nodes, out_tokens,
+                                 src_slot, new_len, draft_logits=None, temperature: float = 1.0,
+                                 seed: int = 0, offset: int = 0, near_ties=None,
+                                 scale: Optional[float] = None, status=None):
+    """st_verification_step without a workspace argument: the library's
+    static per-GPU buffer serves as the workspace (no allocation)."""
+    step = _step_struct(tree, q, k_cache, v_cache, prefix_len, max_prefix, out, lse, tokens,
+                        logits, draft_logits, temperature, seed, offset, accept_len, accept_nodes,
+                        out_tokens, near_ties, src_slot, new_len, scale)
+    _check(load_library().st_verification_step_noalloc(tree.ref, ctypes.byref(step),
+                                                       _ptr(status), _stream()),
+           "st_verification_step_noalloc")
 
 
 def st_verification_step_ex(tree: Tree, q, k_cache, v_cache, prefix_len, max_prefix: int, out,

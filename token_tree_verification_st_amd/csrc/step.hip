@@ -8,6 +8,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace {
 
 size_t verify_ws(const st_tree* t, const st_step* s) {
@@ -126,3 +128,46 @@ extern "C" int st_verification_step_ex(const st_tree* tree, const st_step* s, in
   if ((draft_is_probs || top_p < 1.f) && !s->draft_logits) return ST_E_INVALID;
   return step_impl(tree, s, workspace, ws_bytes, status, stream, nullptr, draft_is_probs, top_p);
 }
+
+// ---------------------------------------------------------------- no allocation
+//
+// The one-call step for callers that cannot allocate (code under HIP graph
+// capture, serving loops that forbid hipMalloc): its workspace is a
+// file-scope device array of kScratchBytes, which every GPU the library runs
+// on holds (at its own address) until the process ends.  Nothing in the
+// step's workspace needs to start at zero: every partial, verdict and argmax
+// slice that a later launch reads is written first by an earlier one.
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device (null if the lookup fails).
+void* scratch_on_current_device() {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" int st_verification_step_noalloc(const st_tree* tree, const st_step* s,
+                                            int32_t* status, void* stream) {
+  const size_t need = st_verification_step_workspace(tree, s);
+  if (need == 0) return ST_E_INVALID;
+  if (need > kScratchBytes) return ST_E_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return ST_E_LAUNCH;
+  return step_impl(tree, s, ws, kScratchBytes, status, stream, nullptr);
+}
+
