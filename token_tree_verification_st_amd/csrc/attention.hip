@@ -219,6 +219,37 @@ __device__ __forceinline__ int kswz(int key) {
   return D >= 128 ? (key & (D / 8 - 1)) : ((key >> 1) & (D / 8 - 1));
 }
 
+// The 32-bit LDS address of a pointer into the workgroup's LDS block.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Eight ds_read_b64_tr_b16 (each lane gets one dim of four keys) issued
+// together, with the wait for their results inside the same block.  Written
+// out rather than through the builtin because the compiler, unable to tell
+// these reads from the in-flight direct loads that refill other ring stages,
+// would otherwise wait for every outstanding direct load before the first of
+// them; the kernel's own waits already cover the stage read here.
+__device__ __forceinline__ void ds_read_tr16_x8(const uint32_t (&a)[8], u32x2 (&o)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+        "v"(a[7])
+      : "memory");
+}
+
 // vmcnt(n) with the other counters left alone (gfx9 encoding).
 #define ST_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
@@ -435,18 +466,27 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
   }
   const int jq = r16 >> 2, qq = r16 & 3;
   const int key1 = 4 * grp + jq, key2 = key1 + 16;
+  // V^T fragments, four dims blocks (eight transposed reads) at a time
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int ch = 2 * db + (qq >> 1), sub = 4 * (qq & 1);
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(sV + key1 * D + 8 * (ch ^ vswz<D>(key1)) + sub));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(sV + key2 * D + 8 * (ch ^ vswz<D>(key2)) + sub));
-    const bf16x8 vf =
-        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  for (int d0 = 0; d0 < NDB; d0 += 4) {
+    uint32_t ad[8];
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-      acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb], acc[rb][db], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int ch = 2 * (d0 + i) + (qq >> 1), sub = 4 * (qq & 1);
+      ad[2 * i] = lds_addr(sV + key1 * D + 8 * (ch ^ vswz<D>(key1)) + sub);
+      ad[2 * i + 1] = lds_addr(sV + key2 * D + 8 * (ch ^ vswz<D>(key2)) + sub);
+    }
+    u32x2 t[8];
+    ds_read_tr16_x8(ad, t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 vf = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(t[2 * i], t[2 * i + 1], 0, 1, 2, 3));
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb)
+        acc[rb][d0 + i] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb], acc[rb][d0 + i], 0, 0, 0);
+    }
   }
 }
 
@@ -492,7 +532,7 @@ attn_stream_kernel(AttnArgs a) {
   constexpr int MPT = (MWORDS + 255) / 256;           // mask words per thread
   static_assert(DPC * PRIME <= 63, "in-flight loads exceed the vmcnt range");
   __shared__ __attribute__((aligned(1024)))
-  uint8_t lds[BODY + QBYTES + MWORDS * 8 + ST_MAX_NODES * 4];
+  uint8_t lds[BODY + QBYTES + MWORDS * 8 + ST_MAX_NODES * 4 + 64];
   uint16_t* sQ = (uint16_t*)(lds + BODY);
   uint64_t* sMask = (uint64_t*)(lds + BODY + QBYTES);
   int* sPar = (int*)(sMask + MWORDS);
@@ -510,14 +550,17 @@ attn_stream_kernel(AttnArgs a) {
   const uint16_t* kgp = (const uint16_t*)a.k + head_off;
   const uint16_t* vgp = (const uint16_t*)a.v + head_off;
   uint16_t* ring = (uint16_t*)lds + kg * NSTAGE * STAGE;
-  // (the argmax reduction borrows the parent-array words of LDS before the
-  // masks are built; a second LDS object would cost the ring's prefetch: the
+  // (the argmax reduction's words follow the parent array, in the same LDS
+  // object: a second LDS object would cost the ring's prefetch, as the
   // compiler then waits for every direct load before each LDS read)
-  int* am_scratch = sPar;
-  // paged pool: the raw table entries of the first chunks, read before the
-  // request's size is known (a chunk's key depends on the split alone; the
-  // index is clamped into the table row, and an entry is checked where it is
-  // used, for a chunk inside the request's keys)
+  int* am_scratch = sPar + ST_MAX_NODES;
+  // The request's sizes first, waited for alone: every later address depends
+  // on them.  (Loads issued behind the first chunks' direct loads, 16 KB a
+  // wavefront all over the chip, wait for all of them.)
+  const ReqInfo rq = request_info(a, it.b);
+  // paged pool: the raw table entries of the first chunks (a chunk's key
+  // depends on the split alone; the index is clamped into the table row, and
+  // an entry is checked where it is used, for a chunk inside the request's keys)
   int e_first[PRIME];
 #pragma unroll
   for (int s = 0; s < PRIME; ++s)
@@ -529,26 +572,12 @@ attn_stream_kernel(AttnArgs a) {
   st::ArgmaxRegs amr;
   if (am) st::argmax_slice_load<true>(a.am.logits, a.am.V, it.w / a.am.nslices, it.w % a.am.nslices, amr);
 
-  // contiguous caches: this wavefront's first chunk is issued before the
-  // request's sizes arrive when its 32 rows lie inside the (request, head)
-  // cache.  It is kept when the chunk lies wholly inside the request's keys;
-  // otherwise it is waited for (no direct load may still be writing LDS when
-  // the slot is reloaded or the workgroup ends) and replaced.
-  const int key0 = k0 + kg * kCK;
-  const bool spec = !PAGED && key0 + kCK <= a.S_max;
-  const ChunkOff<D, RWV> coff(rw, lane);
-  if (spec)
-    chunk_dma<D, RWV, false>(ring, ring + kCK * D, a, it, kgp, vgp, key0, key0 + kCK - 1, rw,
-                             lane, coff);
-
-  const ReqInfo rq = request_info(a, it.b);
   const int rows_b = rq.n * a.G;
   const int row0 = it.rblk * ROWS;
   if (!rq.ok || row0 >= rows_b || k0 >= rq.key_end) {
     if (!rq.ok && threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
       st::set_status(a.status, ST_STATUS_BAD_PREFIX);
     if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
-    if (spec) ST_WAIT_VMCNT(0);
     return;
   }
   const int k1 = min(k0 + a.KS, rq.key_end);
@@ -558,14 +587,9 @@ attn_stream_kernel(AttnArgs a) {
   const int nmine = (nch - kg + KWV - 1) / KWV;  // chunks kg, kg + KWV, ...
   const int niter = (nch + KWV - 1) / KWV;       // the same for every wavefront
   const int want = min(PRIME, nmine);
-  // the first chunk goes first, then Q and the masks, then the rest of the ring
+  const ChunkOff<D, RWV> coff(rw, lane);
   // paged pool: the block of each chunk is looked up one refill ahead
   auto entry = [&](int c) { return PAGED ? table_entry(a, it.b, k0 + c * kCK) : 0; };
-  const bool keep = spec && nmine > 0 && klast - key0 >= kCK - 1;
-  if (spec && !keep) ST_WAIT_VMCNT(0);
-  if (nmine > 0 && !keep)
-    chunk_dma<D, RWV, PAGED>(ring, ring + kCK * D, a, it, kgp, vgp, key0, klast, rw, lane, coff,
-                             PAGED ? table_phys(a, e_first[0]) : 0);
 
   // Q of the workgroup's rows (rows past the end repeat the last): staged in
   // LDS once when several key groups share the rows, else loaded directly.
@@ -594,27 +618,34 @@ attn_stream_kernel(AttnArgs a) {
     }
   }
 
-  // Ancestor masks are needed only when the key range reaches tree keys: read
-  // the workgroup's rows of `mask`, or (mask == null) the request's parent
-  // array, from which they are derived below.  Clamped, unconditional loads.
+  // Ancestor masks are needed only when the key range reaches tree keys: the
+  // workgroup's rows of `mask`, or (mask == null) the request's parent array,
+  // from which they are derived below, copied straight to LDS (clamped
+  // addresses; words past the tree's W are cleared after the copy).  Direct
+  // loads like the ring's, so that the waits for the ring cover them too.
   const bool need_mask = k1 > rq.P;
   const bool derive = a.mask == nullptr;
-  uint64_t mword[MPT];
-  int par = -1;
-#pragma unroll
-  for (int i = 0; i < MPT; ++i) mword[i] = 0ull;
   if (need_mask) {
+#if defined(__HIP_DEVICE_COMPILE__)
     if (derive) {
-      par = a.parent[rq.lo + min(tid, rq.n - 1)];
+      if (wave * 64 < rq.n) {
+        const int32_t* src = a.parent + rq.lo + min(tid, rq.n - 1);
+        __builtin_amdgcn_global_load_lds(src, ST_LDS_PTR(sPar + wave * 64), 4, 0, 0);
+      }
     } else {
-#pragma unroll
-      for (int i = 0; i < MPT; ++i) {
-        const int idx = min(tid + 256 * i, MWORDS - 1), row = row0 + idx / 4, w = idx % 4;
-        const int node = min(row, rows_b - 1) / a.G;
-        mword[i] = a.mask[(size_t)(rq.lo + node) * a.W + min(w, a.W - 1)];
+      for (int i = wave; i < 2 * MWORDS / 64; i += 4) {  // 32-bit halves of mask words
+        const int j = i * 64 + lane, idx = j >> 1;
+        const int row = min(row0 + idx / 4, rows_b - 1), w = min(idx % 4, a.W - 1);
+        const uint32_t* src =
+            (const uint32_t*)(a.mask + (size_t)(rq.lo + row / a.G) * a.W + w) + (j & 1);
+        __builtin_amdgcn_global_load_lds(src, ST_LDS_PTR((uint32_t*)sMask + i * 64), 4, 0, 0);
       }
     }
+#endif
   }
+  if (nmine > 0)
+    chunk_dma<D, RWV, PAGED>(ring, ring + kCK * D, a, it, kgp, vgp, k0 + kg * kCK, klast, rw,
+                             lane, coff, PAGED ? table_phys(a, e_first[0]) : 0);
 #pragma unroll
   for (int s = 1; s < PRIME; ++s)
     if (s < nmine)
@@ -625,8 +656,7 @@ attn_stream_kernel(AttnArgs a) {
   if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
   if (need_mask) {
     if (derive) {
-      if (tid < rq.n) sPar[tid] = par;
-      lds_barrier();
+      lds_barrier();  // every wavefront's share of the parent array has landed
       if (tid < ROWS) {
         const int row = row0 + tid;
         uint64_t w0 = 0ull, w1 = 0ull, w2 = 0ull, w3 = 0ull;
@@ -638,10 +668,11 @@ attn_stream_kernel(AttnArgs a) {
         sMask[tid * 4 + 3] = w3;
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < MPT; ++i) {
-        const int idx = tid + 256 * i, row = row0 + idx / 4, w = idx % 4;
-        if (idx < MWORDS) sMask[idx] = (row < rows_b && w < a.W) ? mword[i] : 0ull;
+      // words past the tree's W and rows past the request are cleared, each
+      // by the wavefront that copied it (its own copies have landed)
+      for (int i = wave; i < 2 * MWORDS / 64; i += 4) {
+        const int j = i * 64 + lane, idx = j >> 1;
+        if (row0 + idx / 4 >= rows_b || idx % 4 >= a.W) ((uint32_t*)sMask)[j] = 0u;
       }
     }
   }
