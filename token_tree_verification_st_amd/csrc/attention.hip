@@ -197,6 +197,17 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The same barrier with the ring's prefetch left in flight.  A release fence
+// on LDS makes the compiler wait for every outstanding direct load (they
+// write LDS), including chunks still streaming into other ring stages; here
+// each wavefront has already waited, with counted waits, for its own direct
+// loads that other wavefronts read after the barrier, so only its LDS
+// operations need to complete.  The asm's memory clobber keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier_inflight() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // V tiles sit in LDS in their natural [key][dim] layout (256-byte rows, no
 // padding).  The MFMA operand V^T is read with ds_read_b64_tr_b16, which
 // hands each lane one dim of four keys.  Each 16-byte chunk c of key row r is
@@ -568,16 +579,22 @@ attn_stream_kernel(AttnArgs a) {
                                  min((k0 + (s * KWV + kg) * kCK) >> a.pg.lbs,
                                      a.pg.bt_stride - 1)]
                        : 0;
+  // A vocab argmax slice (the one-call step): loaded after the ring's first
+  // chunks and reduced after the loop, so that neither its loads nor its
+  // reduction delay the first chunk's compute.
   const bool am = a.am.logits != nullptr && it.w < a.am.units;
   st::ArgmaxRegs amr;
-  if (am) st::argmax_slice_load<true>(a.am.logits, a.am.V, it.w / a.am.nslices, it.w % a.am.nslices, amr);
 
   const int rows_b = rq.n * a.G;
   const int row0 = it.rblk * ROWS;
   if (!rq.ok || row0 >= rows_b || k0 >= rq.key_end) {
     if (!rq.ok && threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
       st::set_status(a.status, ST_STATUS_BAD_PREFIX);
-    if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
+    if (am) {
+      st::argmax_slice_load<true>(a.am.logits, a.am.V, it.w / a.am.nslices, it.w % a.am.nslices,
+                                  amr);
+      argmax_unit_finish(a, it.w, amr, am_scratch);
+    }
     return;
   }
   const int k1 = min(k0 + a.KS, rq.key_end);
@@ -653,10 +670,12 @@ attn_stream_kernel(AttnArgs a) {
                                k0 + (s * KWV + kg) * kCK, klast, rw, lane, coff,
                                PAGED ? table_phys(a, e_first[s]) : 0);
   wait_chunks<PRIME - 1, DPC>(want - 1);  // the first chunk, Q and the masks are older
-  if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
+  if (am)
+    st::argmax_slice_load<true>(a.am.logits, a.am.V, it.w / a.am.nslices, it.w % a.am.nslices,
+                                amr);
   if (need_mask) {
     if (derive) {
-      lds_barrier();  // every wavefront's share of the parent array has landed
+      lds_barrier_inflight();  // every wavefront's share of the parent array has landed
       if (tid < ROWS) {
         const int row = row0 + tid;
         uint64_t w0 = 0ull, w1 = 0ull, w2 = 0ull, w3 = 0ull;
@@ -676,7 +695,7 @@ attn_stream_kernel(AttnArgs a) {
       }
     }
   }
-  lds_barrier();  // Q (when staged) and the masks are in LDS
+  lds_barrier_inflight();  // Q (when staged) and the masks are in LDS
   if constexpr (QLDS) {
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
@@ -748,6 +767,7 @@ attn_stream_kernel(AttnArgs a) {
       refill = refill + 1 == NSTAGE ? 0 : refill + 1;
     }
   }
+  if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     l[rb] = xor16_add(l[rb]);
