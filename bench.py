@@ -52,6 +52,9 @@ def parse():
                     help="also time st_tree_attention_paged with this block size")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--only", default=None, choices=("attention", "verify", "step"),
+                    help="for counter runs: launch only this call (warm-up, then a graph of "
+                         "--steps calls), print its per-call time and exit")
     return ap.parse_args()
 
 
@@ -398,6 +401,39 @@ def bench_tree_build(args):
     print(json.dumps(line), flush=True)
 
 
+def only(args, reps, R, fns, one_step):
+    """One call alone, for counter runs: warm-up, a graph of K launches (events
+    around its replay), then the calibration copy; every dispatch of the
+    call's kernels in the process is one of these."""
+    import torch
+    fn = one_step if args.only == "step" else fns[args.only]
+    for i in range(args.warmup):
+        fn(reps[i % R])
+    torch.cuda.synchronize()
+    K = args.steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            fn(reps[i % R])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    st_words = [int(r.buf["status"].item()) for r in reps]
+    assert not any(st_words), f"device status {st_words}"
+    print(json.dumps({"only": args.only, "workload": args.workload, "calls": K,
+                      "us_per_call": round(e0.elapsed_time(e1) / K * 1e3, 3)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -452,6 +488,10 @@ def main():
                                   draft=d.buf.get("draft_probs"))
         else:
             stp.verification_step(d, stochastic=stochastic)
+
+    if args.only:
+        only(args, reps, R, fns, one_step)
+        return
 
     for i in range(args.warmup):
         one_step(reps[i % R])
@@ -575,8 +615,9 @@ def main():
     attn_us = per_call["attention"]
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     from token_tree_verification_st_amd.profiling import read_traffic
-    traffic = read_traffic(args.traffic or os.path.join(
-        ROOT, "profiles", f"attention_{wl.name}_traffic.md"))
+    traffic_md = args.traffic or os.path.join(ROOT, "profiles", f"attention_{wl.name}_traffic.md")
+    traffic = read_traffic(traffic_md)
+    traffic_partials = read_traffic(traffic_md, "split_partial_bytes")
     attn_flops = algorithmic_attention_flops(wl)
     tflops = attn_flops / (attn_us * 1e-6) / 1e12
     peak_tf = MFMA_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
@@ -587,7 +628,7 @@ def main():
             "peak": peak_tf if mfma_bound else HBM_PEAK_GBS,
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "frac": round(tflops / peak_tf if mfma_bound else achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "traffic": traffic, "traffic_split_partials": traffic_partials,
             "kernel": "st_tree_attention", "algorithmic_bytes": attn_bytes,
             "algorithmic_flops": attn_flops, "hbm_gbs": round(achieved, 1),
             "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / peak_tf, 4),

@@ -1031,21 +1031,34 @@ __device__ inline void combine_block_n(const AttnArgs& a, int blk) {
   const int d = 4 * (threadIdx.x % LPR);
   const int TH = a.T * a.Hq;
   if (grow >= TH) return;
-  // Every row has a.NS partial slots: the first CHUNK splits' loads go out
-  // before the row's request (and with it its split count) is known.
+  // Every row has a.NS partial slots.  With one request the first CHUNK
+  // splits' loads go out before its split count is known; in a batch, where
+  // short requests have fewer splits (or one, and no partials at all), the
+  // row's request is looked up first and only its splits are read.
   float2 ml[CHUNK];
   f32x4 x[CHUNK];
+  const bool single = a.B == 1;
+  if (single) {
 #pragma unroll
-  for (int j = 0; j < CHUNK; ++j) {
-    const size_t pr = (size_t)min(j, a.NS - 1) * TH + grow;
-    ml[j] = a.ws_ml[pr];
-    x[j] = *(const f32x4*)(a.ws_acc + pr * D + d);
+    for (int j = 0; j < CHUNK; ++j) {
+      const size_t pr = (size_t)min(j, a.NS - 1) * TH + grow;
+      ml[j] = a.ws_ml[pr];
+      x[j] = *(const f32x4*)(a.ws_acc + pr * D + d);
+    }
   }
   const int t = grow / a.Hq;
   const int b = st::request_of(a.node_off, a.B, t);
   const ReqInfo rq = request_info(a, b);
   if (!rq.ok || rq.nsplit <= 1) return;
   const int ns = rq.nsplit;
+  if (!single) {
+#pragma unroll
+    for (int j = 0; j < CHUNK; ++j) {
+      const size_t pr = (size_t)min(j, ns - 1) * TH + grow;
+      ml[j] = a.ws_ml[pr];
+      x[j] = *(const f32x4*)(a.ws_acc + pr * D + d);
+    }
+  }
   float M = -INFINITY, L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < ns; s0 += CHUNK) {

@@ -6,6 +6,9 @@
         COPY_BYTES LM_GRID OUT.md CMD_F CMD_W
     python -m token_tree_verification_st_amd.profiling traffic FETCH_CSV WRITE_CSV COPY_BYTES \\
         WORKLOAD OUT.md COMMAND_FETCH COMMAND_WRITE
+    python -m token_tree_verification_st_amd.profiling kernels_traffic FETCH_CSV WRITE_CSV \\
+        COPY_BYTES OUT.md TITLE COMMAND_FETCH COMMAND_WRITE KERNEL_PREFIX...
+    python -m token_tree_verification_st_amd.profiling sq OUT.md KERNEL TITLE CSV... -- COMMAND...
 
 `traffic` reads two --pmc runs of the same bench command (FETCH_SIZE, then
 WRITE_SIZE, KiB per dispatch).  Each counter is scaled by what it reads for
@@ -203,23 +206,53 @@ def traffic_md(fetch_csv, write_csv, copy_bytes, workload, cmd_f, cmd_w):
            "| kernel | dispatches | fetch bytes | write bytes |", "|---|---|---|---|"]
     for k, (fb, wb, n) in per_kernel.items():
         out.append(f"| {k} | {n} | {fb:.0f} | {wb:.0f} |")
-    out += ["", "Machine-readable (read by bench.py):", "",
+    # the split partials: written by the streaming kernel, read back by the merge
+    partials = sum(wb for k, (fb, wb, n) in per_kernel.items() if k.startswith("attn_stream")) + \
+        sum(fb for k, (fb, wb, n) in per_kernel.items() if k.startswith("attn_combine"))
+    merges = any(k.startswith("attn_combine") for k in per_kernel)
+    out += ["", f"Split partials (the streaming kernel's writes{' and the merge reading them back' if merges else ''}): "
+            f"{partials:.0f} bytes per call." if merges else
+            "", "Machine-readable (read by bench.py):", "",
             f"source_sha256: {attention_source_hash()}",
-            f"bytes_per_launch: {total:.0f}", ""]
+            f"bytes_per_launch: {total:.0f}",
+            f"split_partial_bytes: {partials if merges else 0:.0f}", ""]
     return "\n".join(out)
 
 
-def read_traffic(path: str):
-    """bytes_per_launch from a traffic summary, or None when the summary is
-    missing or was taken from different attention sources."""
+def read_traffic(path: str, field: str = "bytes_per_launch"):
+    """bytes_per_launch (or another figure, e.g. split_partial_bytes) from a
+    traffic summary, or None when the summary is missing or was taken from
+    different attention sources."""
     if not os.path.exists(path):
         return None
     text = open(path).read()
     h = re.search(r"^source_sha256: (\w+)", text, re.M)
-    b = re.search(r"^bytes_per_launch: (\d+)", text, re.M)
+    b = re.search(rf"^{field}: (\d+)", text, re.M)
     if not h or not b or h.group(1) != attention_source_hash():
         return None
     return int(b.group(1))
+
+
+def kernels_traffic_md(fetch_csv, write_csv, copy_bytes, title, cmd_f, cmd_w, prefixes):
+    """HBM bytes per dispatch of every kernel whose short name starts with one
+    of ``prefixes``, scaled by the same run's calibration copy."""
+    f = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    w = _per_dispatch(write_csv, "WRITE_SIZE")
+    if COPY_KERNEL not in f or COPY_KERNEL not in w:
+        raise SystemExit("the calibration copy is missing from the counter runs")
+    f_scale = copy_bytes / (f[COPY_KERNEL][2] * 1024.0)
+    w_scale = copy_bytes / (w[COPY_KERNEL][2] * 1024.0)
+    out = [f"# {title}", "", "Commands (run from /tmp with TMPDIR=/tmp; $R = repository root):",
+           "", "```", cmd_f, cmd_w, "```", "",
+           f"Calibration: a device copy of {copy_bytes} bytes in the same process reads "
+           f"FETCH_SIZE x {f_scale:.3f} and WRITE_SIZE x {w_scale:.3f} of its true bytes.", "",
+           "| kernel | dispatches | fetch bytes | write bytes |", "|---|---|---|---|"]
+    for k in sorted(set(f) | set(w)):
+        if any(k.startswith(p) for p in prefixes):
+            fb = f.get(k, (0.0, 0, 0.0))[0] * 1024.0 * f_scale
+            wb = w.get(k, (0.0, 0, 0.0))[0] * 1024.0 * w_scale
+            out.append(f"| {k} | {f.get(k, (0, 0, 0))[1]} | {fb:.0f} | {wb:.0f} |")
+    return "\n".join(out) + "\n"
 
 
 def sq_md(csvs, kernel: str, title: str, commands) -> str:
@@ -269,6 +302,10 @@ def main(argv):
         out, kernel, title = argv[1:4]
         i = argv.index("--")
         open(out, "w").write(sq_md(argv[4:i], kernel, title, argv[i + 1:]))
+    elif argv[0] == "kernels_traffic":   # FETCH WRITE COPY OUT TITLE CMD_F CMD_W PREFIX...
+        fcsv, wcsv, copy_bytes, out, title, cmd_f, cmd_w = argv[1:8]
+        open(out, "w").write(kernels_traffic_md(fcsv, wcsv, int(copy_bytes), title, cmd_f, cmd_w,
+                                                argv[8:]))
     elif argv[0] == "traffic":
         fcsv, wcsv, copy_bytes, workload, out, cmd_f, cmd_w = argv[1:8]
         open(out, "w").write(traffic_md(fcsv, wcsv, int(copy_bytes), workload, cmd_f, cmd_w))
