@@ -362,7 +362,7 @@ int st_verification_step_ex(const st_tree* tree, const st_step* step, int draft_
  * st_verification_step_noalloc -- st_verification_step for callers that
  * cannot allocate memory (code under HIP graph capture, serving loops or
  * harnesses that forbid hipMalloc).  It takes no workspace: the library's own
- * static device buffer of 16 MiB per GPU (ST_NOALLOC_SCRATCH_BYTES), reserved
+ * static device buffer of 64 MiB per GPU (ST_NOALLOC_SCRATCH_BYTES), reserved
  * when the library is loaded and held until the process ends, serves as the
  * step's workspace.  The call allocates and frees nothing.  Outputs equal
  * st_verification_step's for the same arguments.  Returns ST_E_WORKSPACE when
@@ -372,7 +372,7 @@ int st_verification_step_ex(const st_tree* tree, const st_step* step, int draft_
  * one buffer: calls that overlap on one GPU (other streams, other threads)
  * race and must be serialised by the caller; calls on one stream are ordered.
  */
-#define ST_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+#define ST_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int st_verification_step_noalloc(const st_tree* tree, const st_step* step, int32_t* status,
                                  void* stream);
 

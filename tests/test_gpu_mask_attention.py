@@ -172,6 +172,49 @@ def test_attention_workspace_reused_across_calls():
         assert status_of(dw) == 0
 
 
+# Split plans for batches: one split size for all requests (1), or splits sized
+# per request on the device (2, the planner's choice for 2..64 requests), with
+# the planner's workgroup target, a small one (many splits, up to the cap) and
+# a large one; the batches mix long and short requests.
+@pytest.mark.parametrize("target", [0, 24, 4096])
+@pytest.mark.parametrize("balance", [1, 2])
+def test_attention_split_plans(balance, target):
+    cases = [(128, 4, 4, 5, 1500, 90), (64, 8, 2, 9, 900, 40), (128, 16, 2, 3, 2000, 25),
+             (128, 4, 4, 1, 1200, 60)]
+    for i, (D, Hq, Hkv, B, pmax, nmax) in enumerate(cases):
+        wl = _small_case(90 + i, D=D, Hq=Hq, Hkv=Hkv, B=B, pmax=pmax, nmax=nmax)
+        with plan_override(attn_balance=balance, attn_target_wg=target):
+            err, lerr = attention_errors(wl, to_device(wl), derive_mask=i % 2 == 1)
+        say(f"balance {balance} target {target} case {i} (B {B}, prefixes "
+            f"{wl.prefix_len.tolist()}): max-abs {err:.2e} lse {lerr:.2e}")
+        assert err <= BF16_TOL and lerr <= 1e-3
+
+
+def test_attention_split_plans_agree():
+    """The two split plans of one ragged batch give outputs within the bf16
+    rounding of each other, and both set the bad-prefix status for a request
+    whose prefix exceeds max_prefix."""
+    from token_tree_verification_st_amd import step
+    wl = _small_case(97, B=6, pmax=1800, nmax=70)
+    outs = []
+    for balance in (1, 2):
+        with plan_override(attn_balance=balance, attn_target_wg=40):
+            dw = to_device(wl)
+            step.run_mask(dw)
+            step.run_attention(dw)
+            torch.cuda.synchronize()
+            assert status_of(dw) == 0
+            outs.append(dw.buf["out"].float().cpu())
+            bad = to_device(wl, max_prefix=int(wl.prefix_len.max()) - 1)
+            step.run_mask(bad)
+            step.run_attention(bad)
+            torch.cuda.synchronize()
+            assert status_of(bad) & 16
+    diff = float((outs[0] - outs[1]).abs().max())
+    say(f"uniform vs per-request splits: max-abs {diff:.2e}")
+    assert diff <= 2 * BF16_TOL
+
+
 def test_attention_peaked_softmax_exercises_rescaling():
     wl = _small_case(21, q_sigma=8.0, pmax=1500)
     err, lerr = attention_errors(wl, to_device(wl))

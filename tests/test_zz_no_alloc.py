@@ -35,10 +35,12 @@ def _noalloc(dw, stochastic):
 
 
 def test_noalloc_step_equals_step_on_consecutive_calls():
-    """llama7b (4 MiB of split partials in the static buffer), then the
-    smaller stochastic tree batch and the fp32 tiny tree, each against the
-    workspace entry point on a fresh copy of the same inputs."""
-    for name in ("llama7b", "stochastic_tree", "tiny_fp32", "llama7b"):
+    """llama7b (4 MiB of split partials in the static buffer), the ragged
+    batch (39 MiB: splits sized per request, room for up to 4 a request), then
+    the smaller stochastic tree batch, the fp32 tiny tree and llama7b again,
+    each against the workspace entry point on a fresh copy of the same
+    inputs."""
+    for name in ("llama7b", "ragged_batch", "stochastic_tree", "tiny_fp32", "llama7b"):
         wl = make_workload(name, 0)
         stochastic = wl.draft_logits is not None
         ref, got = to_device(wl), to_device(wl)
@@ -60,16 +62,18 @@ def test_noalloc_step_equals_step_on_consecutive_calls():
 
 
 def test_noalloc_step_refuses_a_step_larger_than_its_buffer():
+    """3 requests of 256 nodes x 64 heads (D 128): 49152 rows whose split
+    partials (room for 4 splits a row) exceed the 64 MiB buffer."""
     rng = np.random.default_rng(5)
-    trees = [tree_random_attach(rng, 64, 6) for _ in range(4)]
-    wl = build_workload("big", rng, dtype="bf16", Hq=64, Hkv=8, D=128, V=64,
-                        prefix_lens=[32768] * 4, trees=trees, max_depth=6, token_rule="uniform")
+    trees = [tree_random_attach(rng, 256, 6) for _ in range(3)]
+    wl = build_workload("big", rng, dtype="bf16", Hq=64, Hkv=64, D=128, V=64,
+                        prefix_lens=[512] * 3, trees=trees, max_depth=255, token_rule="uniform")
     dw = to_device(wl)
     b = dw.buf
     step = bd._step_struct(dw.tree, dw.q, dw.k_cache, dw.v_cache, dw.prefix_len, dw.max_prefix,
                            b["out"], b["lse"], dw.tokens, dw.logits, None, 1.0, 0, 0,
                            b["accept_len"], b["accept_nodes"], b["out_tokens"], None,
                            b["src_slot"], b["new_len"], None)
-    assert bd.st_verification_step_workspace(dw.tree, step) > 16 << 20
+    assert bd.st_verification_step_workspace(dw.tree, step) > 64 << 20
     with pytest.raises(RuntimeError, match="workspace"):
         _noalloc(dw, False)

@@ -30,6 +30,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -52,15 +54,19 @@ struct AttnArgs {
   float* lse;
   float2* ws_ml;   // [NS][T*Hq] (m in log2 units, l)
   float* ws_acc;   // [NS][T*Hq][D]
+  int32_t* ws_ns;  // balanced plans: [T] the split count of each node's request
   int32_t* status;
   st::ArgmaxJob am;  // vocab argmax slices reduced in the prologue (am.logits null: none)
   int B, T, Hq, Hkv, G, S_max, W, max_nodes, max_prefix;
-  int KS;          // keys per split (multiple of 16)
-  int NS;          // splits of the longest request
+  int KS;          // keys per split (multiple of 16); balanced plans: unused
+  int NS;          // splits of the longest request; balanced plans: the most any request has
   int RB;          // rows per workgroup
   int n_rblk;      // row blocks of the widest request
-  int items;       // B * Hkv * NS * n_rblk
+  int items;       // B * Hkv * NS * n_rblk; balanced plans: an upper bound
   int per_xcd;     // ceil(items / 8)
+  int balanced;    // splits sized per request on the device (B <= 64)
+  int target;      // balanced plans: the workgroups the chunk budget aims for
+  int cmax;        // balanced plans: 32-key chunks of the longest possible request
   float scale_log2;
   st::KvPaging pg; // pg.bt null: contiguous caches
 };
@@ -97,6 +103,7 @@ __device__ inline const T* kv_row(const AttnArgs& a, const void* cache, int b, i
 
 struct Item {
   int w, b, g, split, rblk;
+  int ks;  // keys per split of the item's request
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8).  Item w
@@ -285,6 +292,164 @@ __device__ __forceinline__ void ds_read_tr16_x8(const uint32_t (&a)[8], u32x2 (&
 // and the final division uses the same reference, so the result is unchanged.
 constexpr int kCK = 32;
 constexpr float kLazy = 8.f;
+
+// ---------------------------------------------------------------- balanced splits
+//
+// In a batch whose requests differ in length, one split size for all leaves
+// the longest request's workgroups running alone at the end, each with one or
+// two chunks in flight.  A balanced plan (batches of at most 64 requests)
+// sizes each request's splits instead, from the sizes in device memory, which
+// every workgroup of the attention kernel reads and turns into the same plan:
+//   - request b of c_b 32-key chunks, for a budget of q chunks, gets
+//     min(NS, ceil(c_b / q)) splits of kc_b = ceil(c_b / splits) chunks each
+//     (then as many splits as that size needs, so none is empty), and kv
+//     heads x row blocks x splits workgroups (items);
+//   - q is the smallest budget (at least two chunks) whose items fit in
+//     `target` workgroups, the ones the chip holds at once: the longest item
+//     is as short as it can be without a second round of workgroups; when no
+//     budget fits, no request is split;
+//   - the workgroups of a request's first split and first kv head record the
+//     split count of each of its nodes (ws_ns), which the merge reads;
+//   - a unit is one (kv head, split) of a request; its row blocks read the
+//     same keys.
+// Lane i of a wavefront holds request i.  A request that fails the size
+// checks gets one chunk and one row block per head (its workgroups report it).
+struct BalLane {
+  int lo, n, P, ok;  // the request's node offset, nodes, prefix and size check
+  int rb, ns, kc;    // row blocks, splits, chunks per split
+};
+
+__device__ inline BalLane balanced_lane(const AttnArgs& a, int lane) {
+  const int i = min(lane, a.B - 1);
+  const int lo = a.node_off[i], hi = a.node_off[i + 1], P = a.prefix_len[i];
+  BalLane r;
+  r.lo = lo;
+  r.n = hi - lo;
+  r.P = P;
+  r.ok = (lo >= 0) & (hi <= a.T) & (r.n >= 1) & (r.n <= a.max_nodes) & (P >= 0) &
+         (P <= a.max_prefix) & (P + r.n <= a.S_max);
+  const int c = r.ok ? (P + r.n + kCK - 1) / kCK : 1;
+  r.rb = r.ok ? (r.n * a.G + a.RB - 1) / a.RB : 1;
+  const int hr = lane < a.B ? a.Hkv * r.rb : 0;  // workgroups of one split of the request
+  // The smallest budget q in [2, cmax] whose items fit in `target`
+  // workgroups (cmax: the chunks of the longest possible request, so every
+  // request is one split at q = cmax).  With W = sum of hr * c and H = sum of
+  // hr, the items at q lie in [W / q, W / q + H], so q is at least W / target
+  // and, when H < target, at most W / (target - H).  The items only fall as
+  // q grows: the 64 lanes test 64 budgets spread over the range at once and
+  // the first that fits narrows it, until the budgets are consecutive (one
+  // round when the range holds at most 64).  The search counts min(NS,
+  // ceil(c / q)) splits a request, at least the final count below.  Nothing
+  // fits at cmax: no request is split.
+  // Request j's sizes are read from lane j four requests at a time, without
+  // branches (lanes past B have hr = 0 and B <= 64, so j + 3 <= 63).
+  long W = 0;
+  int H = 0;
+  for (int j = 0; j < a.B; j += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int hj = __builtin_amdgcn_readlane(hr, j + u);
+      W += (long)hj * __builtin_amdgcn_readlane(c, j + u);
+      H += hj;
+    }
+  }
+  // (bounds in double precision: W and the quotients are exact there to well
+  // past any size here; the upper bound gets one chunk of margin)
+  const int cm = max(2, a.cmax);
+  const double Wd = (double)W;
+  int qlo = (int)fmin((double)cm, fmax(2.0, ceil(Wd / a.target)));
+  int qhi = H < a.target ? (int)fmin((double)cm, fmax((double)qlo, ceil(Wd / (a.target - H)) + 1.0))
+                         : cm;
+  int q = cm;
+  while (true) {
+    const int step = (qhi - qlo + 62) / 63;  // lanes 0..63 reach qhi
+    const int qj = lane == 63 ? qhi : min(qlo + lane * max(step, 1), qhi);
+    const unsigned uq = (unsigned)qj;
+    int items = 0;
+    for (int j = 0; j < a.B; j += 4) {
+      int part[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // c >= 1: a request within q chunks counts one
+        const unsigned cj = (unsigned)__builtin_amdgcn_readlane(c, j + u);
+        part[u] = __builtin_amdgcn_readlane(hr, j + u) * min(a.NS, (int)((cj + uq - 1u) / uq));
+      }
+      items += (part[0] + part[1]) + (part[2] + part[3]);
+    }
+    const uint64_t fit = __ballot(items <= a.target);
+    if (!fit) break;  // only when the range ends at cmax
+    const int jf = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)fit) - 1);
+    q = __builtin_amdgcn_readlane(qj, jf);
+    if (step <= 1 || jf == 0) break;
+    qlo = __builtin_amdgcn_readlane(qj, jf - 1) + 1;
+    qhi = q;
+  }
+  const int ns0 = q >= c ? 1 : min(a.NS, (c + q - 1) / q);
+  r.kc = (c + ns0 - 1) / ns0;
+  r.ns = (c + r.kc - 1) / r.kc;
+  return r;
+}
+
+// The grid of a balanced plan: request b takes a run of workgroups [base,
+// base + size), requests in order, with its units padded to a multiple of 8:
+// unit j = 8 * grp + x of the request sits at base + grp * 8 * rb + r * 8 + x
+// for row block r.  Workgroups go round-robin over the 8 XCDs (blockIdx % 8),
+// so a request's units are dealt over the XCDs and the row blocks of one
+// unit, which read the same keys, follow each other on one XCD (its L2 serves
+// the second).  Workgroups of a padding unit have no item.
+__device__ inline void balanced_order(const AttnArgs& a, const BalLane& L, int lane, int& base,
+                                      int& size, int& total) {
+  const int units = lane < a.B ? a.Hkv * L.ns : 0;
+  size = ((units + 7) & ~7) * L.rb;
+  base = 0;
+  total = 0;
+  for (int j = 0; j < a.B; j += 4) {  // lanes past B have size 0 (B <= 64)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sj = __builtin_amdgcn_readlane(size, j + u);
+      base += j + u < lane ? sj : 0;
+      total += sj;
+    }
+  }
+}
+
+// The workgroup's item and its request's sizes; false for a workgroup with
+// no item.  Uniform across the workgroup (every wavefront derives the same
+// values).
+__device__ inline bool locate_item(const AttnArgs& a, Item& it, ReqInfo& rq) {
+  if (!a.balanced) {
+    if (!decode_item(a, it)) return false;
+    it.ks = a.KS;
+    rq = request_info(a, it.b);
+    return true;
+  }
+  const int lane = threadIdx.x & 63;
+  const BalLane L = balanced_lane(a, lane);
+  int base, size, total;
+  balanced_order(a, L, lane, base, size, total);
+  const int bid = blockIdx.x;
+  if (bid >= total) return false;
+  const uint64_t hit = __ballot(lane < a.B && base <= bid && bid < base + size);
+  const int b = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+  const int rb = __builtin_amdgcn_readlane(L.rb, b);
+  const int ns = __builtin_amdgcn_readlane(L.ns, b);
+  const int local = bid - __builtin_amdgcn_readlane(base, b);
+  const int grp = local / (8 * rb), rem = local - grp * 8 * rb;
+  const int j = grp * 8 + (rem & 7);
+  if (j >= a.Hkv * ns) return false;  // padding
+  it.w = bid;
+  it.b = b;
+  it.rblk = rem >> 3;
+  it.g = j / ns;
+  it.split = j - it.g * ns;
+  it.ks = __builtin_amdgcn_readlane(L.kc, b) * kCK;
+  rq.lo = __builtin_amdgcn_readlane(L.lo, b);
+  rq.n = __builtin_amdgcn_readlane(L.n, b);
+  rq.P = __builtin_amdgcn_readlane(L.P, b);
+  rq.ok = __builtin_amdgcn_readlane(L.ok, b) != 0;
+  rq.key_end = rq.P + rq.n;
+  rq.nsplit = ns;
+  return true;
+}
 
 // Cross-lane reductions over the lane groups l, l^16, l^32, l^48, which hold
 // the same query row: gfx950 permlane swaps exchange 16-lane rows in VALU.
@@ -548,27 +713,40 @@ attn_stream_kernel(AttnArgs a) {
   uint64_t* sMask = (uint64_t*)(lds + BODY + QBYTES);
   int* sPar = (int*)(sMask + MWORDS);
 
-  Item it;
-  if (!decode_item(a, it)) return;
   // the wavefront index is uniform: keep it (and all that derives from it) scalar
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rw = wave % RWV, kg = wave / RWV;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int k0 = it.split * a.KS;
+  // (the argmax reduction's words follow the parent array, in the same LDS
+  // object: a second LDS object would cost the ring's prefetch, as the
+  // compiler then waits for every direct load before each LDS read)
+  int* am_scratch = sPar + ST_MAX_NODES;
+  // A vocab argmax slice (the one-call step), one for each workgroup of the
+  // grid below the slice count, with an item or without: loaded after the
+  // ring's first chunks and reduced after the loop, so that neither its loads
+  // nor its reduction delay the first chunk's compute.
+  const int au = blockIdx.x;
+  const bool am = a.am.logits != nullptr && au < a.am.units;
+  st::ArgmaxRegs amr;
+  // The item and its request's sizes first, waited for alone: every later
+  // address depends on them.  (Loads issued behind the first chunks' direct
+  // loads, 16 KB a wavefront all over the chip, wait for all of them.)
+  Item it;
+  ReqInfo rq;
+  if (!locate_item(a, it, rq)) {
+    if (am) {
+      st::argmax_slice_load<true>(a.am.logits, a.am.V, au / a.am.nslices, au % a.am.nslices, amr);
+      argmax_unit_finish(a, au, amr, am_scratch);
+    }
+    return;
+  }
+  const int k0 = it.split * it.ks;
   // contiguous caches: the (request, head) base, fixed for the workgroup
   const size_t head_off = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
   const uint16_t* kgp = (const uint16_t*)a.k + head_off;
   const uint16_t* vgp = (const uint16_t*)a.v + head_off;
   uint16_t* ring = (uint16_t*)lds + kg * NSTAGE * STAGE;
-  // (the argmax reduction's words follow the parent array, in the same LDS
-  // object: a second LDS object would cost the ring's prefetch, as the
-  // compiler then waits for every direct load before each LDS read)
-  int* am_scratch = sPar + ST_MAX_NODES;
-  // The request's sizes first, waited for alone: every later address depends
-  // on them.  (Loads issued behind the first chunks' direct loads, 16 KB a
-  // wavefront all over the chip, wait for all of them.)
-  const ReqInfo rq = request_info(a, it.b);
   // paged pool: the raw table entries of the first chunks (a chunk's key
   // depends on the split alone; the index is clamped into the table row, and
   // an entry is checked where it is used, for a chunk inside the request's keys)
@@ -579,11 +757,6 @@ attn_stream_kernel(AttnArgs a) {
                                  min((k0 + (s * KWV + kg) * kCK) >> a.pg.lbs,
                                      a.pg.bt_stride - 1)]
                        : 0;
-  // A vocab argmax slice (the one-call step): loaded after the ring's first
-  // chunks and reduced after the loop, so that neither its loads nor its
-  // reduction delay the first chunk's compute.
-  const bool am = a.am.logits != nullptr && it.w < a.am.units;
-  st::ArgmaxRegs amr;
 
   const int rows_b = rq.n * a.G;
   const int row0 = it.rblk * ROWS;
@@ -591,13 +764,12 @@ attn_stream_kernel(AttnArgs a) {
     if (!rq.ok && threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
       st::set_status(a.status, ST_STATUS_BAD_PREFIX);
     if (am) {
-      st::argmax_slice_load<true>(a.am.logits, a.am.V, it.w / a.am.nslices, it.w % a.am.nslices,
-                                  amr);
-      argmax_unit_finish(a, it.w, amr, am_scratch);
+      st::argmax_slice_load<true>(a.am.logits, a.am.V, au / a.am.nslices, au % a.am.nslices, amr);
+      argmax_unit_finish(a, au, amr, am_scratch);
     }
     return;
   }
-  const int k1 = min(k0 + a.KS, rq.key_end);
+  const int k1 = min(k0 + it.ks, rq.key_end);
   const int klast = k1 - 1;
   const int wrow0 = row0 + rw * WROWS;
   const int nch = (k1 - k0 + kCK - 1) / kCK;
@@ -671,8 +843,7 @@ attn_stream_kernel(AttnArgs a) {
                                PAGED ? table_phys(a, e_first[s]) : 0);
   wait_chunks<PRIME - 1, DPC>(want - 1);  // the first chunk, Q and the masks are older
   if (am)
-    st::argmax_slice_load<true>(a.am.logits, a.am.V, it.w / a.am.nslices, it.w % a.am.nslices,
-                                amr);
+    st::argmax_slice_load<true>(a.am.logits, a.am.V, au / a.am.nslices, au % a.am.nslices, amr);
   if (need_mask) {
     if (derive) {
       lds_barrier_inflight();  // every wavefront's share of the parent array has landed
@@ -767,7 +938,7 @@ attn_stream_kernel(AttnArgs a) {
       refill = refill + 1 == NSTAGE ? 0 : refill + 1;
     }
   }
-  if (am) argmax_unit_finish(a, it.w, amr, am_scratch);
+  if (am) argmax_unit_finish(a, au, amr, am_scratch);
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     l[rb] = xor16_add(l[rb]);
@@ -835,6 +1006,12 @@ attn_stream_kernel(AttnArgs a) {
       if (grp == 0) a.ws_ml[pr] = make_float2(m[rb], l[rb]);
     }
   }
+  // balanced plans: the split count of each node of the row block, for the
+  // merge (once per node: first split, first kv head, the node's first row)
+  if (a.balanced && it.split == 0 && it.g == 0 && tid < ROWS) {
+    const int row = row0 + tid;
+    if (row < rows_b && row % a.G == 0) a.ws_ns[rq.lo + row / a.G] = rq.nsplit;
+  }
 }
 
 // ---------------------------------------------------------------- VALU path
@@ -866,8 +1043,8 @@ attn_valu_kernel(AttnArgs a) {
   __shared__ float sP[R][KT];
 
   Item it;
-  if (!decode_item(a, it)) return;
-  const ReqInfo rq = request_info(a, it.b);
+  ReqInfo rq;
+  if (!locate_item(a, it, rq)) return;
   if (!rq.ok) {
     if (threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
       st::set_status(a.status, ST_STATUS_BAD_PREFIX);
@@ -875,9 +1052,9 @@ attn_valu_kernel(AttnArgs a) {
   }
   const int rows_b = rq.n * a.G;
   if (it.rblk * R >= rows_b) return;
-  const int k0 = it.split * a.KS;
+  const int k0 = it.split * it.ks;
   if (k0 >= rq.key_end) return;
-  const int k1 = min(k0 + a.KS, rq.key_end);
+  const int k1 = min(k0 + it.ks, rq.key_end);
 
   const int tid = threadIdx.x, r = tid >> 4, c = tid & 15;
   const int row = it.rblk * R + r;
@@ -1047,10 +1224,18 @@ __device__ inline void combine_block_n(const AttnArgs& a, int blk) {
     }
   }
   const int t = grow / a.Hq;
-  const int b = st::request_of(a.node_off, a.B, t);
-  const ReqInfo rq = request_info(a, b);
-  if (!rq.ok || rq.nsplit <= 1) return;
-  const int ns = rq.nsplit;
+  int ns;
+  if (a.balanced) {
+    // recorded by the attention kernel for every node of a request that
+    // passed its checks (a failed one's is stale; clamped, its reads stay in
+    // the workspace)
+    ns = min(max(a.ws_ns[t], 0), a.NS);
+  } else {
+    const int b = st::request_of(a.node_off, a.B, t);
+    const ReqInfo rq = request_info(a, b);
+    ns = rq.ok ? rq.nsplit : 0;
+  }
+  if (ns <= 1) return;
   if (!single) {
 #pragma unroll
     for (int j = 0; j < CHUNK; ++j) {
@@ -1139,7 +1324,9 @@ struct Plan {
   bool stream;  // bf16 streaming MFMA kernel (else fp32 VALU kernel + combine)
   int rwv, rbw; // streaming kernel: 64-row groups per workgroup, 16-row blocks per wave
   int RB, n_rblk, KS, NS, items, per_xcd;
-  size_t ml_bytes, ws_bytes;
+  bool balanced;  // splits sized per request on the device
+  int target;     // workgroups a split plan aims for
+  size_t ml_bytes, ns_off, ws_bytes;
 };
 
 int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_prefix, Plan& p) {
@@ -1153,6 +1340,20 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
   const long rows_max = (long)t->max_nodes * G;
   long gran = 16;  // split granularity in keys
   p.stream = dtype == ST_BF16;
+  // Batches of 2..64 requests (bf16): splits sized per request on the device
+  // (balanced_lane), from the sizes in device memory, so that the workgroups
+  // of short and long requests stream about as many keys each.
+  const int forced_ks = ovr.attn_split_keys;
+  const int force_bal = ovr.attn_balance;
+  // The planner's choice takes it only where a split can happen at all: one
+  // workgroup per request and kv head must leave room under the workgroup
+  // target of the shape it would run (below: (4,2), two per CU, above 64 rows
+  // a kv head; one per CU up to 64).
+  const long bal_target =
+      ovr.attn_target_wg > 0 ? ovr.attn_target_wg : rows_max > 64 ? 512 : 256;
+  const bool balanced =
+      p.stream && t->B <= 64 && forced_ks == 0 &&
+      (force_bal == 2 || (force_bal == 0 && t->B >= 2 && (long)t->B * Hkv < bal_target));
   if (!p.stream) {
     p.rwv = p.rbw = 0;
     p.RB = 16;
@@ -1171,6 +1372,11 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
     // longer than its loads, so run two workgroups per CU (32 rows a
     // wavefront, half the registers), whose softmax and MFMA phases overlap.
     if (rows_max > 64) p.rbw = 2;
+    // With splits sized per request (below), up to 128 rows a kv head go to
+    // one workgroup of four row groups: (4,2) reads each key once, where (2,2)
+    // needs two workgroups whose splits must run side by side, and its
+    // one-key-group ring keeps three chunks in flight.
+    if (balanced && rows_max > 64) p.rwv = 4;
     // 0..6: (1,1) (1,2) (1,4) (2,4) (4,4), then two workgroups per CU: (2,2) (4,2)
     const int forced = ovr.attn_shape;
     if (forced >= 0 && forced <= 6) {
@@ -1194,7 +1400,6 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
   if (ns < 1) ns = 1;
   long ks = (keys_max + ns - 1) / ns;
   ks = (ks + gran - 1) / gran * gran;
-  const int forced_ks = ovr.attn_split_keys;
   if (forced_ks > 0) ks = (forced_ks + gran - 1) / gran * gran;
   const long kmax = (keys_max + gran - 1) / gran * gran;
   // the streaming kernel wants at least two chunks per wavefront; the fp32
@@ -1203,13 +1408,29 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
   if (ks > kmax) ks = kmax;
   p.KS = (int)ks;
   p.NS = (int)((keys_max + ks - 1) / ks);
-  const long items = base * p.NS;
+  long items = base * p.NS;
+  p.target = (int)target;
+  // Balanced plans: NS becomes the most splits a request may take (the
+  // uniform plan's count, at least 4, at most one per two chunks of the
+  // longest request).  The grid bounds the device's layout: at most `target`
+  // items when any request is split, else one per (request, head, row block),
+  // plus each request's padding to a multiple of 8 units.
+  p.balanced = balanced;
+  if (p.balanced) {
+    const long cap = (kmax / 32 + 1) / 2;
+    p.NS = (int)std::max(1L, std::min(std::max((long)p.NS, 4L), cap));
+    items = std::min(base * p.NS, target + base) + 7L * t->B * p.n_rblk;
+    p.KS = 0;
+  }
   if (items > (1L << 30)) return ST_E_UNSUPPORTED;
   p.items = (int)items;
   p.per_xcd = (p.items + 7) / 8;
   const size_t TH = (size_t)t->total_nodes * Hq;
   p.ml_bytes = p.NS > 1 ? st::align_up((size_t)p.NS * TH * sizeof(float2), 256) : 0;
   p.ws_bytes = p.NS > 1 ? p.ml_bytes + (size_t)p.NS * TH * D * sizeof(float) : 0;
+  // balanced plans: the nodes' split counts after the partials
+  p.ns_off = st::align_up(p.ws_bytes, 256);
+  if (p.balanced) p.ws_bytes = p.ns_off + (size_t)t->total_nodes * sizeof(int32_t);
   return ST_OK;
 }
 
@@ -1219,7 +1440,7 @@ int st::attention_workgroups(const st_tree* tree, int Hq, int Hkv, int D, st_dty
                              int max_prefix) {
   Plan p;
   if (make_plan(tree, Hq, Hkv, D, dtype, max_prefix, p)) return 0;
-  return p.items;
+  return 8 * p.per_xcd;  // the grid: every workgroup can take an argmax slice
 }
 
 extern "C" size_t st_tree_attention_workspace(const st_tree* tree, int Hq, int Hkv, int D,
@@ -1257,6 +1478,7 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
   a.lse = lse;
   a.ws_ml = p.ws_bytes ? (float2*)workspace : nullptr;
   a.ws_acc = p.ws_bytes ? (float*)((char*)workspace + p.ml_bytes) : nullptr;
+  a.ws_ns = p.balanced ? (int32_t*)((char*)workspace + p.ns_off) : nullptr;
   a.status = status;
   a.B = tree->B;
   a.T = tree->total_nodes;
@@ -1273,6 +1495,9 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
   a.n_rblk = p.n_rblk;
   a.items = p.items;
   a.per_xcd = p.per_xcd;
+  a.balanced = p.balanced ? 1 : 0;
+  a.target = p.target;
+  a.cmax = (int)std::min<long>(((long)max_prefix + tree->max_nodes + kCK - 1) / kCK, 1L << 30);
   a.scale_log2 = scale * kLog2e;
   a.pg = paging ? *paging : st::KvPaging{nullptr, 0, 0, 0};
   a.am = st::ArgmaxJob{nullptr, nullptr, 0, 0, 0, nullptr};

@@ -36,6 +36,7 @@ struct KvPaging {
 struct TestingPlan {
   int attn_shape = -1, attn_target_wg = 0, attn_split_keys = 0;
   int linear_ksplit = 0, linear_stages = 0;
+  int attn_balance = 0;
 };
 const TestingPlan& testing_plan();
 

@@ -140,7 +140,7 @@ extern "C" int st_verification_step_ex(const st_tree* tree, const st_step* s, in
 
 namespace {
 
-constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr size_t kScratchBytes = (size_t)64 << 20;
 __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 // The device address of `scratch` on the current device, looked up on the

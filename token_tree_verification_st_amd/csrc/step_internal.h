@@ -55,7 +55,8 @@ int tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dt
                         void* stream, const CompactArgs* compact,
                         const ArgmaxJob* argmax = nullptr, const KvPaging* paging = nullptr);
 
-// Work items (workgroups with work) of the attention plan for these sizes.
+// Workgroups of the attention launch for these sizes: each one, with an item
+// or without, can take one vocab argmax slice.
 int attention_workgroups(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype,
                          int max_prefix);
 
