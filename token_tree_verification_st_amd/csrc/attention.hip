@@ -31,6 +31,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace {
 
@@ -548,7 +549,9 @@ __device__ __forceinline__ void chunk_dma(uint16_t* sK, uint16_t* sV, const Attn
 }
 
 // One wavefront's work on one 32-key chunk for its RBW row blocks.
-template <int D, int RBW>
+// NA <= RBW: the row blocks computed (the first NA; a wavefront whose later
+// row blocks lie wholly past the request's rows leaves them untouched).
+template <int D, int RBW, int NA = RBW>
 __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t* sV,
                                               const uint64_t* sM, int kt, int P, int k1,
                                               float c, int r16, int grp,
@@ -566,7 +569,7 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
   }
   f32x4 s[RBW][2];
 #pragma unroll
-  for (int rb = 0; rb < RBW; ++rb)
+  for (int rb = 0; rb < NA; ++rb)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -581,7 +584,7 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
     const int t0 = kt - P, nv = k1 - kt;
     const uint32_t in_range = nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
+    for (int rb = 0; rb < NA; ++rb) {
       const uint64_t* mr = sM + (rb * 16 + r16) * 4;
       uint32_t win;
       if (t0 >= 0) {
@@ -606,7 +609,7 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
   float mc[RBW];
   bool any = false;
 #pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) {
+  for (int rb = 0; rb < NA; ++rb) {
     float t = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
                     fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
     t = xor16_max(t);
@@ -616,7 +619,7 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
   }
   if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
+    for (int rb = 0; rb < NA; ++rb) {
       const bool need = mc[rb] > m[rb] + kLazy;
       const float alpha = need ? fast_exp2(m[rb] - mc[rb]) : 1.f;
       m[rb] = need ? mc[rb] : m[rb];
@@ -627,7 +630,7 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
   }
   bf16x8 pb[RBW];
 #pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) {
+  for (int rb = 0; rb < NA; ++rb) {
     const float nm = m[rb] == -INFINITY ? 0.f : -m[rb];
     float ps = 0.f;
 #pragma unroll
@@ -659,7 +662,7 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
       const bf16x8 vf = __builtin_bit_cast(
           bf16x8, __builtin_shufflevector(t[2 * i], t[2 * i + 1], 0, 1, 2, 3));
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
+      for (int rb = 0; rb < NA; ++rb)
         acc[rb][d0 + i] =
             __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb], acc[rb][d0 + i], 0, 0, 0);
     }
@@ -913,30 +916,41 @@ attn_stream_kernel(AttnArgs a) {
   } else {
     // A ring shared by the row groups of a key group: at the top of round r
     // (after the barrier, so every row group is done with chunk r - 1) refill
-    // the stage chunk r - 1 used with chunk r + NSTAGE - 1.
-    int stage = 0, refill = NSTAGE - 1;
-    int next = NSTAGE - 1 < nmine ? entry((NSTAGE - 1) * KWV + kg) : 0;  // next refill's block
-    for (int r = 0; r < niter; ++r) {
-      wait_chunks<NSTAGE - 2, DPC>(min(NSTAGE - 2, nmine - r - 1));
-      lds_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      if (r + NSTAGE - 1 < nmine) {
-        uint16_t* sb = ring + refill * STAGE;
-        chunk_dma<D, RWV, PAGED>(sb, sb + kCK * D, a, it, kgp, vgp,
-                                 k0 + ((r + NSTAGE - 1) * KWV + kg) * kCK, klast, rw, lane,
-                                 coff, next);
-        if (PAGED && r + NSTAGE < nmine) next = entry((r + NSTAGE) * KWV + kg);
+    // the stage chunk r - 1 used with chunk r + NSTAGE - 1.  A row group
+    // computes only its row blocks that hold rows of the request (all, half
+    // or none of them); it still loads its share of every chunk.
+    // (one instance of the loop for each count, chosen outside it)
+    auto shared_loop = [&](auto na) {
+      constexpr int NA = decltype(na)::value;
+      int stage = 0, refill = NSTAGE - 1;
+      int next = NSTAGE - 1 < nmine ? entry((NSTAGE - 1) * KWV + kg) : 0;  // next refill's block
+      for (int r = 0; r < niter; ++r) {
+        wait_chunks<NSTAGE - 2, DPC>(min(NSTAGE - 2, nmine - r - 1));
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (r + NSTAGE - 1 < nmine) {
+          uint16_t* sb = ring + refill * STAGE;
+          chunk_dma<D, RWV, PAGED>(sb, sb + kCK * D, a, it, kgp, vgp,
+                                   k0 + ((r + NSTAGE - 1) * KWV + kg) * kCK, klast, rw, lane,
+                                   coff, next);
+          if (PAGED && r + NSTAGE < nmine) next = entry((r + NSTAGE) * KWV + kg);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (NA > 0 && r < nmine) {
+          const uint16_t* sK = ring + stage * STAGE;
+          chunk_compute<D, RBW, (NA > 0 ? NA : 1)>(sK, sK + kCK * D, sMw,
+                                                   k0 + (r * KWV + kg) * kCK, rq.P, k1,
+                                                   a.scale_log2, r16, grp, qf, acc, m, l);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        stage = stage + 1 == NSTAGE ? 0 : stage + 1;
+        refill = refill + 1 == NSTAGE ? 0 : refill + 1;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (r < nmine) {
-        const uint16_t* sK = ring + stage * STAGE;
-        chunk_compute<D, RBW>(sK, sK + kCK * D, sMw, k0 + (r * KWV + kg) * kCK, rq.P, k1,
-                              a.scale_log2, r16, grp, qf, acc, m, l);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      stage = stage + 1 == NSTAGE ? 0 : stage + 1;
-      refill = refill + 1 == NSTAGE ? 0 : refill + 1;
-    }
+    };
+    const int nact = min(max((rows_b - wrow0 + 15) / 16, 0), RBW);
+    if (nact > RBW / 2) shared_loop(std::integral_constant<int, RBW>{});
+    else if (nact > 0) shared_loop(std::integral_constant<int, (RBW > 1 ? RBW / 2 : RBW)>{});
+    else shared_loop(std::integral_constant<int, 0>{});
   }
   if (am) argmax_unit_finish(a, au, amr, am_scratch);
 #pragma unroll
