@@ -468,15 +468,133 @@ struct CutRow {
 // While many entries lie between a row's bounds, each step is a pass over
 // every entry of both rows with one block reduction (masses and counts).
 // Once at most kCutCand entries of each open row remain between its bounds
-// they are gathered into LDS (in thread and entry order) and wavefront 0
-// finishes both searches alone: the mass at or above a trial cut is then the
-// mass at or above the upper bound at the gathering plus the candidates at or
-// above the cut.
+// they are gathered into LDS and wavefront 0 finishes both searches alone: it
+// sorts each row's candidates (largest first) and keeps running sums over
+// them from the mass at or above the upper bound; the cut is the first
+// candidate whose running sum reaches top_p of the total (every larger value
+// keeps less), and the kept mass is the running sum at that value's last
+// copy.  No candidate reaching it leaves the cut at the lower bound.
 //
 // The search starts from a lower bound that is always inside the nucleus:
 // entries below (1 - top_p) Z / (2 V) hold at most half of the mass the
 // nucleus may leave out, so the mass at or above it exceeds top_p Z.  (Its
 // own mass is then unknown until the lower bound first moves.)
+// The smaller and the larger of v and its partner lane's v (lane ^ JJ): DPP
+// within 16-lane rows, permlane swaps across them, a shuffle for JJ = 4.
+template <int JJ>
+__device__ __forceinline__ void minmax_partner(float v, float& mn, float& mx) {
+  if constexpr (JJ == 16 || JJ == 32) {
+    float x0, x1;
+    swap_rows<JJ == 32>(v, x0, x1);
+    mn = fminf(x0, x1);
+    mx = fmaxf(x0, x1);
+  } else {
+    const float p = JJ == 1   ? dpp_f32<0xB1>(v)   // quad_perm [1,0,3,2]
+                    : JJ == 2 ? dpp_f32<0x4E>(v)   // quad_perm [2,3,0,1]
+                    : JJ == 8 ? dpp_f32<0x128>(v)  // row_ror:8
+                              : __shfl_xor(v, JJ);
+    mn = fminf(v, p);
+    mx = fmaxf(v, p);
+  }
+}
+
+// Bitonic sort, largest first, of two sets of kCutLane * 64 values held as
+// x[j] of lane l = element j * 64 + l.  Stage K merges runs of K elements;
+// substage JJ compares elements i and i ^ JJ, the lower one keeping the
+// larger value where bit K of i is clear (the run is ordered largest first)
+// and the smaller where it is set.  JJ >= 64 pairs registers of one lane.
+template <int K, int JJ>
+__device__ __forceinline__ void bitonic_sub(float (&a)[kCutLane], float (&b)[kCutLane],
+                                            int lane) {
+  if constexpr (JJ >= ST_WAVE) {
+    constexpr int R = JJ / ST_WAVE;
+#pragma unroll
+    for (int j = 0; j < kCutLane; ++j) {
+      if (j & R) continue;
+      const bool desc = ((j * ST_WAVE) & K) == 0;
+      const float a0 = a[j], a1 = a[j ^ R], b0 = b[j], b1 = b[j ^ R];
+      a[j] = desc ? fmaxf(a0, a1) : fminf(a0, a1);
+      a[j ^ R] = desc ? fminf(a0, a1) : fmaxf(a0, a1);
+      b[j] = desc ? fmaxf(b0, b1) : fminf(b0, b1);
+      b[j ^ R] = desc ? fminf(b0, b1) : fmaxf(b0, b1);
+    }
+  } else {
+    const bool lower = (lane & JJ) == 0;
+#pragma unroll
+    for (int j = 0; j < kCutLane; ++j) {
+      const bool desc = K < ST_WAVE ? (lane & K) == 0 : ((j * ST_WAVE) & K) == 0;
+      float mn, mx;
+      minmax_partner<JJ>(a[j], mn, mx);
+      a[j] = lower == desc ? mx : mn;
+      minmax_partner<JJ>(b[j], mn, mx);
+      b[j] = lower == desc ? mx : mn;
+    }
+  }
+  if constexpr (JJ > 1) bitonic_sub<K, JJ / 2>(a, b, lane);
+}
+template <int K>
+__device__ __forceinline__ void bitonic_desc(float (&a)[kCutLane], float (&b)[kCutLane],
+                                             int lane) {
+  static_assert(kCutLane * ST_WAVE == 512, "the network below sorts 512 values");
+  bitonic_sub<K, K / 2>(a, b, lane);
+  if constexpr (K < kCutLane * ST_WAVE) bitonic_desc<K * 2>(a, b, lane);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// A row's cut from its candidates sorted largest first (negative: none):
+// running sums from the mass at or above the row's upper bound (fp64, in
+// sorted order), the first candidate whose sum reaches `want` becomes the
+// lower bound with the sum at its value's last copy as its mass, and the row
+// is decided.  An open row with no such candidate keeps its lower bound.
+__device__ inline void sorted_cut(const float (&x)[kCutLane], int lane, CutRow& r) {
+  if (!r.open()) return;  // wave-uniform
+  double run[kCutLane];
+  double carry = r.m_hi;
+#pragma unroll
+  for (int j = 0; j < kCutLane; ++j) {
+    run[j] = carry + wave_incl_scan((double)fmaxf(x[j], 0.f));
+    carry = uniform_f64(readlane_f64(run[j], ST_WAVE - 1));
+  }
+  int fj = -1, fl = 0;
+#pragma unroll
+  for (int j = 0; j < kCutLane; ++j) {
+    const uint64_t m = __ballot(x[j] >= 0.f && run[j] >= r.want);
+    if (fj < 0 && m) {
+      fj = j;
+      fl = __ffsll((unsigned long long)m) - 1;
+    }
+  }
+  if (fj >= 0) {
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < kCutLane; ++j)
+      if (j == fj) v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(x[j]), fl));
+    // the value's last copy (copies are adjacent in the sorted order)
+    int lj = 0, ll = 0;
+#pragma unroll
+    for (int j = 0; j < kCutLane; ++j) {
+      const uint64_t m = __ballot(x[j] == v);
+      if (m) {
+        lj = j;
+        ll = 63 - __clzll((long long)m);
+      }
+    }
+    double kept = 0.0;
+#pragma unroll
+    for (int j = 0; j < kCutLane; ++j)
+      if (j == lj) kept = readlane_f64(run[j], ll);
+    r.lo = __float_as_uint(v);
+    r.m_lo = uniform_f64(kept);
+  }
+  r.hi = r.lo + 1u;
+}
+
 __device__ inline uint32_t nucleus_floor(double z, float top_p, int V, float xmax) {
   const float f = __double2float_rd((1.0 - (double)top_p) * z / (2.0 * V));
   return (f > 0.f && f < xmax) ? __float_as_uint(f) : 0u;
@@ -562,45 +680,14 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
 #pragma unroll
       for (int j = 0; j < kCutLane; ++j) {
         const int q = j * ST_WAVE + lane;
-        xt[j] = q < ct ? c.cand[0][q] : 0.f;
-        xd[j] = q < cd ? c.cand[1][q] : 0.f;
+        xt[j] = q < ct ? c.cand[0][q] : -1.f;
+        xd[j] = q < cd ? c.cand[1][q] : -1.f;
       }
-      // every candidate lies below the upper bounds of the gathering, so the
-      // masses above those bounds are the base of every trial sum
-      const double base_t = rt.m_hi, base_d = rd.m_hi;
-      while (true) {
-        // a row with no candidate strictly between its bounds is decided:
-        // every trial cut in there keeps only the mass above the upper bound
-        const float lt_ = __uint_as_float(rt.lo), ht_ = __uint_as_float(rt.hi);
-        const float ld_ = __uint_as_float(rd.lo), hd_ = __uint_as_float(rd.hi);
-        bool it = false, id = false;
-#pragma unroll
-        for (int j = 0; j < kCutLane; ++j) {
-          it |= xt[j] > lt_ && xt[j] < ht_;
-          id |= xd[j] > ld_ && xd[j] < hd_;
-        }
-        if (__ballot(it) == 0ull) rt.hi = rt.lo + 1u;
-        if (__ballot(id) == 0ull) rd.hi = rd.lo + 1u;
-        if (!(rt.open() || rd.open())) break;  // wave-uniform
-        const uint32_t mt = rt.mid(), md = rd.mid();
-        const float ft = __uint_as_float(mt), fd = __uint_as_float(md);
-        double gt = 0.0, gd = 0.0;
-#pragma unroll
-        for (int j = 0; j < kCutLane; j += 4) {
-          float a = 0.f, b = 0.f;
-#pragma unroll
-          for (int i = j; i < j + 4; ++i) {
-            a += xt[i] >= ft ? xt[i] : 0.f;
-            b += xd[i] >= fd ? xd[i] : 0.f;
-          }
-          gt += (double)a;
-          gd += (double)b;
-        }
-        const double st = uniform_f64(base_t + wave_sum(gt));
-        const double sd = uniform_f64(base_d + wave_sum(gd));
-        rt.take(mt, st, 0);
-        rd.take(md, sd, 0);
-      }
+      // both candidate sets sorted, largest first (a row's missing entries
+      // are -1 and sort last); then each row's cut from running sums
+      bitonic_desc<2>(xt, xd, lane);
+      sorted_cut(xt, lane, rt);
+      sorted_cut(xd, lane, rd);
       if (tid == 0) {
         c.cut[0] = rt.lo;
         c.cut[1] = rd.lo;
