@@ -190,6 +190,16 @@ def test_attention_split_plans(balance, target):
         assert err <= BF16_TOL and lerr <= 1e-3
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_attention_split_plans_batch_limits(B):
+    """64 requests (every lane of the device plan holds one) and 65 (one split
+    size for the batch), mixed lengths, few heads so that splits happen."""
+    wl = _small_case(300 + B, D=64, Hq=2, Hkv=1, B=B, pmax=1200, nmax=20)
+    err, lerr = attention_errors(wl, to_device(wl), derive_mask=True)
+    say(f"B {B}: max-abs {err:.2e} lse {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= 1e-3
+
+
 def test_attention_split_plans_agree():
     """The two split plans of one ragged batch give outputs within the bf16
     rounding of each other, and both set the bad-prefix status for a request

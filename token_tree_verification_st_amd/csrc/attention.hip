@@ -1428,12 +1428,14 @@ int make_plan(const st_tree* t, int Hq, int Hkv, int D, st_dtype dtype, int max_
   // uniform plan's count, at least 4, at most one per two chunks of the
   // longest request).  The grid bounds the device's layout: at most `target`
   // items when any request is split, else one per (request, head, row block),
-  // plus each request's padding to a multiple of 8 units.
+  // plus each request's padding to a multiple of 8 units (none when the kv
+  // heads are a multiple of 8).  Workgroups past the items run the plan and
+  // exit, late in the launch: the bound is kept tight.
   p.balanced = balanced;
   if (p.balanced) {
     const long cap = (kmax / 32 + 1) / 2;
     p.NS = (int)std::max(1L, std::min(std::max((long)p.NS, 4L), cap));
-    items = std::min(base * p.NS, target + base) + 7L * t->B * p.n_rblk;
+    items = std::min(base * p.NS, std::max(target, base)) + (Hkv % 8 ? 7L * t->B * p.n_rblk : 0L);
     p.KS = 0;
   }
   if (items > (1L << 30)) return ST_E_UNSUPPORTED;
