@@ -1317,19 +1317,23 @@ attn_combine_kernel(AttnArgs a) {
   combine_block<Tout, D>(a, blockIdx.x);
 }
 
-// The merge of the splits followed, in the same launch, by the compaction of
-// the accepted paths (blocks n_combine.. : one per request and cache head).
-// The attention kernel has finished reading the tree slots when this starts.
+// The compaction of the accepted paths (the first B * 2 * Hkv blocks: one per
+// request and cache head, each walking its request's tree first) and, in the
+// same launch, the merge of the splits (the blocks after them).  The walks
+// are latency-bound chains, so they are dispatched first and run beside the
+// merge.  The attention kernel has finished reading the tree slots when this
+// starts, and the two parts touch disjoint memory.
 template <typename Tout, int D>
 __global__ void __launch_bounds__(256)
 attn_combine_compact_kernel(AttnArgs a, st::CompactArgs c, int n_combine) {
   const int blk = blockIdx.x;
-  if (blk < n_combine) {
-    combine_block<Tout, D>(a, blk);
+  const int n_compact = c.B * 2 * c.Hkv;
+  if (blk < n_compact) {
+    st::kv_compact_block(c, blk / (2 * c.Hkv), blk % (2 * c.Hkv));
   } else {
-    const int k = blk - n_combine;
-    st::kv_compact_block(c, k / (2 * c.Hkv), k % (2 * c.Hkv));
+    combine_block<Tout, D>(a, blk - n_compact);
   }
+  (void)n_combine;
 }
 
 // ---------------------------------------------------------------- planning
