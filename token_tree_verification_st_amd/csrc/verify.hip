@@ -24,6 +24,7 @@
 #include "step_internal.h"
 
 #include <float.h>
+#include <type_traits>
 #include <limits.h>
 
 // Every comparison that decides a token must see the same value wherever it is
@@ -424,12 +425,37 @@ __device__ __forceinline__ double kept_sum(const float (&X)[NPT], float cut, int
 // The search's last phase: one wavefront, at most kCutLane candidates a lane.
 constexpr int kCutLane = 8;
 constexpr int kCutCand = kCutLane * ST_WAVE;  // per row
+// The search's first phase: a histogram of each row's weights over the top
+// 11 bits of their bit patterns (1/8 of a binade a bin), bin masses in
+// integer units of 2^-36 (order-independent exact sums; a weight is at most 1,
+// and the truncation is below 2^-36 a weight).
+constexpr int kBinShift = 21;
+constexpr int kBins = 1 << (32 - kBinShift);
+constexpr double kFix = 68719476736.0;  // 2^36
+// floor(x * 2^36) for 0 <= x <= 1 in fp32 arithmetic: x * 16 splits exactly
+// into its integer part and its fraction (both exact in fp32), the fraction
+// times 2^32 is exact too, and both convert without rounding.
+__device__ __forceinline__ unsigned long long fix36(float x) {
+  const float x16 = x * 16.f;
+  const uint32_t hi = (uint32_t)x16;
+  const uint32_t lo = (uint32_t)((x16 - (float)hi) * 4294967296.f);
+  return ((unsigned long long)hi << 32) | lo;
+}
+struct BinCut {
+  uint32_t lo, hi;
+  double m_lo, m_hi;
+  int n_lo, n_hi, found;
+};
 struct CutLds {
   double red[6 * kMaxWaves];  // two slot sets of three sums
   float cand[2][kCutCand];    // the entries still between the bounds
   int wtot[kMaxWaves];
   uint32_t cut[2];
   double kept[2];
+  unsigned long long hm[2][kBins];  // bin masses
+  int hc[2][kBins];                 // bin counts
+  double wm[2][kMaxWaves], wn[2][kMaxWaves];
+  BinCut hb[2];
 };
 
 // One row's bisection state over fp32 bit patterns: `want` is top_p of the
@@ -475,6 +501,14 @@ struct CutRow {
 // keeps less), and the kept mass is the running sum at that value's last
 // copy.  No candidate reaching it leaves the cut at the lower bound.
 //
+// Before the passes, one histogram pass brackets each row's cut: bin masses
+// and counts of the weights at or above the row's starting bound, suffix sums
+// over the bins (largest first) give the mass and count at or above every
+// bin, and the bin whose suffix first reaches top_p of the total holds the
+// cut.  Its bounds, with the masses and counts at them, start the search, so
+// that the candidates are usually few enough to gather at once (the passes
+// remain for a bin that holds more).
+//
 // The search starts from a lower bound that is always inside the nucleus:
 // entries below (1 - top_p) Z / (2 V) hold at most half of the mass the
 // nucleus may leave out, so the mass at or above it exceeds top_p Z.  (Its
@@ -498,18 +532,17 @@ __device__ __forceinline__ void minmax_partner(float v, float& mn, float& mx) {
   }
 }
 
-// Bitonic sort, largest first, of two sets of kCutLane * 64 values held as
-// x[j] of lane l = element j * 64 + l.  Stage K merges runs of K elements;
-// substage JJ compares elements i and i ^ JJ, the lower one keeping the
-// larger value where bit K of i is clear (the run is ordered largest first)
-// and the smaller where it is set.  JJ >= 64 pairs registers of one lane.
-template <int K, int JJ>
-__device__ __forceinline__ void bitonic_sub(float (&a)[kCutLane], float (&b)[kCutLane],
-                                            int lane) {
+// Bitonic sort, largest first, of two sets of L * 64 values held as x[j] of
+// lane l = element j * 64 + l.  Stage K merges runs of K elements; substage
+// JJ compares elements i and i ^ JJ, the lower one keeping the larger value
+// where bit K of i is clear (the run is ordered largest first) and the
+// smaller where it is set.  JJ >= 64 pairs registers of one lane.
+template <int L, int K, int JJ>
+__device__ __forceinline__ void bitonic_sub(float (&a)[L], float (&b)[L], int lane) {
   if constexpr (JJ >= ST_WAVE) {
     constexpr int R = JJ / ST_WAVE;
 #pragma unroll
-    for (int j = 0; j < kCutLane; ++j) {
+    for (int j = 0; j < L; ++j) {
       if (j & R) continue;
       const bool desc = ((j * ST_WAVE) & K) == 0;
       const float a0 = a[j], a1 = a[j ^ R], b0 = b[j], b1 = b[j ^ R];
@@ -521,7 +554,7 @@ __device__ __forceinline__ void bitonic_sub(float (&a)[kCutLane], float (&b)[kCu
   } else {
     const bool lower = (lane & JJ) == 0;
 #pragma unroll
-    for (int j = 0; j < kCutLane; ++j) {
+    for (int j = 0; j < L; ++j) {
       const bool desc = K < ST_WAVE ? (lane & K) == 0 : ((j * ST_WAVE) & K) == 0;
       float mn, mx;
       minmax_partner<JJ>(a[j], mn, mx);
@@ -530,14 +563,13 @@ __device__ __forceinline__ void bitonic_sub(float (&a)[kCutLane], float (&b)[kCu
       b[j] = lower == desc ? mx : mn;
     }
   }
-  if constexpr (JJ > 1) bitonic_sub<K, JJ / 2>(a, b, lane);
+  if constexpr (JJ > 1) bitonic_sub<L, K, JJ / 2>(a, b, lane);
 }
-template <int K>
-__device__ __forceinline__ void bitonic_desc(float (&a)[kCutLane], float (&b)[kCutLane],
-                                             int lane) {
-  static_assert(kCutLane * ST_WAVE == 512, "the network below sorts 512 values");
-  bitonic_sub<K, K / 2>(a, b, lane);
-  if constexpr (K < kCutLane * ST_WAVE) bitonic_desc<K * 2>(a, b, lane);
+template <int L, int K = 2>
+__device__ __forceinline__ void bitonic_desc(float (&a)[L], float (&b)[L], int lane) {
+  static_assert(L == 1 || L == 2 || L == 4 || L == 8, "a power-of-two count a lane");
+  bitonic_sub<L, K, K / 2>(a, b, lane);
+  if constexpr (K < L * ST_WAVE) bitonic_desc<L, K * 2>(a, b, lane);
 }
 
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
@@ -552,18 +584,19 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 // sorted order), the first candidate whose sum reaches `want` becomes the
 // lower bound with the sum at its value's last copy as its mass, and the row
 // is decided.  An open row with no such candidate keeps its lower bound.
-__device__ inline void sorted_cut(const float (&x)[kCutLane], int lane, CutRow& r) {
+template <int L>
+__device__ inline void sorted_cut(const float (&x)[L], int lane, CutRow& r) {
   if (!r.open()) return;  // wave-uniform
-  double run[kCutLane];
+  double run[L];
   double carry = r.m_hi;
 #pragma unroll
-  for (int j = 0; j < kCutLane; ++j) {
+  for (int j = 0; j < L; ++j) {
     run[j] = carry + wave_incl_scan((double)fmaxf(x[j], 0.f));
     carry = uniform_f64(readlane_f64(run[j], ST_WAVE - 1));
   }
   int fj = -1, fl = 0;
 #pragma unroll
-  for (int j = 0; j < kCutLane; ++j) {
+  for (int j = 0; j < L; ++j) {
     const uint64_t m = __ballot(x[j] >= 0.f && run[j] >= r.want);
     if (fj < 0 && m) {
       fj = j;
@@ -573,12 +606,12 @@ __device__ inline void sorted_cut(const float (&x)[kCutLane], int lane, CutRow& 
   if (fj >= 0) {
     float v = 0.f;
 #pragma unroll
-    for (int j = 0; j < kCutLane; ++j)
+    for (int j = 0; j < L; ++j)
       if (j == fj) v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(x[j]), fl));
     // the value's last copy (copies are adjacent in the sorted order)
     int lj = 0, ll = 0;
 #pragma unroll
-    for (int j = 0; j < kCutLane; ++j) {
+    for (int j = 0; j < L; ++j) {
       const uint64_t m = __ballot(x[j] == v);
       if (m) {
         lj = j;
@@ -587,7 +620,7 @@ __device__ inline void sorted_cut(const float (&x)[kCutLane], int lane, CutRow& 
     }
     double kept = 0.0;
 #pragma unroll
-    for (int j = 0; j < kCutLane; ++j)
+    for (int j = 0; j < L; ++j)
       if (j == lj) kept = readlane_f64(run[j], ll);
     r.lo = __float_as_uint(v);
     r.m_lo = uniform_f64(kept);
@@ -622,9 +655,105 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
             (double)top_p * zt, ft ? -1.0 : zt, 0.0, kUnknown, 0};
   CutRow rd{fd, (uint32_t)__builtin_amdgcn_readfirstlane(both ? __float_as_uint(qmax) + 1u : 1u),
             (double)top_p * zd, fd ? -1.0 : zd, 0.0, kUnknown, 0};
+  {
+    // histogram of the weights at or above the starting bounds
+    for (int i = tid; i < 2 * kBins; i += kNodeBlock) {
+      (&c.hm[0][0])[i] = 0ull;
+      (&c.hc[0][0])[i] = 0;
+    }
+    if (tid < 2) c.hb[tid].found = 0;
+    __syncthreads();
+    const float flt = __uint_as_float(ft), fld = __uint_as_float(fd);
+#pragma unroll
+    for (int e = 0; e < NPT; ++e) {
+      if (P[e] > 0.f && P[e] >= flt) {
+        const int b = (int)(__float_as_uint(P[e]) >> kBinShift);
+        atomicAdd(&c.hm[0][b], fix36(P[e]));
+        atomicAdd(&c.hc[0][b], 1);
+      }
+      if (both && Q[e] > 0.f && Q[e] >= fld) {
+        const int b = (int)(__float_as_uint(Q[e]) >> kBinShift);
+        atomicAdd(&c.hm[1][b], fix36(Q[e]));
+        atomicAdd(&c.hc[1][b], 1);
+      }
+    }
+    __syncthreads();
+    // suffix sums, largest bin first: thread t holds bins kBins-1-2t and
+    // kBins-2-2t; integers below 2^53, so every double sum is exact
+    const int w = tid / ST_WAVE, b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
+    double m0[2], m1[2], n0[2], n1[2], im[2], in_[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      m0[r] = (double)c.hm[r][b0];
+      m1[r] = (double)c.hm[r][b1];
+      n0[r] = (double)c.hc[r][b0];
+      n1[r] = (double)c.hc[r][b1];
+      im[r] = wave_incl_scan(m0[r] + m1[r]);
+      in_[r] = wave_incl_scan(n0[r] + n1[r]);
+      if (lane == ST_WAVE - 1) {
+        c.wm[r][w] = im[r];
+        c.wn[r][w] = in_[r];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (r == 1 && !both) break;
+      double pm = 0.0, pn = 0.0;  // the waves before this one (all read at once)
+#pragma unroll
+      for (int k = 0; k < kMaxWaves; ++k) {
+        const double a = c.wm[r][k], b = c.wn[r][k];
+        pm += k < w ? a : 0.0;
+        pn += k < w ? b : 0.0;
+      }
+      const double am = pm + im[r] - (m0[r] + m1[r]);  // mass of the bins above b0
+      const double an = pn + in_[r] - (n0[r] + n1[r]);
+      const CutRow& row = r ? rd : rt;
+      const double wf = row.want * kFix;
+      const uint32_t floor_bits = r ? fd : ft;
+      // the crossing bin: its suffix reaches top_p of the total, the bins
+      // above it do not (exactly one bin of one thread)
+      int hit = -1;
+      double sa = 0.0, sn = 0.0, bm = 0.0, bn = 0.0;
+      if (am < wf && am + m0[r] >= wf) {
+        hit = b0;
+        sa = am;
+        sn = an;
+        bm = m0[r];
+        bn = n0[r];
+      } else if (am + m0[r] < wf && am + m0[r] + m1[r] >= wf) {
+        hit = b1;
+        sa = am + m0[r];
+        sn = an + n0[r];
+        bm = m1[r];
+        bn = n1[r];
+      }
+      if (hit >= 0) {
+        const uint32_t blo = (uint32_t)hit << kBinShift;
+        const unsigned long long bhi = (unsigned long long)(hit + 1) << kBinShift;
+        c.hb[r] = BinCut{blo > floor_bits ? blo : floor_bits,
+                         (uint32_t)(bhi > 0xFFFFFFFFull ? 0xFFFFFFFFull : bhi),
+                         (sa + bm) / kFix, sa / kFix, (int)(sn + bn), (int)sn, 1};
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (r == 1 && !both) break;
+      if (__builtin_amdgcn_readfirstlane(c.hb[r].found)) {
+        CutRow& row = r ? rd : rt;
+        row.lo = (uint32_t)__builtin_amdgcn_readfirstlane(c.hb[r].lo);
+        row.hi = (uint32_t)__builtin_amdgcn_readfirstlane(c.hb[r].hi);
+        row.m_lo = uniform_f64(c.hb[r].m_lo);
+        row.m_hi = uniform_f64(c.hb[r].m_hi);
+        row.n_lo = __builtin_amdgcn_readfirstlane(c.hb[r].n_lo);
+        row.n_hi = __builtin_amdgcn_readfirstlane(c.hb[r].n_hi);
+      }
+    }
+  }
   int set = 0;
-  bool few = false;
-  while (rt.open() || rd.open()) {  // block-uniform
+  bool few = (!rt.open() || rt.between() <= kCutCand) && (!rd.open() || rd.between() <= kCutCand);
+  while (!few && (rt.open() || rd.open())) {  // block-uniform
     const uint32_t mt = rt.mid(), md = rd.mid();
     int nt = 0, nd = 0;
     double st = kept_sum<VEC, NPT>(P, __uint_as_float(mt), nt);
@@ -640,54 +769,45 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
     if (few) break;
   }
   if (few && (rt.open() || rd.open())) {
-    // gather the candidates: a thread's entries in [lo, hi), placed after
-    // those of the threads before it (counts packed as in the search)
+    // gather the candidates, each row's entries in [lo, hi), into LDS slots
+    // taken from a counter (their order does not matter: they are sorted)
     const float lt = __uint_as_float(rt.lo), ht = __uint_as_float(rt.hi);
     const float ld = __uint_as_float(rd.lo), hd = __uint_as_float(rd.hi);
     const bool ot = rt.open(), od = rd.open();
-    int mine = 0;
-#pragma unroll
-    for (int e = 0; e < NPT; ++e) {
-      mine += (ot && P[e] >= lt && P[e] < ht) ? 1 : 0;
-      mine += (od && Q[e] >= ld && Q[e] < hd) ? 65536 : 0;
-    }
-    int inc = mine;
-#pragma unroll
-    for (int o = 1; o < ST_WAVE; o <<= 1) {
-      const int v = __shfl_up(inc, o, ST_WAVE);
-      inc += lane >= o ? v : 0;
-    }
-    if (lane == ST_WAVE - 1) c.wtot[tid / ST_WAVE] = inc;
+    if (tid < 2) c.wtot[tid] = 0;
     __syncthreads();
-    int off = inc - mine;
-    for (int w = 0; w < tid / ST_WAVE; ++w) off += c.wtot[w];
-    int pt = off & 0xFFFF, pd = off >> 16;
 #pragma unroll
     for (int e = 0; e < NPT; ++e) {
-      if (ot && P[e] >= lt && P[e] < ht) {
+      if (ot && P[e] > 0.f && P[e] >= lt && P[e] < ht) {  // (zeros are never needed)
+        const int pt = atomicAdd(&c.wtot[0], 1);
         if (pt < kCutCand) c.cand[0][pt] = P[e];
-        ++pt;
       }
-      if (od && Q[e] >= ld && Q[e] < hd) {
+      if (od && Q[e] > 0.f && Q[e] >= ld && Q[e] < hd) {
+        const int pd = atomicAdd(&c.wtot[1], 1);
         if (pd < kCutCand) c.cand[1][pd] = Q[e];
-        ++pd;
       }
     }
     __syncthreads();
     if (tid < ST_WAVE) {
       const int ct = ot ? rt.between() : 0, cd = od ? rd.between() : 0;
-      float xt[kCutLane], xd[kCutLane];
-#pragma unroll
-      for (int j = 0; j < kCutLane; ++j) {
-        const int q = j * ST_WAVE + lane;
-        xt[j] = q < ct ? c.cand[0][q] : -1.f;
-        xd[j] = q < cd ? c.cand[1][q] : -1.f;
-      }
       // both candidate sets sorted, largest first (a row's missing entries
-      // are -1 and sort last); then each row's cut from running sums
-      bitonic_desc<2>(xt, xd, lane);
-      sorted_cut(xt, lane, rt);
-      sorted_cut(xd, lane, rd);
+      // are -1 and sort last), by the smallest network that holds them; then
+      // each row's cut from running sums
+      auto finish = [&](auto per_lane) {
+        constexpr int L = decltype(per_lane)::value;
+        float xt[L], xd[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+          const int q = j * ST_WAVE + lane;
+          xt[j] = q < ct ? c.cand[0][q] : -1.f;
+          xd[j] = q < cd ? c.cand[1][q] : -1.f;
+        }
+        bitonic_desc<L>(xt, xd, lane);
+        sorted_cut<L>(xt, lane, rt);
+        sorted_cut<L>(xd, lane, rd);
+      };
+      if (max(ct, cd) <= 2 * ST_WAVE) finish(std::integral_constant<int, 2>{});
+      else finish(std::integral_constant<int, kCutLane>{});
       if (tid == 0) {
         c.cut[0] = rt.lo;
         c.cut[1] = rd.lo;
