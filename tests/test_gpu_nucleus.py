@@ -156,13 +156,15 @@ def _levels(rng, T, V, n):
 
 @pytest.mark.parametrize("pattern,top_p", [("plateaus", 0.9), ("flat", 0.90001),
                                            ("near_total", 0.99999), ("spike", 0.9),
-                                           ("plateaus_draft_probs", 0.7)])
+                                           ("plateaus_draft_probs", 0.7), ("wide", 0.9)])
 def test_nucleus_search_paths(pattern, top_p):
     """Rows that drive the nucleus search down each of its paths at full
     vocabulary: plateaus (thousands of weights tied at the cut, so the bounds
     never hold few enough entries to gather), a flat row (every token kept),
     a nucleus holding all but 1e-5 of the mass (the search may end at its
-    starting bound), one dominant token (a one-token nucleus)."""
+    starting bound), one dominant token (a one-token nucleus), and logits of
+    spread 2.5 (a few hundred weights in the 1/8-binade bin of the cut: the
+    larger sorting network)."""
     rng = np.random.default_rng(500 + len(pattern))
     B = 4
     trees = [tree_random_attach(rng, 24, 5) for _ in range(B)]
@@ -179,6 +181,9 @@ def test_nucleus_search_paths(pattern, top_p):
     elif pattern == "flat":
         wl.logits[:] = 0.0
         wl.draft_logits[:] = 0.0
+    elif pattern == "wide":
+        wl.logits[:] = rng.normal(0.0, 2.5, (T, V)).astype(np.float32)
+        wl.draft_logits[:] = rng.normal(0.0, 2.5, (T, V)).astype(np.float32)
     elif pattern == "near_total":
         wl.logits[:] = rng.normal(0.0, 0.5, (T, V)).astype(np.float32)
         wl.draft_logits[:] = rng.normal(0.0, 0.5, (T, V)).astype(np.float32)
