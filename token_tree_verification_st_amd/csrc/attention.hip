@@ -335,8 +335,10 @@ __device__ inline BalLane balanced_lane(const AttnArgs& a, int lane) {
   // The smallest budget q in [2, cmax] whose items fit in `target`
   // workgroups (cmax: the chunks of the longest possible request, so every
   // request is one split at q = cmax).  With W = sum of hr * c and H = sum of
-  // hr, the items at q lie in [W / q, W / q + H], so q is at least W / target
-  // and, when H < target, at most W / (target - H).  The items only fall as
+  // hr, the items at q are at most W / q + H, so q = W / (target - H) fits
+  // when H < target; they are at least W / q unless the cap NS binds, so the
+  // search starts at W / target (where the cap binds, a larger q than the
+  // smallest that fits may result; every q it picks fits).  The items only fall as
   // q grows: the 64 lanes test 64 budgets spread over the range at once and
   // the first that fits narrows it, until the budgets are consecutive (one
   // round when the range holds at most 64).  The search counts min(NS,

@@ -483,36 +483,6 @@ struct CutRow {
   }
 };
 
-// Nucleus (top-p) cuts of the target and draft weights P and Q (totals zt,
-// zd; largest entries at most pmax, qmax): the largest value `cut` whose mass
-// at or above it still reaches top_p of the total, found by bisection over
-// the bit patterns of non-negative floats (which order like the values).  The
-// kept set {X >= cut} is the smallest set of most likely tokens holding top_p
-// of the mass, with every token tied at the cut.  Entries below the cut are
-// zeroed and zt, zd become the kept mass.  Only P is cut when `both` is false.
-//
-// While many entries lie between a row's bounds, each step is a pass over
-// every entry of both rows with one block reduction (masses and counts).
-// Once at most kCutCand entries of each open row remain between its bounds
-// they are gathered into LDS and wavefront 0 finishes both searches alone: it
-// sorts each row's candidates (largest first) and keeps running sums over
-// them from the mass at or above the upper bound; the cut is the first
-// candidate whose running sum reaches top_p of the total (every larger value
-// keeps less), and the kept mass is the running sum at that value's last
-// copy.  No candidate reaching it leaves the cut at the lower bound.
-//
-// Before the passes, one histogram pass brackets each row's cut: bin masses
-// and counts of the weights at or above the row's starting bound, suffix sums
-// over the bins (largest first) give the mass and count at or above every
-// bin, and the bin whose suffix first reaches top_p of the total holds the
-// cut.  Its bounds, with the masses and counts at them, start the search, so
-// that the candidates are usually few enough to gather at once (the passes
-// remain for a bin that holds more).
-//
-// The search starts from a lower bound that is always inside the nucleus:
-// entries below (1 - top_p) Z / (2 V) hold at most half of the mass the
-// nucleus may leave out, so the mass at or above it exceeds top_p Z.  (Its
-// own mass is then unknown until the lower bound first moves.)
 // The smaller and the larger of v and its partner lane's v (lane ^ JJ): DPP
 // within 16-lane rows, permlane swaps across them, a shuffle for JJ = 4.
 template <int JJ>
@@ -628,6 +598,36 @@ __device__ inline void sorted_cut(const float (&x)[L], int lane, CutRow& r) {
   r.hi = r.lo + 1u;
 }
 
+// Nucleus (top-p) cuts of the target and draft weights P and Q (totals zt,
+// zd; largest entries at most pmax, qmax): the largest value `cut` whose mass
+// at or above it still reaches top_p of the total, searched for over the bit
+// patterns of non-negative floats (which order like the values).  The
+// kept set {X >= cut} is the smallest set of most likely tokens holding top_p
+// of the mass, with every token tied at the cut.  Entries below the cut are
+// zeroed and zt, zd become the kept mass.  Only P is cut when `both` is false.
+//
+// While many entries lie between a row's bounds, each step is a pass over
+// every entry of both rows with one block reduction (masses and counts).
+// Once at most kCutCand entries of each open row remain between its bounds
+// they are gathered into LDS and wavefront 0 finishes both searches alone: it
+// sorts each row's candidates (largest first) and keeps running sums over
+// them from the mass at or above the upper bound; the cut is the first
+// candidate whose running sum reaches top_p of the total (every larger value
+// keeps less), and the kept mass is the running sum at that value's last
+// copy.  No candidate reaching it leaves the cut at the lower bound.
+//
+// Before the passes, one histogram pass brackets each row's cut: bin masses
+// and counts of the weights at or above the row's starting bound, suffix sums
+// over the bins (largest first) give the mass and count at or above every
+// bin, and the bin whose suffix first reaches top_p of the total holds the
+// cut.  Its bounds, with the masses and counts at them, start the search, so
+// that the candidates are usually few enough to gather at once (the passes
+// remain for a bin that holds more).
+//
+// The search starts from a lower bound that is always inside the nucleus:
+// entries below (1 - top_p) Z / (2 V) hold at most half of the mass the
+// nucleus may leave out, so the mass at or above it exceeds top_p Z.  (Its
+// own mass is then unknown until the lower bound first moves.)
 __device__ inline uint32_t nucleus_floor(double z, float top_p, int V, float xmax) {
   const float f = __double2float_rd((1.0 - (double)top_p) * z / (2.0 * V));
   return (f > 0.f && f < xmax) ? __float_as_uint(f) : 0u;
