@@ -28,6 +28,8 @@ typedef struct {
   int32_t linear_stages;   /* 0 or 4: planner's choice (four-stage ring); 8: eight stages  */
   int32_t attn_balance;    /* 0: planner's choice; 1: one split size for the whole batch;
                               2: splits sized per request on the device (bf16, B <= 64)    */
+  int32_t step_serial;     /* 0: planner's choice; 1: the verification step enqueues every
+                              launch on the caller's stream (no side stream)              */
 } st_testing_plan;
 
 /* Installs `plan` for every later call in the process; NULL restores the

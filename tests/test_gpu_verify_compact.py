@@ -401,3 +401,32 @@ def test_one_call_step_argmax_in_attention_with_idle_workgroups():
     stp.verification_step(c, fused=True)
     torch.cuda.synchronize()
     assert status_of(c) & 4
+
+
+@pytest.mark.parametrize("name,top_p", [("tiny_fp32", 1.0), ("stochastic_tree", 1.0),
+                                        ("stochastic_chain", 0.9), ("llama7b", 1.0)])
+def test_step_side_stream_equals_serial(name, top_p):
+    """The step's acceptance kernel on the side stream beside attention (the
+    default) gives what the same launches give in order on one stream, bit for
+    bit, on two steps in a row (the second reuses the side stream's events)."""
+    wl = make_workload(name, 0)
+    stochastic = "stochastic" in wl.steps
+    outs = []
+    for serial in (1, 0, 0):
+        dw = to_device(wl)
+        with plan_override(step_serial=serial):
+            stp.verification_step(dw, stochastic=stochastic, top_p=top_p)
+            torch.cuda.synchronize()
+        outs.append(dw)
+    ref = outs[0]
+    for dw in outs[1:]:
+        for k in ("accept_len", "accept_nodes", "out_tokens", "src_slot", "new_len", "status",
+                  "out", "lse"):
+            assert torch.equal(ref.buf[k], dw.buf[k]), k
+        if stochastic:
+            assert torch.equal(ref.buf["near_ties"], dw.buf["near_ties"])
+        assert torch.equal(ref.k_cache, dw.k_cache) and torch.equal(ref.v_cache, dw.v_cache)
+    assert status_of(ref) == 0
+    if stochastic and top_p == 1.0:
+        stochastic_parity(wl, outs[1], label=name)
+    say(f"{name} top_p={top_p}: side-stream step equals the serial step")

@@ -57,7 +57,8 @@ class StTestingPlan(ctypes.Structure):
     """Mirror of st_testing_plan (include/st_testing.h)."""
     _fields_ = [("attn_shape", ctypes.c_int32), ("attn_target_wg", ctypes.c_int32),
                 ("attn_split_keys", ctypes.c_int32), ("linear_ksplit", ctypes.c_int32),
-                ("linear_stages", ctypes.c_int32), ("attn_balance", ctypes.c_int32)]
+                ("linear_stages", ctypes.c_int32), ("attn_balance", ctypes.c_int32),
+                ("step_serial", ctypes.c_int32)]
 
 
 _lib = None

@@ -1478,7 +1478,7 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
                             const uint64_t* mask, void* out, float* lse, void* workspace,
                             size_t ws_bytes, int32_t* status, void* stream,
                             const st::CompactArgs* compact, const st::ArgmaxJob* argmax,
-                            const st::KvPaging* paging) {
+                            const st::KvPaging* paging, const st::SideLaunch* side) {
   Plan p;
   int rc = make_plan(tree, Hq, Hkv, D, dtype, max_prefix, p);
   if (rc) return rc;
@@ -1558,6 +1558,10 @@ int st::tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtyp
     else hipLaunchKernelGGL((attn_valu_kernel<float, 64>), grid, block, 0, s, a);
   }
   if ((rc = st::check_launch())) return rc;
+  if (side) {
+    if ((rc = side->launch(side->ctx))) return rc;
+    if (hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return ST_E_LAUNCH;
+  }
   const int TH = tree->total_nodes * Hq;
   const int rpb = 256 / (D / 4);
   const int n_combine = p.NS > 1 ? (TH + rpb - 1) / rpb : 0;

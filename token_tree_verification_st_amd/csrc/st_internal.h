@@ -37,6 +37,7 @@ struct TestingPlan {
   int attn_shape = -1, attn_target_wg = 0, attn_split_keys = 0;
   int linear_ksplit = 0, linear_stages = 0;
   int attn_balance = 0;
+  int step_serial = 0;
 };
 const TestingPlan& testing_plan();
 

@@ -2,8 +2,8 @@
 // then the split merge and the KV compaction in one launch, whose workgroups
 // also walk the trees.  For greedy acceptance the vocab argmax runs inside
 // the attention launch when it fits (one 8192-entry slice per workgroup), so
-// the step is two launches; for stochastic acceptance the node kernel runs
-// first.
+// the step is two launches; for stochastic acceptance the node kernel runs on
+// a side stream beside the attention kernel.
 #include "step_internal.h"
 
 #include <math.h>
@@ -15,6 +15,40 @@ namespace {
 size_t verify_ws(const st_tree* t, const st_step* s) {
   return s->draft_logits ? st_verify_stochastic_workspace(t, s->V)
                          : st_verify_greedy_workspace(t, s->V);
+}
+
+// A second stream per device, for the stochastic node kernel of a step: the
+// kernel reads only logits and writes only the verification workspace, so it
+// runs beside the attention kernel, and the merge + compaction launch that
+// walks the trees waits for it.  The stream and its two events are created on
+// a device's first step and kept until the process ends (default priority,
+// non-blocking, events without timing).  Events are re-recorded by every step,
+// so `mu` is held from the fork's record to the join's wait.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+std::mutex side_mu;
+
+// The current device's side stream, or null when one cannot be made (the step
+// then stays on the caller's stream).  Call with side_mu held.
+const SideStream* side_stream_locked() {
+  static SideStream dev_side[64];
+  static bool tried[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& d = dev_side[dev];
+  if (!tried[dev]) {
+    tried[dev] = true;
+    if (hipStreamCreateWithFlags(&d.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&d.join, hipEventDisableTiming) != hipSuccess) {
+      d = SideStream{};
+      (void)hipGetLastError();
+    }
+  }
+  return d.s ? &d : nullptr;
 }
 
 bool step_fields_ok(const st_step* s) {
@@ -39,7 +73,7 @@ namespace {
 // table; s->S_max is then the logical capacity).
 int step_impl(const st_tree* tree, const st_step* s, void* workspace, size_t ws_bytes,
               int32_t* status, void* stream, const st::KvPaging* pg, int draft_probs = 0,
-              float top_p = 1.f) {
+              float top_p = 1.f, bool serial = st::testing_plan().step_serial != 0) {
   int rc = st::check_tree_host(tree);
   if (rc) return rc;
   if (!step_fields_ok(s)) return ST_E_INVALID;
@@ -75,14 +109,10 @@ int step_impl(const st_tree* tree, const st_step* s, void* workspace, size_t ws_
     c.walk = st::kWalkGreedy;
   }
   if (rc) return rc;
-  if (s->draft_logits &&
-      (rc = st::stochastic_node_launch(c.sw, s->logits, s->draft_logits, s->temperature, s->seed,
-                                       s->offset, tree->B, stream, draft_probs, top_p)))
-    return rc;
   // Greedy with bf16 attention: when there is at most one argmax slice per
   // attention workgroup (and V is a multiple of 4), the workgroups reduce them
   // in their prologue (the slice's loads overlap the first K/V chunk's);
-  // otherwise the argmax gets a launch of its own first.
+  // otherwise the argmax gets a launch of its own.
   const st::ArgmaxJob job =
       s->draft_logits ? st::ArgmaxJob{}
                       : st::ArgmaxJob{s->logits, (st::ArgmaxPart*)c.g.part, s->V, c.g.nslices,
@@ -90,12 +120,51 @@ int step_impl(const st_tree* tree, const st_step* s, void* workspace, size_t ws_
   const bool fuse_argmax =
       !s->draft_logits && s->dtype == ST_BF16 && (s->V & 3) == 0 &&
       job.units <= st::attention_workgroups(tree, s->Hq, s->Hkv, s->D, s->dtype, s->max_prefix);
-  if (!s->draft_logits && !fuse_argmax && (rc = st::greedy_argmax_launch(c.g, s->logits, stream)))
-    return rc;
-  return st::tree_attention_impl(tree, s->Hq, s->Hkv, s->D, s->dtype, s->scale, s->q,
-                                 s->k_cache, s->v_cache, s->S_max, s->prefix_len, s->max_prefix,
-                                 nullptr, s->out, s->lse, (char*)workspace + off, aws, status,
-                                 stream, &c, fuse_argmax ? &job : nullptr, pg);
+  const bool own_launch = s->draft_logits || !fuse_argmax;
+  auto acceptance = [&](void* strm) {
+    return s->draft_logits
+               ? st::stochastic_node_launch(c.sw, s->logits, s->draft_logits, s->temperature,
+                                            s->seed, s->offset, tree->B, strm, draft_probs, top_p)
+               : st::greedy_argmax_launch(c.g, s->logits, strm);
+  };
+  auto attention = [&](const st::SideLaunch* side) {
+    return st::tree_attention_impl(tree, s->Hq, s->Hkv, s->D, s->dtype, s->scale, s->q,
+                                   s->k_cache, s->v_cache, s->S_max, s->prefix_len,
+                                   s->max_prefix, nullptr, s->out, s->lse,
+                                   (char*)workspace + off, aws, status, stream, &c,
+                                   fuse_argmax ? &job : nullptr, pg, side);
+  };
+  // The stochastic node kernel goes beside attention.  A greedy argmax launch
+  // stays in order: it is short, and the fork and join cost more than the
+  // overlap gives.
+  if (s->draft_logits && !serial) {
+    std::lock_guard<std::mutex> lock(side_mu);
+    if (const SideStream* ss = side_stream_locked()) {
+      // fork: the side stream starts after the caller's earlier work; the
+      // attention launcher enqueues the acceptance kernel there after its own
+      // kernel and makes the caller's stream wait for `join` before the
+      // merge + compaction launch.
+      if (hipEventRecord(ss->fork, (hipStream_t)stream) != hipSuccess ||
+          hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+        return ST_E_LAUNCH;
+      struct Ctx {
+        decltype(acceptance)* run;
+        const SideStream* ss;
+      } ctx{&acceptance, ss};
+      const st::SideLaunch side{[](void* p) {
+                                  const Ctx& x = *(const Ctx*)p;
+                                  const int r = (*x.run)(x.ss->s);
+                                  if (r) return r;
+                                  return hipEventRecord(x.ss->join, x.ss->s) == hipSuccess
+                                             ? (int)ST_OK
+                                             : (int)ST_E_LAUNCH;
+                                },
+                                &ctx, ss->join};
+      return attention(&side);
+    }
+  }
+  if (own_launch && (rc = acceptance(stream))) return rc;
+  return attention(nullptr);
 }
 
 }  // namespace
@@ -168,6 +237,7 @@ extern "C" int st_verification_step_noalloc(const st_tree* tree, const st_step* 
   if (need > kScratchBytes) return ST_E_WORKSPACE;
   void* ws = scratch_on_current_device();
   if (!ws) return ST_E_LAUNCH;
-  return step_impl(tree, s, ws, kScratchBytes, status, stream, nullptr);
+  // every launch on the caller's stream: no side stream to create on a first call
+  return step_impl(tree, s, ws, kScratchBytes, status, stream, nullptr, 0, 1.f, true);
 }
 

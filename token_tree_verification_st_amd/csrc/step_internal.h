@@ -36,6 +36,14 @@ struct ArgmaxJob {
   int32_t* status;
 };
 
+// Work on another stream that the attention launcher enqueues after its
+// attention kernel: `launch(ctx)` enqueues it and records `join` there.
+struct SideLaunch {
+  int (*launch)(void* ctx);
+  void* ctx;
+  hipEvent_t join;
+};
+
 // Checks the arguments of st_kv_compact and fills CompactArgs (compact.hip).
 int fill_compact_args(int B, int Hkv, int D, st_dtype dtype, void* k_cache, void* v_cache,
                       int S_max, const int32_t* prefix_len, const int32_t* accept_len,
@@ -46,14 +54,17 @@ int fill_compact_args(int B, int Hkv, int D, st_dtype dtype, void* k_cache, void
 // also moves the accepted paths' KV rows (after the attention kernel has read
 // them), or a compaction launch follows when there is nothing to merge; with
 // `argmax` set, the streaming kernel's workgroups also reduce those argmax
-// slices (the fp32 kernel does not: the slices are then launched first)
-// (attention.hip).
+// slices (the fp32 kernel does not: the slices are then launched first);
+// with `side` set, its launch is enqueued right after the attention kernel
+// (on another stream) and the stream waits for its `join` event before the
+// merge (attention.hip).
 int tree_attention_impl(const st_tree* tree, int Hq, int Hkv, int D, st_dtype dtype, float scale,
                         const void* q, const void* k_cache, const void* v_cache, int S_max,
                         const int32_t* prefix_len, int max_prefix, const uint64_t* mask,
                         void* out, float* lse, void* workspace, size_t ws_bytes, int32_t* status,
                         void* stream, const CompactArgs* compact,
-                        const ArgmaxJob* argmax = nullptr, const KvPaging* paging = nullptr);
+                        const ArgmaxJob* argmax = nullptr, const KvPaging* paging = nullptr,
+                        const SideLaunch* side = nullptr);
 
 // Workgroups of the attention launch for these sizes: each one, with an item
 // or without, can take one vocab argmax slice.
