@@ -250,22 +250,25 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // out rather than through the builtin because the compiler, unable to tell
 // these reads from the in-flight direct loads that refill other ring stages,
 // would otherwise wait for every outstanding direct load before the first of
-// them; the kernel's own waits already cover the stage read here.
-__device__ __forceinline__ void ds_read_tr16_x8(const uint32_t (&a)[8], u32x2 (&o)[8]) {
+// them; the kernel's own waits already cover the stage read here.  The read
+// at address a[j] goes to o[2j], the read OFF bytes further on (the key 16
+// rows on: the V swizzle repeats every 8 rows) to o[2j + 1], an immediate
+// offset rather than an address of its own.
+template <int OFF>
+__device__ __forceinline__ void ds_read_tr16_x8(const uint32_t (&a)[4], u32x2 (&o)[8]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
         "=&v"(o[6]), "=&v"(o[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
-        "v"(a[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
       : "memory");
 }
 
@@ -476,6 +479,25 @@ __device__ __forceinline__ float xor32_add(float x) {
                                                   false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// xor16_max and xor32_max of two values at once, in three swaps instead of
+// four.  permlane16_swap(a, b) exchanges a's odd 16-lane rows with b's even
+// ones, permlane32_swap(a, b) a's upper 32 lanes with b's lower ones.  With
+// rows x0 = [a0 a1 a2 a3], x1 = [b0 b1 b2 b3]: the first swap and max give
+// [a0|a1, b0|b1, a2|a3, b2|b3]; the 32-lane swap and max give [A, B, A, B]
+// (A, B the maxima over all four rows); a last 16-lane swap spreads A over
+// one register and B over the other.
+__device__ __forceinline__ void xor_max_pair(float& x0, float& x1) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x1),
+                                                  false, false);
+  const float v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                   false);
+  const float w = fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+  const auto r3 = __builtin_amdgcn_permlane16_swap(__float_as_uint(w), __float_as_uint(w), false,
+                                                   false);
+  x0 = __uint_as_float(r3[0]);
+  x1 = __uint_as_float(r3[1]);
+}
 
 // Wait until at most n chunks (DPC loads each) of this wavefront are in flight.
 template <int N, int DPC>
@@ -509,6 +531,30 @@ struct ChunkOff {
       const int row = inst * RPI + lane / CH, pos = lane % CH;
       k[i] = 2u * (uint32_t)(row * D + 8 * (pos ^ kswz<D>(row)));
       v[i] = 2u * (uint32_t)(row * D + 8 * (pos ^ vswz<D>(row)));
+    }
+  }
+};
+
+// Byte offsets of this lane's LDS fragment reads within a stage's K and V
+// tiles, the same for every chunk: K as the QK^T operand (key row r16, the
+// lane group's 16-byte piece of each 32-dim k-step), V^T through the
+// transposing read (key 4 grp + r16 / 4, one dims block per entry).  The
+// reads of keys 16..31 are these plus 16 rows (both swizzles repeat within
+// 16 rows), an immediate offset.
+template <int D>
+struct FragOff {
+  static constexpr int NKS = D / 32, NDB = D / 16;
+  static constexpr int ROW16 = 16 * D * 2;  // bytes of 16 key rows
+  uint32_t k[NKS], v[NDB];
+  __device__ FragOff(int r16, int grp) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      k[ks] = 2u * (uint32_t)(r16 * D + 8 * ((4 * ks + grp) ^ kswz<D>(r16)));
+    const int jq = r16 >> 2, qq = r16 & 3, key1 = 4 * grp + jq;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int ch = 2 * db + (qq >> 1), sub = 4 * (qq & 1);
+      v[db] = 2u * (uint32_t)(key1 * D + 8 * (ch ^ vswz<D>(key1)) + sub);
     }
   }
 };
@@ -555,6 +601,7 @@ __device__ __forceinline__ void chunk_dma(uint16_t* sK, uint16_t* sV, const Attn
 // row blocks lie wholly past the request's rows leaves them untouched).
 template <int D, int RBW, int NA = RBW>
 __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t* sV,
+                                              const FragOff<D>& fo,
                                               const uint64_t* sM, int kt, int P, int k1,
                                               float c, int r16, int grp,
                                               const bf16x8 (&qf)[RBW][D / 32],
@@ -563,12 +610,11 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
   constexpr int NKS = D / 32, NDB = D / 16;
   u32x4 kf[2][NKS];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int key = 16 * kb + r16;
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      kf[kb][ks] = *(const u32x4*)(sK + key * D + 8 * ((4 * ks + grp) ^ kswz<D>(key)));
-  }
+      kf[kb][ks] =
+          *(const u32x4*)((const uint8_t*)sK + fo.k[ks] + kb * FragOff<D>::ROW16);
   f32x4 s[RBW][2];
 #pragma unroll
   for (int rb = 0; rb < NA; ++rb)
@@ -611,12 +657,24 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
   float mc[RBW];
   bool any = false;
 #pragma unroll
+  for (int rb = 0; rb < NA; ++rb) {  // the lane's eight scores, in max3 steps
+    const float t1 = fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), s[rb][0][2]);
+    const float t2 = fmaxf(fmaxf(s[rb][0][3], s[rb][1][0]), s[rb][1][1]);
+    const float t3 = fmaxf(fmaxf(s[rb][1][2], s[rb][1][3]), t1);
+    mc[rb] = fmaxf(t2, t3);
+  }
+#pragma unroll
+  for (int rb = 0; rb < NA; rb += 2) {  // over the four lane groups of each row
+    if (rb + 1 < NA) {
+      xor_max_pair(mc[rb], mc[rb + 1]);
+    } else {
+      mc[rb] = xor16_max(mc[rb]);
+      mc[rb] = xor32_max(mc[rb]);
+    }
+  }
+#pragma unroll
   for (int rb = 0; rb < NA; ++rb) {
-    float t = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
-                    fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
-    t = xor16_max(t);
-    t = xor32_max(t);
-    mc[rb] = t * c;  // c > 0: the max of the scaled scores
+    mc[rb] *= c;  // c > 0: the max of the scaled scores
     any |= mc[rb] > m[rb] + kLazy;
   }
   if (__builtin_amdgcn_ballot_w64(any)) {
@@ -634,31 +692,26 @@ __device__ __forceinline__ void chunk_compute(const uint16_t* sK, const uint16_t
 #pragma unroll
   for (int rb = 0; rb < NA; ++rb) {
     const float nm = m[rb] == -INFINITY ? 0.f : -m[rb];
-    float ps = 0.f;
+    float ps;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float p = fast_exp2(fmaf(s[rb][kb][j], c, nm));
         pb[rb][4 * kb + j] = (__bf16)p;
-        ps += p;
+        ps = kb == 0 && j == 0 ? p : ps + p;
       }
     l[rb] += ps;
   }
-  const int jq = r16 >> 2, qq = r16 & 3;
-  const int key1 = 4 * grp + jq, key2 = key1 + 16;
   // V^T fragments, four dims blocks (eight transposed reads) at a time
+  const uint32_t vb = lds_addr(sV);
 #pragma unroll
   for (int d0 = 0; d0 < NDB; d0 += 4) {
-    uint32_t ad[8];
+    uint32_t ad[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = 2 * (d0 + i) + (qq >> 1), sub = 4 * (qq & 1);
-      ad[2 * i] = lds_addr(sV + key1 * D + 8 * (ch ^ vswz<D>(key1)) + sub);
-      ad[2 * i + 1] = lds_addr(sV + key2 * D + 8 * (ch ^ vswz<D>(key2)) + sub);
-    }
+    for (int i = 0; i < 4; ++i) ad[i] = vb + fo.v[d0 + i];
     u32x2 t[8];
-    ds_read_tr16_x8(ad, t);
+    ds_read_tr16_x8<FragOff<D>::ROW16>(ad, t);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bf16x8 vf = __builtin_bit_cast(
@@ -782,6 +835,7 @@ attn_stream_kernel(AttnArgs a) {
   const int niter = (nch + KWV - 1) / KWV;       // the same for every wavefront
   const int want = min(PRIME, nmine);
   const ChunkOff<D, RWV> coff(rw, lane);
+  const FragOff<D> fo(r16, grp);
   // paged pool: the block of each chunk is looked up one refill ahead
   auto entry = [&](int c) { return PAGED ? table_entry(a, it.b, k0 + c * kCK) : 0; };
 
@@ -902,7 +956,7 @@ attn_stream_kernel(AttnArgs a) {
       wait_chunks<NSTAGE - 1, DPC>(min(NSTAGE - 1, nmine - r - 1));
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t* sK = ring + stage * STAGE;
-      chunk_compute<D, RBW>(sK, sK + kCK * D, sMw, k0 + (r * KWV + kg) * kCK, rq.P, k1,
+      chunk_compute<D, RBW>(sK, sK + kCK * D, fo, sMw, k0 + (r * KWV + kg) * kCK, rq.P, k1,
                             a.scale_log2, r16, grp, qf, acc, m, l);
       __builtin_amdgcn_sched_barrier(0);
       if (r + NSTAGE < nmine) {
@@ -940,7 +994,7 @@ attn_stream_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if (NA > 0 && r < nmine) {
           const uint16_t* sK = ring + stage * STAGE;
-          chunk_compute<D, RBW, (NA > 0 ? NA : 1)>(sK, sK + kCK * D, sMw,
+          chunk_compute<D, RBW, (NA > 0 ? NA : 1)>(sK, sK + kCK * D, fo, sMw,
                                                    k0 + (r * KWV + kg) * kCK, rq.P, k1,
                                                    a.scale_log2, r16, grp, qf, acc, m, l);
         }
