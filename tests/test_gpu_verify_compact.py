@@ -404,11 +404,14 @@ def test_one_call_step_argmax_in_attention_with_idle_workgroups():
 
 
 @pytest.mark.parametrize("name,top_p", [("tiny_fp32", 1.0), ("stochastic_tree", 1.0),
-                                        ("stochastic_chain", 0.9), ("llama7b", 1.0)])
+                                        ("stochastic_chain", 0.9), ("llama7b", 1.0),
+                                        ("ragged_batch", 1.0)])
 def test_step_side_stream_equals_serial(name, top_p):
     """The step's acceptance kernel on the side stream beside attention (the
-    default) gives what the same launches give in order on one stream, bit for
-    bit, on two steps in a row (the second reuses the side stream's events)."""
+    default for the stochastic node kernel and for a greedy argmax over 16 MB
+    or more of logits, as ragged_batch's) gives what the same launches give in
+    order on one stream, bit for bit, on two steps in a row (the second reuses
+    the side stream's events)."""
     wl = make_workload(name, 0)
     stochastic = "stochastic" in wl.steps
     outs = []

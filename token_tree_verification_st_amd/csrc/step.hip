@@ -2,8 +2,8 @@
 // then the split merge and the KV compaction in one launch, whose workgroups
 // also walk the trees.  For greedy acceptance the vocab argmax runs inside
 // the attention launch when it fits (one 8192-entry slice per workgroup), so
-// the step is two launches; for stochastic acceptance the node kernel runs on
-// a side stream beside the attention kernel.
+// the step is two launches; the stochastic node kernel, or a greedy argmax
+// too large for that, runs on a side stream beside the attention kernel.
 #include "step_internal.h"
 
 #include <math.h>
@@ -17,10 +17,10 @@ size_t verify_ws(const st_tree* t, const st_step* s) {
                          : st_verify_greedy_workspace(t, s->V);
 }
 
-// A second stream per device, for the stochastic node kernel of a step: the
-// kernel reads only logits and writes only the verification workspace, so it
-// runs beside the attention kernel, and the merge + compaction launch that
-// walks the trees waits for it.  The stream and its two events are created on
+// A second stream per device, for the acceptance kernel of a step (the
+// stochastic node kernel, or a large greedy argmax): it reads only logits and
+// writes only the verification workspace, so it runs beside the attention
+// kernel, and the merge + compaction launch that walks the trees waits for it.  The stream and its two events are created on
 // a device's first step and kept until the process ends (default priority,
 // non-blocking, events without timing).  Events are re-recorded by every step,
 // so `mu` is held from the fork's record to the join's wait.
@@ -134,10 +134,12 @@ int step_impl(const st_tree* tree, const st_step* s, void* workspace, size_t ws_
                                    (char*)workspace + off, aws, status, stream, &c,
                                    fuse_argmax ? &job : nullptr, pg, side);
   };
-  // The stochastic node kernel goes beside attention.  A greedy argmax launch
-  // stays in order: it is short, and the fork and join cost more than the
-  // overlap gives.
-  if (s->draft_logits && !serial) {
+  // The stochastic node kernel goes beside attention, and so does a greedy
+  // argmax launch over at least 16 MB of logits; a smaller one stays in
+  // order (the fork and join cost more than the overlap gives).
+  const bool big_argmax = !s->draft_logits && !fuse_argmax &&
+                          (size_t)tree->total_nodes * (size_t)s->V * 4 >= ((size_t)16 << 20);
+  if ((s->draft_logits || big_argmax) && !serial) {
     std::lock_guard<std::mutex> lock(side_mu);
     if (const SideStream* ss = side_stream_locked()) {
       // fork: the side stream starts after the caller's earlier work; the
