@@ -787,12 +787,38 @@ attn_stream_kernel(AttnArgs a) {
   const int au = blockIdx.x;
   const bool am = a.am.logits != nullptr && au < a.am.units;
   st::ArgmaxRegs amr;
-  // The item and its request's sizes first, waited for alone: every later
-  // address depends on them.  (Loads issued behind the first chunks' direct
-  // loads, 16 KB a wavefront all over the chip, wait for all of them.)
+  uint16_t* ring = (uint16_t*)lds + kg * NSTAGE * STAGE;
+  const ChunkOff<D, RWV> coff(rw, lane);
+  // The item and its request's sizes, waited for alone: every later address
+  // depends on them.  (Loads issued behind the first chunks' direct loads,
+  // 16 KB a wavefront all over the chip, wait for all of them.)  Contiguous
+  // caches under one split size: the key group's first chunk depends on the
+  // workgroup index alone, so its direct loads go out while the sizes are on
+  // their way (issued after the sizes' scalar loads; rows below the cache
+  // capacity, so in bounds whatever the sizes).  It is kept if all 32 of its
+  // keys belong to the split, else waited for and loaded again clamped.
   Item it;
   ReqInfo rq;
-  if (!locate_item(a, it, rq)) {
+  bool located, spec = false;
+  if (!a.balanced) {
+    located = decode_item(a, it);
+    ReqWords w{0, 0, 0};
+    if (located) {
+      it.ks = a.KS;
+      w = request_load(a, it.b);
+      const int kt0 = it.split * a.KS + kg * kCK;
+      if (!PAGED && kg * kCK < a.KS && kt0 + kCK <= a.S_max) {
+        const size_t ho = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
+        chunk_dma<D, RWV, false>(ring, ring + kCK * D, a, it, (const uint16_t*)a.k + ho,
+                                 (const uint16_t*)a.v + ho, kt0, kt0 + kCK - 1, rw, lane, coff);
+        spec = true;
+      }
+      rq = request_finish(a, w);
+    }
+  } else {
+    located = locate_item(a, it, rq);
+  }
+  if (!located) {
     if (am) {
       st::argmax_slice_load<true>(a.am.logits, a.am.V, au / a.am.nslices, au % a.am.nslices, amr);
       argmax_unit_finish(a, au, amr, am_scratch);
@@ -804,7 +830,6 @@ attn_stream_kernel(AttnArgs a) {
   const size_t head_off = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
   const uint16_t* kgp = (const uint16_t*)a.k + head_off;
   const uint16_t* vgp = (const uint16_t*)a.v + head_off;
-  uint16_t* ring = (uint16_t*)lds + kg * NSTAGE * STAGE;
   // paged pool: the raw table entries of the first chunks (a chunk's key
   // depends on the split alone; the index is clamped into the table row, and
   // an entry is checked where it is used, for a chunk inside the request's keys)
@@ -819,6 +844,7 @@ attn_stream_kernel(AttnArgs a) {
   const int rows_b = rq.n * a.G;
   const int row0 = it.rblk * ROWS;
   if (!rq.ok || row0 >= rows_b || k0 >= rq.key_end) {
+    if (spec) ST_WAIT_VMCNT(0);
     if (!rq.ok && threadIdx.x == 0 && it.g == 0 && it.split == 0 && it.rblk == 0)
       st::set_status(a.status, ST_STATUS_BAD_PREFIX);
     if (am) {
@@ -834,7 +860,6 @@ attn_stream_kernel(AttnArgs a) {
   const int nmine = (nch - kg + KWV - 1) / KWV;  // chunks kg, kg + KWV, ...
   const int niter = (nch + KWV - 1) / KWV;       // the same for every wavefront
   const int want = min(PRIME, nmine);
-  const ChunkOff<D, RWV> coff(rw, lane);
   const FragOff<D> fo(r16, grp);
   // paged pool: the block of each chunk is looked up one refill ahead
   auto entry = [&](int c) { return PAGED ? table_entry(a, it.b, k0 + c * kCK) : 0; };
@@ -891,7 +916,10 @@ attn_stream_kernel(AttnArgs a) {
     }
 #endif
   }
-  if (nmine > 0)
+  // the speculative first chunk stands if it holds 32 keys of the split
+  const bool spec_ok = spec && nmine > 0 && klast - (k0 + kg * kCK) >= kCK - 1;
+  if (spec && !spec_ok) ST_WAIT_VMCNT(0);  // landed before its stage is loaded again
+  if (nmine > 0 && !spec_ok)
     chunk_dma<D, RWV, PAGED>(ring, ring + kCK * D, a, it, kgp, vgp, k0 + kg * kCK, klast, rw,
                              lane, coff, PAGED ? table_phys(a, e_first[0]) : 0);
 #pragma unroll
