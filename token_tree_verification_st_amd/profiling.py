@@ -90,24 +90,32 @@ def grid_table(trace_csv: str, prefix: str) -> str:
 
 def attention_calls_table(trace_csv: str) -> str:
     """The streaming attention kernel's launches split by what follows them on
-    the stream: the split merge (a plain st_tree_attention call) or the
-    merge + compaction launch (the one-call step), with the plain calls'
+    the same hardware queue: the split merge (a plain st_tree_attention call)
+    or the merge + compaction launch (the one-call step, whose acceptance
+    kernel may run beside it on another queue), with the plain calls'
     duration from the streaming kernel's start to the merge's end."""
     rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
-    plain, step, call = [], [], []
-    for i, r in enumerate(rows[:-1]):
-        if not _short(r["Kernel_Name"]).startswith("attn_stream_kernel"):
-            continue
-        nxt = _short(rows[i + 1]["Kernel_Name"])
-        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        if nxt.startswith("attn_combine_kernel"):
-            plain.append(dur)
-            call.append((int(rows[i + 1]["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        elif nxt.startswith("attn_combine_compact_kernel"):
-            step.append(dur)
-    out = ["", "attn_stream_kernel by caller (the launch that follows it):", "",
+    by_queue = defaultdict(list)
+    for r in rows:
+        by_queue[r["Queue_Id"]].append(r)
+    plain, single, step, call = [], [], [], []
+    for q in by_queue.values():
+        for i, r in enumerate(q[:-1]):
+            if not _short(r["Kernel_Name"]).startswith("attn_stream_kernel"):
+                continue
+            nxt = _short(q[i + 1]["Kernel_Name"])
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            if nxt.startswith("attn_combine_kernel"):
+                plain.append(dur)
+                call.append((int(q[i + 1]["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            elif nxt.startswith("attn_combine_compact_kernel"):
+                step.append(dur)
+            else:
+                single.append(dur)
+    out = ["", "attn_stream_kernel by caller (the launch that follows it on its queue):", "",
            "| launches | count | avg us | min us | max us |", "|---|---|---|---|---|"]
     for name, v in (("st_tree_attention (then the split merge)", plain),
+                    ("st_tree_attention, one split a request (no merge)", single),
                     ("verification step (then merge + compaction)", step),
                     ("st_tree_attention call, stream start to merge end", call)):
         if v:
