@@ -800,12 +800,27 @@ attn_stream_kernel(AttnArgs a) {
   Item it;
   ReqInfo rq;
   bool located, spec = false;
+  // paged pool: the raw table entries of the first chunks (a chunk's key
+  // depends on the split alone; the index is clamped into the table row, and
+  // an entry is checked where it is used, for a chunk inside the request's
+  // keys), loaded beside the sizes when the item is known without them
+  int e_first[PRIME];
+  auto first_entries = [&]() {
+#pragma unroll
+    for (int s = 0; s < PRIME; ++s)
+      e_first[s] = PAGED ? a.pg.bt[(size_t)it.b * a.pg.bt_stride +
+                                   min((it.split * it.ks + (s * KWV + kg) * kCK) >> a.pg.lbs,
+                                       a.pg.bt_stride - 1)]
+                         : 0;
+  };
   if (!a.balanced) {
     located = decode_item(a, it);
     ReqWords w{0, 0, 0};
     if (located) {
       it.ks = a.KS;
       w = request_load(a, it.b);
+      first_entries();
+      __builtin_amdgcn_sched_barrier(0);  // both sets of loads issued before either wait
       const int kt0 = it.split * a.KS + kg * kCK;
       if (!PAGED && kg * kCK < a.KS && kt0 + kCK <= a.S_max) {
         const size_t ho = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
@@ -817,6 +832,7 @@ attn_stream_kernel(AttnArgs a) {
     }
   } else {
     located = locate_item(a, it, rq);
+    if (located) first_entries();
   }
   if (!located) {
     if (am) {
@@ -830,16 +846,6 @@ attn_stream_kernel(AttnArgs a) {
   const size_t head_off = ((size_t)it.b * a.Hkv + it.g) * (size_t)a.S_max * D;
   const uint16_t* kgp = (const uint16_t*)a.k + head_off;
   const uint16_t* vgp = (const uint16_t*)a.v + head_off;
-  // paged pool: the raw table entries of the first chunks (a chunk's key
-  // depends on the split alone; the index is clamped into the table row, and
-  // an entry is checked where it is used, for a chunk inside the request's keys)
-  int e_first[PRIME];
-#pragma unroll
-  for (int s = 0; s < PRIME; ++s)
-    e_first[s] = PAGED ? a.pg.bt[(size_t)it.b * a.pg.bt_stride +
-                                 min((k0 + (s * KWV + kg) * kCK) >> a.pg.lbs,
-                                     a.pg.bt_stride - 1)]
-                       : 0;
 
   const int rows_b = rq.n * a.G;
   const int row0 = it.rblk * ROWS;
