@@ -396,23 +396,28 @@ __device__ inline BalLane balanced_lane(const AttnArgs& a, int lane) {
 }
 
 // The grid of a balanced plan: request b takes a run of workgroups [base,
-// base + size), requests in order, with its units padded to a multiple of 8:
-// unit j = 8 * grp + x of the request sits at base + grp * 8 * rb + r * 8 + x
-// for row block r.  Workgroups go round-robin over the 8 XCDs (blockIdx % 8),
-// so a request's units are dealt over the XCDs and the row blocks of one
-// unit, which read the same keys, follow each other on one XCD (its L2 serves
-// the second).  Workgroups of a padding unit have no item.
+// base + size), with its units padded to a multiple of 8: unit j = 8 * grp + x
+// of the request sits at base + grp * 8 * rb + r * 8 + x for row block r.
+// Workgroups go round-robin over the 8 XCDs (blockIdx % 8), so a request's
+// units are dealt over the XCDs and the row blocks of one unit, which read
+// the same keys, follow each other on one XCD (its L2 serves the second).
+// Workgroups of a padding unit have no item.  The runs go longest item first
+// (most chunks per split, then request order): workgroups are dispatched in
+// index order and the later ones share a CU with an earlier one, whose
+// first chunks their own queue behind, so the longest items start first.
 __device__ inline void balanced_order(const AttnArgs& a, const BalLane& L, int lane, int& base,
                                       int& size, int& total) {
   const int units = lane < a.B ? a.Hkv * L.ns : 0;
   size = ((units + 7) & ~7) * L.rb;
+  const int key = lane < a.B ? L.kc : -1;
   base = 0;
   total = 0;
   for (int j = 0; j < a.B; j += 4) {  // lanes past B have size 0 (B <= 64)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int sj = __builtin_amdgcn_readlane(size, j + u);
-      base += j + u < lane ? sj : 0;
+      const int kj = __builtin_amdgcn_readlane(key, j + u);
+      base += (kj > key || (kj == key && j + u < lane)) ? sj : 0;
       total += sj;
     }
   }
