@@ -433,3 +433,53 @@ def test_step_side_stream_equals_serial(name, top_p):
     if stochastic and top_p == 1.0:
         stochastic_parity(wl, outs[1], label=name)
     say(f"{name} top_p={top_p}: side-stream step equals the serial step")
+
+
+def test_step_concurrent_callers_share_the_side_stream():
+    """Two host threads, each stepping on its own stream, share the device's
+    side stream and its events: every step equals the serial one bit for bit
+    (stochastic_chain with its node kernel beside attention, ragged_batch with
+    its large argmax beside attention)."""
+    import threading
+    wls = {name: make_workload(name, 0) for name in ("stochastic_chain", "ragged_batch")}
+    stoch = {name: "stochastic" in wl.steps for name, wl in wls.items()}
+    keys = ("accept_len", "accept_nodes", "out_tokens", "src_slot", "new_len", "status", "out",
+            "lse")
+    ref = {}
+    with plan_override(step_serial=1):
+        for name, wl in wls.items():
+            dw = to_device(wl)
+            stp.verification_step(dw, stochastic=stoch[name])
+            torch.cuda.synchronize()
+            ref[name] = ({k: dw.buf[k].clone() for k in keys}, dw.k_cache.clone())
+    reps = 6
+    got = {name: [] for name in wls}
+    errors = []
+
+    def worker(name):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(reps):
+                    dw = to_device(wls[name])
+                    torch.cuda.current_stream().wait_stream(torch.cuda.default_stream())
+                    stp.verification_step(dw, stochastic=stoch[name])
+                    s.synchronize()
+                    got[name].append(({k: dw.buf[k].clone() for k in keys}, dw.k_cache.clone()))
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(name,)) for name in wls]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for name in wls:
+        assert len(got[name]) == reps
+        for bufs, kc in got[name]:
+            for k in keys:
+                assert torch.equal(bufs[k], ref[name][0][k]), (name, k)
+            assert torch.equal(kc, ref[name][1]), name
+    say(f"two threads x {reps} steps on their own streams equal the serial steps")
