@@ -20,9 +20,11 @@
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless marked [host].  The caller owns all
- *     memory; the library never allocates, frees or synchronises.  Every call
- *     enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL is
- *     the default stream) and returns at once.
+ *     memory; the library never allocates device memory, frees or
+ *     synchronises.  Every call enqueues its kernels on `stream` (a
+ *     hipStream_t passed as void*; NULL is the default stream) and returns at
+ *     once.  (The one-call step also uses a stream of its own on each device,
+ *     ordered after and before `stream` by events: see st_verification_step.)
  *   - Request b owns tree nodes node_off[b] .. node_off[b+1]-1 (N_b >= 1
  *     nodes).  Local node 0 is the root, the last token the target already
  *     emitted; parent[] holds request-local indices with parent[root] = -1
@@ -281,6 +283,18 @@ int st_kv_compact_paged(int B, int Hkv, int D, st_dtype dtype, void* k_pool, voi
  * tree slots (it shares the launch that merges the attention splits), so the
  * three kernels need no other ordering.  All fields are checked before
  * anything is enqueued.
+ *
+ * The acceptance kernel when it is a launch of its own (stochastic
+ * acceptance, or a greedy vocab argmax over 16 MB or more of logits) runs
+ * beside the attention kernel on a second stream of the library's: it starts
+ * after the work enqueued on `stream` before the call (an event recorded on
+ * `stream`), and the launch that follows on `stream` waits for it (an event
+ * recorded on the second stream), so to the caller the step is ordered on
+ * `stream` as if it had one stream.  That stream (default priority,
+ * non-blocking) and its two events are created on the first such step on
+ * each device and kept until the process ends; a mutex orders concurrent
+ * callers' use of the events.  Under HIP graph capture of `stream` the two
+ * streams become parallel branches of the captured graph.
  */
 typedef struct {
   int32_t Hq, Hkv, D;
