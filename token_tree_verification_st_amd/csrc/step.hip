@@ -20,10 +20,11 @@ size_t verify_ws(const st_tree* t, const st_step* s) {
 // A second stream per device, for the acceptance kernel of a step (the
 // stochastic node kernel, or a large greedy argmax): it reads only logits and
 // writes only the verification workspace, so it runs beside the attention
-// kernel, and the merge + compaction launch that walks the trees waits for it.  The stream and its two events are created on
-// a device's first step and kept until the process ends (default priority,
-// non-blocking, events without timing).  Events are re-recorded by every step,
-// so `mu` is held from the fork's record to the join's wait.
+// kernel, and the merge + compaction launch that walks the trees waits for
+// it.  The stream and its two events are created on a device's first such
+// step and kept until the process ends (default priority, non-blocking,
+// events without timing).  Every step re-records the events, so `side_mu` is
+// held from the fork's record to the join's wait.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
@@ -97,7 +98,8 @@ int step_impl(const st_tree* tree, const st_step* s, void* workspace, size_t ws_
 
   // Each compaction workgroup of the last launch walks its request's tree
   // itself (a few microseconds of latency-bound work that then needs no
-  // launch of its own).  Stochastic: the node kernel goes first.
+  // launch of its own).  The walk's inputs (node verdicts or argmax partials)
+  // come from the acceptance kernel, launched below.
   if (s->draft_logits) {
     rc = st::stochastic_prepare(tree, s->V, s->tokens, s->logits, s->draft_logits,
                                 s->temperature, s->accept_len, s->accept_nodes, s->out_tokens,
