@@ -294,3 +294,24 @@ def test_attention_host_errors():
                                    dw.buf["mask"].data_ptr(), dw.buf["out"].data_ptr(), None,
                                    dw.buf["attn_ws"].data_ptr(), need - 1, None, None)
         assert rc == -3
+
+
+@pytest.mark.parametrize("shape", [-1, 0, 1, 2, 5, 6])
+@pytest.mark.parametrize("D", [128, 64])
+def test_attention_first_chunk_before_sizes(shape, D):
+    """One split size for the batch (the plan under which each wavefront's
+    first chunk is loaded before the request sizes arrive), 64-key splits: a
+    short request has a split whose second key group's first chunk straddles
+    its key end (loaded again, clamped) and splits past its keys (their
+    workgroups leave early), over cache slots past every request's keys that
+    hold NaN.  Every row matches the oracle."""
+    rng = np.random.default_rng(77 + D)
+    trees = [tree_random_attach(rng, 20, 6), tree_random_attach(rng, 40, 8),
+             tree_chain(9)]
+    wl = build_workload("early_chunk", rng, dtype="bf16", Hq=4, Hkv=2, D=D, V=0,
+                        prefix_lens=[100, 3000, 1703], trees=trees, max_depth=39,
+                        poison_unused=True)
+    with plan_override(attn_balance=1, attn_split_keys=64, attn_shape=shape):
+        err, lerr = attention_errors(wl, to_device(wl))
+    say(f"shape {shape} D {D}: max-abs {err:.2e} lse {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= 1e-3
