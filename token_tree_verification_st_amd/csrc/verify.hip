@@ -427,12 +427,19 @@ constexpr int kCutLane = 8;
 constexpr int kCutCand = kCutLane * ST_WAVE;  // per row
 // The search's first phase: a histogram of each row's weights over the top
 // 11 bits of their bit patterns (1/8 of a binade a bin), bin masses in
-// integer units of 2^-36 (order-independent exact sums; a weight is at most 1,
-// and the truncation is below 2^-36 a weight).
+// integer units of 2^-36 of the row's total (order-independent exact sums:
+// the weights scaled by the total's reciprocal in fp32 sum to at most
+// 1 + 2^-23, each truncated by less than 2^-36, so a row's sums are within
+// 6e-7 of the total's fractions, inside the 1e-6 tie band).  A bin's count
+// rides in the same 64-bit word above bit 40 (one atomic an entry): masses
+// stay below 2^37, counts below 2^24.
 constexpr int kBinShift = 21;
 constexpr int kBins = 1 << (32 - kBinShift);
 constexpr double kFix = 68719476736.0;  // 2^36
-// floor(x * 2^36) for 0 <= x <= 1 in fp32 arithmetic: x * 16 splits exactly
+constexpr int kCountShift = 40;
+constexpr unsigned long long kCountOne = 1ull << kCountShift;
+constexpr unsigned long long kMassMask = kCountOne - 1ull;
+// floor(x * 2^36) for 0 <= x < 2 in fp32 arithmetic: x * 16 splits exactly
 // into its integer part and its fraction (both exact in fp32), the fraction
 // times 2^32 is exact too, and both convert without rounding.
 __device__ __forceinline__ unsigned long long fix36(float x) {
@@ -452,8 +459,7 @@ struct CutLds {
   int wtot[kMaxWaves];
   uint32_t cut[2];
   double kept[2];
-  unsigned long long hm[2][kBins];  // bin masses
-  int hc[2][kBins];                 // bin counts
+  unsigned long long hm[2][kBins];  // bin masses and counts (kCountShift)
   double wm[2][kMaxWaves], wn[2][kMaxWaves];
   BinCut hb[2];
 };
@@ -657,24 +663,25 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
             (double)top_p * zd, fd ? -1.0 : zd, 0.0, kUnknown, 0};
   {
     // histogram of the weights at or above the starting bounds
-    for (int i = tid; i < 2 * kBins; i += kNodeBlock) {
-      (&c.hm[0][0])[i] = 0ull;
-      (&c.hc[0][0])[i] = 0;
-    }
+    for (int i = tid; i < 2 * kBins; i += kNodeBlock) (&c.hm[0][0])[i] = 0ull;
     if (tid < 2) c.hb[tid].found = 0;
     __syncthreads();
     const float flt = __uint_as_float(ft), fld = __uint_as_float(fd);
+    // (a row without mass, as an all-zero probability row, bins nothing;
+    // both factors are block-uniform, kept in scalar registers)
+    const float it = __uint_as_float(__builtin_amdgcn_readfirstlane(
+        __float_as_uint(zt > 0.0 ? (float)(1.0 / zt) : 0.f)));
+    const float id = __uint_as_float(__builtin_amdgcn_readfirstlane(
+        __float_as_uint(both && zd > 0.0 ? (float)(1.0 / zd) : 0.f)));
 #pragma unroll
     for (int e = 0; e < NPT; ++e) {
       if (P[e] > 0.f && P[e] >= flt) {
         const int b = (int)(__float_as_uint(P[e]) >> kBinShift);
-        atomicAdd(&c.hm[0][b], fix36(P[e]));
-        atomicAdd(&c.hc[0][b], 1);
+        atomicAdd(&c.hm[0][b], fix36(P[e] * it) + kCountOne);
       }
       if (both && Q[e] > 0.f && Q[e] >= fld) {
         const int b = (int)(__float_as_uint(Q[e]) >> kBinShift);
-        atomicAdd(&c.hm[1][b], fix36(Q[e]));
-        atomicAdd(&c.hc[1][b], 1);
+        atomicAdd(&c.hm[1][b], fix36(Q[e] * id) + kCountOne);
       }
     }
     __syncthreads();
@@ -684,10 +691,11 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
     double m0[2], m1[2], n0[2], n1[2], im[2], in_[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      m0[r] = (double)c.hm[r][b0];
-      m1[r] = (double)c.hm[r][b1];
-      n0[r] = (double)c.hc[r][b0];
-      n1[r] = (double)c.hc[r][b1];
+      const unsigned long long h0 = c.hm[r][b0], h1 = c.hm[r][b1];
+      m0[r] = (double)(h0 & kMassMask);
+      m1[r] = (double)(h1 & kMassMask);
+      n0[r] = (double)(h0 >> kCountShift);
+      n1[r] = (double)(h1 >> kCountShift);
       im[r] = wave_incl_scan(m0[r] + m1[r]);
       in_[r] = wave_incl_scan(n0[r] + n1[r]);
       if (lane == ST_WAVE - 1) {
@@ -709,7 +717,8 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
       const double am = pm + im[r] - (m0[r] + m1[r]);  // mass of the bins above b0
       const double an = pn + in_[r] - (n0[r] + n1[r]);
       const CutRow& row = r ? rd : rt;
-      const double wf = row.want * kFix;
+      const double z = r ? zd : zt;
+      const double wf = z > 0.0 ? (double)top_p * kFix : 0.0;  // top_p of the total, bin units
       const uint32_t floor_bits = r ? fd : ft;
       // the crossing bin: its suffix reaches top_p of the total, the bins
       // above it do not (exactly one bin of one thread)
@@ -733,7 +742,7 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
         const unsigned long long bhi = (unsigned long long)(hit + 1) << kBinShift;
         c.hb[r] = BinCut{blo > floor_bits ? blo : floor_bits,
                          (uint32_t)(bhi > 0xFFFFFFFFull ? 0xFFFFFFFFull : bhi),
-                         (sa + bm) / kFix, sa / kFix, (int)(sn + bn), (int)sn, 1};
+                         (sa + bm) * (z / kFix), sa * (z / kFix), (int)(sn + bn), (int)sn, 1};
       }
     }
     __syncthreads();
