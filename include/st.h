@@ -194,7 +194,9 @@ size_t st_verify_stochastic_workspace(const st_tree* tree, int V);
  * of word 0, u_smp = top 24 bits of word 1, times 2^-24.
  *   target_logits, draft_logits [T][V] fp32; temperature > 0
  *   V <= 32768 (ST_E_UNSUPPORTED above: one workgroup holds a node's two
- *   rows in registers while it tests the node's children);
+ *   rows in registers while it tests the node's children); the draft row of
+ *   a node without children takes no part in the result and is not read, so
+ *   a non-finite entry there is not flagged;
  *   outputs as for st_verify_greedy;
  *   near_ties [B] int32 or NULL: comparisons on the taken path with
  *   |r[x] - u*q[x]| < 1e-6, plus 1 if the replacement draw's threshold lies

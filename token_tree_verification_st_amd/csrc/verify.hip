@@ -1100,7 +1100,6 @@ stoch_node_kernel(StochArgs g) {
   const int par = g.parent[lo + c], tok = g.tokens[lo + c];
   float P[NPT], Q[NPT];
   load_row<VEC>(g.tl + (size_t)t * g.V, g.V, true, P);
-  load_row<VEC>(g.dl + (size_t)t * g.V, g.V, true, Q);
   if (tid < ST_MAX_NODES / 64) s.kid_mask[tid] = 0;
   if (tid == kNodeBlock - 1) {
     double ua, us;
@@ -1114,6 +1113,16 @@ stoch_node_kernel(StochArgs g) {
   int nk = 0;
 #pragma unroll
   for (int w = 0; w < ST_MAX_NODES / 64; ++w) nk += __popcll(s.kid_mask[w]);
+  // The draft row only for a node with children: a leaf's draw uses p alone,
+  // so its draft row is never read (nor checked for non-finite entries).  The
+  // target row's loads, issued first, stay in flight meanwhile (the barriers
+  // above wait for LDS only).
+  if (nk) {
+    load_row<VEC>(g.dl + (size_t)t * g.V, g.V, true, Q);
+  } else {
+#pragma unroll
+    for (int e = 0; e < NPT; ++e) Q[e] = 0.f;
+  }
   // each child's token logits (issued now, used after the statistics)
   int rank = 0;
   float lt = 0.f, ld = 0.f;
