@@ -437,7 +437,7 @@ def only(args, reps, R, fns, one_step):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the verification path runs on one GPU (no sharding across GPUs); --gpus must be 1"}))
         sys.exit(2)
     if args.workload == "llama7b_layer":
         bench_layer(args)
