@@ -483,3 +483,43 @@ def test_step_concurrent_callers_share_the_side_stream():
                 assert torch.equal(bufs[k], ref[name][0][k]), (name, k)
             assert torch.equal(kc, ref[name][1]), name
     say(f"two threads x {reps} steps on their own streams equal the serial steps")
+
+
+@pytest.mark.parametrize("stochastic", [False, True])
+def test_one_call_step_maximum_sizes(stochastic):
+    """The step at the documented limits: a 256-node chain (a path of 256
+    nodes, max_depth 255), a random 256-node tree whose accepted path skips
+    node indices (rows move), and a root-only request; V = 1001 (not a
+    multiple of 4).  Acceptance, compaction and every attention row match
+    the oracle."""
+    rng = np.random.default_rng(31 + stochastic)
+    trees = [tree_chain(256), tree_random_attach(rng, 256, 40), tree_chain(1)]
+    kw = (dict(token_rule="draft_sample", draft_noise_sigma=0.5, temperature=0.8)
+          if stochastic else dict(token_rule="plant_leaf_path", logit_sigma=1.0))
+    wl = build_workload("maxsize", rng, dtype="bf16", Hq=4, Hkv=2, D=128, V=1001,
+                        prefix_lens=[300, 1500, 0], trees=trees, max_depth=255, **kw)
+    dw = to_device(wl)
+    stp.verification_step(dw, stochastic=stochastic)
+    torch.cuda.synchronize()
+    assert status_of(dw) == 0
+    al, an, ot = device_paths(dw)
+    if stochastic:
+        stochastic_parity(wl, dw, label="maxsize")
+    else:
+        res = oracle.verify_greedy(wl.node_off, wl.parent, wl.tokens, wl.logits, wl.V,
+                                   wl.max_depth)
+        _assert_paths_equal(res, (al, an, ot))
+        assert int(res["accept_len"][0]) == 255 and int(res["accept_len"][2]) == 0
+        assert any(int(n) != j for j, n in enumerate(res["accept_nodes"][1, :res["accept_len"][1] + 1]))
+    kn, vn, _, new_len, _ = oracle.kv_compact(wl.k_cache, wl.v_cache, wl.prefix_len, al, an,
+                                              wl.max_depth + 1)
+    assert np.array_equal(dw.k_cache.cpu().view(torch.int16).numpy().view(np.uint16), kn)
+    assert np.array_equal(dw.v_cache.cpu().view(torch.int16).numpy().view(np.uint16), vn)
+    assert np.array_equal(dw.buf["new_len"].cpu().numpy(), new_len)
+    ref, ref_lse = oracle.tree_attention(wl.q, wl.k_cache, wl.v_cache, wl.dtype, wl.Hq, wl.Hkv,
+                                         wl.node_off, wl.parent, wl.prefix_len)
+    err = float(np.abs(dw.buf["out"].float().cpu().numpy().astype(np.float64) - ref).max())
+    lerr = float(np.abs(dw.buf["lse"].cpu().numpy().astype(np.float64) - ref_lse).max())
+    say(f"max sizes, stochastic={stochastic}: accept_len {al.tolist()}, attention max-abs "
+        f"{err:.2e} lse {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= 1e-3
