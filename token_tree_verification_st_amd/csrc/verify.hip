@@ -1084,17 +1084,15 @@ __global__ void __launch_bounds__(kNodeBlock)
 stoch_node_kernel(StochArgs g) {
   constexpr int NPT = kStochMaxV / kNodeBlock, EPT = VEC ? 4 : 1;
   __shared__ NodeLds s;
-  const int tid = threadIdx.x, lane = tid % ST_WAVE, t = blockIdx.x;
-  // node t's request: the number of request starts at or before t, less one
-  int cnt = 0;
-  for (int b0 = 0; b0 < g.B; b0 += ST_WAVE) {
-    const int b = b0 + lane;
-    cnt += __popcll(__ballot(b < g.B && g.node_off[b] <= t));
-  }
-  const int b = __builtin_amdgcn_readfirstlane(cnt > 0 ? cnt - 1 : 0);
-  const int lo = g.node_off[b], hi = g.node_off[b + 1], n = hi - lo, i = t - lo;
-  if (!((lo >= 0) & (hi <= g.T) & (n >= 1) & (n <= g.max_nodes) & (i >= 0) & (i < n)))
-    return;  // the walk flags the request
+  const int tid = threadIdx.x;
+  // Workgroup i * B + b takes local node i of request b: the requests'
+  // first nodes go first.  Parents precede their children, so those are
+  // mostly nodes with children, which also read the draft row; the leaves,
+  // half the work, come in the later workgroups.
+  const int b = blockIdx.x % g.B, i = blockIdx.x / g.B;
+  const int lo = g.node_off[b], hi = g.node_off[b + 1], n = hi - lo, t = lo + i;
+  if (!((lo >= 0) & (hi <= g.T) & (n >= 1) & (n <= g.max_nodes) & (i < n)))
+    return;  // past the request's nodes (or a request the walk flags)
   // this thread's node of the request (clamped, so the loads are unconditional)
   const int c = tid < n ? tid : 0;
   const int par = g.parent[lo + c], tok = g.tokens[lo + c];
@@ -1329,16 +1327,20 @@ int node_launch(const st::StochWalkArgs& w, const float* target_logits, const fl
   const StochArgs g{w.node_off,   w.parent, w.tokens, target_logits, draft,
                     const_cast<NodeVerdict*>(w.verdict), B, w.T, w.V, w.max_nodes, temperature,
                     seed,         offset,   w.status, draft_probs, top_p};
+  // one workgroup per (local node, request) pair; a launch holds fewer
+  // than 2^32 work-items
+  if ((uint64_t)B * (uint64_t)w.max_nodes * kNodeBlock > 0xffffffffull) return ST_E_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const bool vec = (w.V & 3) == 0, ext = draft_probs || top_p < 1.f;
+  const dim3 grid((unsigned)B * (unsigned)w.max_nodes);
   if (vec && !ext)
-    hipLaunchKernelGGL((stoch_node_kernel<true, false>), dim3(w.T), dim3(kNodeBlock), 0, s, g);
+    hipLaunchKernelGGL((stoch_node_kernel<true, false>), grid, dim3(kNodeBlock), 0, s, g);
   else if (!ext)
-    hipLaunchKernelGGL((stoch_node_kernel<false, false>), dim3(w.T), dim3(kNodeBlock), 0, s, g);
+    hipLaunchKernelGGL((stoch_node_kernel<false, false>), grid, dim3(kNodeBlock), 0, s, g);
   else if (vec)
-    hipLaunchKernelGGL((stoch_node_kernel<true, true>), dim3(w.T), dim3(kNodeBlock), 0, s, g);
+    hipLaunchKernelGGL((stoch_node_kernel<true, true>), grid, dim3(kNodeBlock), 0, s, g);
   else
-    hipLaunchKernelGGL((stoch_node_kernel<false, true>), dim3(w.T), dim3(kNodeBlock), 0, s, g);
+    hipLaunchKernelGGL((stoch_node_kernel<false, true>), grid, dim3(kNodeBlock), 0, s, g);
   return st::check_launch();
 }
 }  // namespace
