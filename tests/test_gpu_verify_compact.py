@@ -1,6 +1,8 @@
 """GPU parity: greedy and stochastic acceptance, KV compaction and the whole step,
 HIP path against the oracle through the C ABI."""
 
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -8,6 +10,7 @@ import torch
 import oracle
 from synth import build_workload, make_workload, tree_chain, tree_random_attach
 from token_tree_verification_st_amd import to_device
+from token_tree_verification_st_amd.binding import Tree
 from token_tree_verification_st_amd import step as stp
 from tests.gpu_util import BF16_TOL, F32_TOL, device_paths, plan_override, require_gpu, say, \
     status_of, stochastic_parity
@@ -231,6 +234,85 @@ def test_stochastic_path_overflow():
     # request 1 stops at its leaf and draws there
     stochastic_parity(wl, dw)
     assert status_of(dw) == res["status"] == oracle.STATUS_PATH_OVERFLOW
+
+
+def _status_after_stochastic(wl, top_p=1.0, probs=None):
+    dw = to_device(wl)
+    draft = None if probs is None else torch.from_numpy(probs).cuda()
+    stp.run_verify(dw, stochastic=True, top_p=top_p, draft=draft)
+    torch.cuda.synchronize()
+    return status_of(dw)
+
+
+@pytest.mark.parametrize("V", [1000, 999])
+@pytest.mark.parametrize("top_p", [1.0, 0.9])
+def test_stochastic_nonfinite_entries(V, top_p):
+    """A NaN, +inf or -inf logit in a target row, or in the draft row of a
+    node with children, sets ST_STATUS_NONFINITE, at the row's first entry,
+    in its middle and at its last entry (the wavefront that holds the row
+    end); so does a negative, NaN or infinite draft probability.  A leaf's
+    draft row is not read, so a NaN there sets nothing, and clean rows set
+    nothing.  Both row layouts (V % 4 == 0 and not) and both kernel
+    instances (plain and top-p)."""
+    rng = np.random.default_rng(31)
+    wl0 = build_workload("nf", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=V, prefix_lens=[1, 1],
+                         trees=[tree_chain(4), tree_chain(3)], max_depth=4, logit_sigma=2.0,
+                         draft_noise_sigma=0.5)
+    # nodes 0-2 and 4-5 have children; 3 and 6 are leaves
+    assert _status_after_stochastic(wl0, top_p) & 4 == 0
+    for row, col in ((1, 0), (5, V // 2), (2, V - 1)):
+        for val in (np.nan, np.inf, -np.inf):
+            for which in ("logits", "draft_logits"):
+                wl = copy.deepcopy(wl0)
+                getattr(wl, which)[row, col] = val
+                st = _status_after_stochastic(wl, top_p)
+                assert st & 4, (which, row, col, val)
+    wl = copy.deepcopy(wl0)
+    wl.draft_logits[3, V - 1] = np.nan
+    wl.draft_logits[6, 0] = np.nan
+    assert _status_after_stochastic(wl, top_p) & 4 == 0
+    # a draft given as probabilities
+    pr = np.exp(wl0.draft_logits.astype(np.float64))
+    probs0 = (pr / pr.sum(axis=1, keepdims=True)).astype(np.float32)
+    assert _status_after_stochastic(wl0, top_p, probs0) & 4 == 0
+    for row, col in ((0, 0), (4, V - 1)):
+        for val in (-0.5, np.nan, np.inf, -np.inf):
+            probs = probs0.copy()
+            probs[row, col] = val
+            assert _status_after_stochastic(wl0, top_p, probs) & 4, (row, col, val)
+
+
+@pytest.mark.parametrize("order", ["short_first", "long_first"])
+def test_stochastic_request_over_max_nodes_beside_a_valid_one(order):
+    """T == B * max_nodes although the requests differ in size: the request
+    with more than max_nodes nodes is flagged (ST_STATUS_BAD_PARENT), while
+    the other request -- whose rows the node kernel
+    first guessed from B * max_nodes and then took from node_off -- matches
+    the oracle run on it alone."""
+    rng = np.random.default_rng(41)
+    sizes = (3, 5) if order == "short_first" else (5, 3)
+    wl = build_workload("over", rng, dtype="bf16", Hq=1, Hkv=1, D=64, V=1000,
+                        prefix_lens=[1, 1], trees=[tree_chain(n) for n in sizes], max_depth=6,
+                        logit_sigma=2.0, draft_noise_sigma=0.3, temperature=0.8)
+    dw = to_device(wl)
+    dw.tree = Tree(dw.tree.node_off, dw.tree.parent, 4, wl.max_depth)  # T = 8 = 2 * 4
+    stp.run_verify(dw, stochastic=True)
+    torch.cuda.synchronize()
+    al, an, ot = device_paths(dw)
+    good = 0 if order == "short_first" else 1
+    assert status_of(dw) & 1
+    lo, hi = int(wl.node_off[good]), int(wl.node_off[good + 1])
+    # the request's own draws: Philox counters name it by its batch index
+    draws = lambda _req, node: oracle.uniforms_for_node(wl.rng_seed, wl.rng_offset, good, node)
+    one = oracle.stochastic_outcomes(np.array([0, hi - lo]), wl.parent[lo:hi], wl.tokens[lo:hi],
+                                     wl.logits[lo:hi], wl.draft_logits[lo:hi], wl.V,
+                                     wl.temperature, wl.rng_seed, wl.rng_offset, wl.max_depth,
+                                     uniforms=draws)
+    L = int(al[good])
+    got = (L, an[good, :L + 1].tolist(), ot[good, :L + 1].tolist(),
+           int(dw.buf["near_ties"].cpu().numpy()[good]))
+    assert any((o["accept_len"], o["accept_nodes"], o["out_tokens"], o["near_ties"]) == got
+               for o in one[0]), (got, one[0])
 
 
 # ---------------------------------------------------------------- compaction and whole step

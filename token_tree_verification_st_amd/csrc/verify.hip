@@ -313,6 +313,7 @@ struct StochArgs {
   int32_t* status;
   int draft_probs;  // dl holds probabilities (used as given) rather than logits
   float top_p;      // < 1: both rows restricted to their nucleus
+  int uniform;      // T == B * max_nodes: every request has max_nodes nodes
 };
 
 constexpr int kStochMaxV = 32768;
@@ -1090,14 +1091,31 @@ stoch_node_kernel(StochArgs g) {
   // mostly nodes with children, which also read the draft row; the leaves,
   // half the work, come in the later workgroups.
   const int b = blockIdx.x % g.B, i = blockIdx.x / g.B;
-  const int lo = g.node_off[b], hi = g.node_off[b + 1], n = hi - lo, t = lo + i;
-  if (!((lo >= 0) & (hi <= g.T) & (n >= 1) & (n <= g.max_nodes) & (i < n)))
-    return;  // past the request's nodes (or a request the walk flags)
-  // this thread's node of the request (clamped, so the loads are unconditional)
-  const int c = tid < n ? tid : 0;
-  const int par = g.parent[lo + c], tok = g.tokens[lo + c];
+  // When every request has max_nodes nodes, node i of request b is row
+  // b * max_nodes + i, and its tree entries and target row are requested
+  // before node_off arrives.  Those rows lie inside the T rows whatever
+  // node_off holds; they are kept only if node_off confirms them.  A thread's
+  // node of the request is clamped, so the loads are unconditional.
+  const int lo_u = b * g.max_nodes;
+  int par = 0, tok = 0;
   float P[NPT], Q[NPT];
-  load_row<VEC>(g.tl + (size_t)t * g.V, g.V, true, P);
+  if (g.uniform) {
+    const int c = tid < g.max_nodes ? tid : 0;
+    par = g.parent[lo_u + c];
+    tok = g.tokens[lo_u + c];
+    load_row<VEC>(g.tl + (size_t)(lo_u + i) * g.V, g.V, true, P);
+  }
+  const int lo = g.node_off[b], hi = g.node_off[b + 1], n = hi - lo, t = lo + i;
+  if (!((lo >= 0) & (hi <= g.T) & (n >= 1) & (n <= g.max_nodes) & (i < n))) {
+    __builtin_amdgcn_s_waitcnt(0);  // no load left in flight
+    return;  // past the request's nodes (or a request the walk flags)
+  }
+  if (!g.uniform || lo != lo_u || n != g.max_nodes) {
+    const int c = tid < n ? tid : 0;
+    par = g.parent[lo + c];
+    tok = g.tokens[lo + c];
+    load_row<VEC>(g.tl + (size_t)t * g.V, g.V, true, P);
+  }
   if (tid < ST_MAX_NODES / 64) s.kid_mask[tid] = 0;
   if (tid == kNodeBlock - 1) {
     double ua, us;
@@ -1111,15 +1129,16 @@ stoch_node_kernel(StochArgs g) {
   int nk = 0;
 #pragma unroll
   for (int w = 0; w < ST_MAX_NODES / 64; ++w) nk += __popcll(s.kid_mask[w]);
+  nk = __builtin_amdgcn_readfirstlane(nk);  // block-uniform
   // The draft row only for a node with children: a leaf's draw uses p alone,
-  // so its draft row is never read (nor checked for non-finite entries).  The
-  // target row's loads, issued first, stay in flight meanwhile (the barriers
-  // above wait for LDS only).
+  // so its draft row is never read (nor checked for non-finite entries), and
+  // nothing below reads Q unless nk > 0.  The target row's loads, issued
+  // first, stay in flight meanwhile (the barriers above wait for LDS only).
   if (nk) {
     load_row<VEC>(g.dl + (size_t)t * g.V, g.V, true, Q);
   } else {
 #pragma unroll
-    for (int e = 0; e < NPT; ++e) Q[e] = 0.f;
+    for (int e = 0; e < NPT; ++e) asm("" : "=v"(Q[e]));  // defined, never read
   }
   // each child's token logits (issued now, used after the statistics)
   int rank = 0;
@@ -1133,47 +1152,75 @@ stoch_node_kernel(StochArgs g) {
     ld = g.dl[at];
   }
 
-  // statistics of both rows
-  float mt = -INFINITY, md = -INFINITY;
-  bool finite = true;
+  // statistics of both rows (the target row's first, while the draft row's
+  // loads may still be in flight): maxima, and minima for the finite check
+  const bool probs = EXT && g.draft_probs;  // a draft given as probabilities
+  float mt = -INFINITY, md = -INFINITY, nt = INFINITY, nd = INFINITY;
 #pragma unroll
   for (int e = 0; e < NPT; ++e) {
-    finite &= isfinite(P[e]) && isfinite(Q[e]) && (!EXT || !g.draft_probs || Q[e] >= 0.f);
     mt = fmaxf(mt, P[e]);
-    md = fmaxf(md, Q[e]);
+    nt = fminf(nt, P[e]);
   }
-  if (!finite) st::set_status(g.status, ST_STATUS_NONFINITE);
+  if (nk) {
+#pragma unroll
+    for (int e = 0; e < NPT; ++e) {
+      md = fmaxf(md, Q[e]);
+      nd = fminf(nd, Q[e]);
+    }
+  }
+  // Non-finite entries: -inf (or a negative probability) shows in the minima;
+  // NaN and +inf make the sums below NaN (an exponential of NaN, or of
+  // inf - inf), except +inf in a probability row, which shows in its maximum.
+  bool bad = nt == -INFINITY || (nk && (probs ? !(nd >= 0.f) : nd == -INFINITY));
   block_max2<kNodeBlock>(mt, md, s.redf);
+  if (nk && probs && md == INFINITY) bad = true;
+  // Entries past the row end (only the wavefront holding the row end has
+  // any; they hold copies of the row's first logit) become -inf, or 0 in a
+  // probability row, so that their terms below are exactly 0.
+  constexpr bool kWaveMask = VEC && !EXT;
+  if (kWaveMask && __builtin_amdgcn_readfirstlane(tid / ST_WAVE + 1) * (NPT * ST_WAVE) > g.V) {
+#pragma unroll
+    for (int e = 0; e < NPT; ++e) {
+      const bool past = row_index<VEC, NPT>(e, tid) >= g.V;
+      P[e] = past ? -INFINITY : P[e];
+      Q[e] = past ? (probs ? 0.f : -INFINITY) : Q[e];
+    }
+  }
   const float sc = kLog2e / g.temperature;
-  // the rows become their exponentials exp2((l - M) * s) in place, exactly 0
-  // past the row end (the draft row only where it is used: a node with
-  // children); a group's terms are summed in fp32, the groups in fp64
-  const int kin = groups_inside<VEC, NPT>(g.V, tid);
+  // the rows become their exponentials exp2((l - M) * s) in place (the draft
+  // row only where it is used: a node with children; a probability row as it
+  // is); a group's terms are summed in fp32, the groups in fp64
+  const int kin = kWaveMask ? NPT / EPT : groups_inside<VEC, NPT>(g.V, tid);
   double zt = 0.0, zd = 0.0;
 #pragma unroll
   for (int k = 0; k < NPT / EPT; ++k) {
-    const bool in = k < kin;
-    float st_ = 0.f, sd_ = 0.f;
+    const bool in = kWaveMask || k < kin;
+    float st_ = 0.f;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const float e = exp2_fast((P[k * EPT + j] - mt) * sc);
       P[k * EPT + j] = in ? e : 0.f;
-      st_ += P[k * EPT + j];
-    }
-    if (nk) {
-#pragma unroll
-      for (int j = 0; j < EPT; ++j) {
-        // a draft given as probabilities is used as it is
-        const float e =
-            EXT && g.draft_probs ? Q[k * EPT + j] : exp2_fast((Q[k * EPT + j] - md) * sc);
-        Q[k * EPT + j] = in ? e : 0.f;
-        sd_ += Q[k * EPT + j];
-      }
+      st_ = j ? st_ + P[k * EPT + j] : P[k * EPT + j];
     }
     zt += (double)st_;
-    zd += (double)sd_;
+  }
+  if (nk) {
+#pragma unroll
+    for (int k = 0; k < NPT / EPT; ++k) {
+      const bool in = kWaveMask || k < kin;
+      float sd_ = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const float e = probs ? Q[k * EPT + j] : exp2_fast((Q[k * EPT + j] - md) * sc);
+        Q[k * EPT + j] = in ? e : 0.f;
+        sd_ = j ? sd_ + Q[k * EPT + j] : Q[k * EPT + j];
+      }
+      zd += (double)sd_;
+    }
   }
   block_sum2<kNodeBlock>(zt, zd, s.red);
+  if (tid == 0 && (zt != zt || (nk && zd != zd))) bad = true;
+  if (bad) st::set_status(g.status, ST_STATUS_NONFINITE);
   // nucleus sampling: both rows restricted to their top-p nucleus (the draft
   // row only where it is used)
   float cut_t = 0.f, cut_d = 0.f;
@@ -1326,7 +1373,8 @@ int node_launch(const st::StochWalkArgs& w, const float* target_logits, const fl
                 int B, void* stream) {
   const StochArgs g{w.node_off,   w.parent, w.tokens, target_logits, draft,
                     const_cast<NodeVerdict*>(w.verdict), B, w.T, w.V, w.max_nodes, temperature,
-                    seed,         offset,   w.status, draft_probs, top_p};
+                    seed,         offset,   w.status, draft_probs, top_p,
+                    w.T == B * w.max_nodes};
   // one workgroup per (local node, request) pair; a launch holds fewer
   // than 2^32 work-items
   if ((uint64_t)B * (uint64_t)w.max_nodes * kNodeBlock > 0xffffffffull) return ST_E_UNSUPPORTED;
