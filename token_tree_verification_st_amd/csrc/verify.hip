@@ -717,7 +717,6 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
       }
       const double am = pm + im[r] - (m0[r] + m1[r]);  // mass of the bins above b0
       const double an = pn + in_[r] - (n0[r] + n1[r]);
-      const CutRow& row = r ? rd : rt;
       const double z = r ? zd : zt;
       const double wf = z > 0.0 ? (double)top_p * kFix : 0.0;  // top_p of the total, bin units
       const uint32_t floor_bits = r ? fd : ft;
