@@ -708,13 +708,11 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       if (r == 1 && !both) break;
-      double pm = 0.0, pn = 0.0;  // the waves before this one (all read at once)
-#pragma unroll
-      for (int k = 0; k < kMaxWaves; ++k) {
-        const double a = c.wm[r][k], b = c.wn[r][k];
-        pm += k < w ? a : 0.0;
-        pn += k < w ? b : 0.0;
-      }
+      // the waves before this one: lane k < w holds wave k's totals (integers
+      // below 2^53, so the sums are exact in any order)
+      const int wk = lane & (kMaxWaves - 1);
+      const double pm = wave_sum(lane < w ? c.wm[r][wk] : 0.0);
+      const double pn = wave_sum(lane < w ? c.wn[r][wk] : 0.0);
       const double am = pm + im[r] - (m0[r] + m1[r]);  // mass of the bins above b0
       const double an = pn + in_[r] - (n0[r] + n1[r]);
       const double z = r ? zd : zt;
@@ -780,22 +778,37 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
   if (few && (rt.open() || rd.open())) {
     // gather the candidates, each row's entries in [lo, hi), into LDS slots
     // taken from a counter (their order does not matter: they are sorted)
-    const float lt = __uint_as_float(rt.lo), ht = __uint_as_float(rt.hi);
-    const float ld = __uint_as_float(rd.lo), hd = __uint_as_float(rd.hi);
     const bool ot = rt.open(), od = rd.open();
     if (tid < 2) c.wtot[tid] = 0;
     __syncthreads();
+    // x is a candidate iff x > 0 and lo <= bits(x) < hi (zeros are never
+    // needed): (bits(x) - max(lo, 1)) < hi - max(lo, 1) as unsigned, which
+    // -0, negative values and NaN patterns fail as the value compares would.
+    // One branch per four entries: most wavefronts hold no candidate.
+    static_assert(NPT % 4 == 0, "entries in fours");
+    auto gather = [&](const float (&X)[NPT], uint32_t lo, uint32_t hi, int* cnt, float* dst) {
+      const uint32_t l1 = lo > 1u ? lo : 1u, span = hi > l1 ? hi - l1 : 0u;
 #pragma unroll
-    for (int e = 0; e < NPT; ++e) {
-      if (ot && P[e] > 0.f && P[e] >= lt && P[e] < ht) {  // (zeros are never needed)
-        const int pt = atomicAdd(&c.wtot[0], 1);
-        if (pt < kCutCand) c.cand[0][pt] = P[e];
+      for (int k = 0; k < NPT / 4; ++k) {
+        bool m[4], any = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          m[j] = __float_as_uint(X[4 * k + j]) - l1 < span;
+          any |= m[j];
+        }
+        if (any) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (m[j]) {
+              const int p = atomicAdd(cnt, 1);
+              if (p < kCutCand) dst[p] = X[4 * k + j];
+            }
+          }
+        }
       }
-      if (od && Q[e] > 0.f && Q[e] >= ld && Q[e] < hd) {
-        const int pd = atomicAdd(&c.wtot[1], 1);
-        if (pd < kCutCand) c.cand[1][pd] = Q[e];
-      }
-    }
+    };
+    if (ot) gather(P, rt.lo, rt.hi, &c.wtot[0], c.cand[0]);
+    if (od) gather(Q, rd.lo, rd.hi, &c.wtot[1], c.cand[1]);
     __syncthreads();
     if (tid < ST_WAVE) {
       const int ct = ot ? rt.between() : 0, cd = od ? rd.between() : 0;
