@@ -513,8 +513,9 @@ __device__ __forceinline__ void minmax_partner(float v, float& mn, float& mx) {
 // lane l = element j * 64 + l.  Stage K merges runs of K elements; substage
 // JJ compares elements i and i ^ JJ, the lower one keeping the larger value
 // where bit K of i is clear (the run is ordered largest first) and the
-// smaller where it is set.  JJ >= 64 pairs registers of one lane.
-template <int L, int K, int JJ>
+// smaller where it is set.  JJ >= 64 pairs registers of one lane.  With
+// TWO false only `a` is sorted (`b` is not touched).
+template <int L, int K, int JJ, bool TWO>
 __device__ __forceinline__ void bitonic_sub(float (&a)[L], float (&b)[L], int lane) {
   if constexpr (JJ >= ST_WAVE) {
     constexpr int R = JJ / ST_WAVE;
@@ -522,11 +523,14 @@ __device__ __forceinline__ void bitonic_sub(float (&a)[L], float (&b)[L], int la
     for (int j = 0; j < L; ++j) {
       if (j & R) continue;
       const bool desc = ((j * ST_WAVE) & K) == 0;
-      const float a0 = a[j], a1 = a[j ^ R], b0 = b[j], b1 = b[j ^ R];
+      const float a0 = a[j], a1 = a[j ^ R];
       a[j] = desc ? fmaxf(a0, a1) : fminf(a0, a1);
       a[j ^ R] = desc ? fminf(a0, a1) : fmaxf(a0, a1);
-      b[j] = desc ? fmaxf(b0, b1) : fminf(b0, b1);
-      b[j ^ R] = desc ? fminf(b0, b1) : fmaxf(b0, b1);
+      if constexpr (TWO) {
+        const float b0 = b[j], b1 = b[j ^ R];
+        b[j] = desc ? fmaxf(b0, b1) : fminf(b0, b1);
+        b[j ^ R] = desc ? fminf(b0, b1) : fmaxf(b0, b1);
+      }
     }
   } else {
     const bool lower = (lane & JJ) == 0;
@@ -536,17 +540,19 @@ __device__ __forceinline__ void bitonic_sub(float (&a)[L], float (&b)[L], int la
       float mn, mx;
       minmax_partner<JJ>(a[j], mn, mx);
       a[j] = lower == desc ? mx : mn;
-      minmax_partner<JJ>(b[j], mn, mx);
-      b[j] = lower == desc ? mx : mn;
+      if constexpr (TWO) {
+        minmax_partner<JJ>(b[j], mn, mx);
+        b[j] = lower == desc ? mx : mn;
+      }
     }
   }
-  if constexpr (JJ > 1) bitonic_sub<L, K, JJ / 2>(a, b, lane);
+  if constexpr (JJ > 1) bitonic_sub<L, K, JJ / 2, TWO>(a, b, lane);
 }
-template <int L, int K = 2>
+template <int L, int K = 2, bool TWO = true>
 __device__ __forceinline__ void bitonic_desc(float (&a)[L], float (&b)[L], int lane) {
   static_assert(L == 1 || L == 2 || L == 4 || L == 8, "a power-of-two count a lane");
-  bitonic_sub<L, K, K / 2>(a, b, lane);
-  if constexpr (K < L * ST_WAVE) bitonic_desc<L, K * 2>(a, b, lane);
+  bitonic_sub<L, K, K / 2, TWO>(a, b, lane);
+  if constexpr (K < L * ST_WAVE) bitonic_desc<L, K * 2, TWO>(a, b, lane);
 }
 
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
@@ -810,32 +816,35 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
     if (ot) gather(P, rt.lo, rt.hi, &c.wtot[0], c.cand[0]);
     if (od) gather(Q, rd.lo, rd.hi, &c.wtot[1], c.cand[1]);
     __syncthreads();
-    if (tid < ST_WAVE) {
-      const int ct = ot ? rt.between() : 0, cd = od ? rd.between() : 0;
-      // both candidate sets sorted, largest first (a row's missing entries
-      // are -1 and sort last), by the smallest network that holds them; then
-      // each row's cut from running sums
-      auto finish = [&](auto per_lane) {
+    if (tid < 2 * ST_WAVE) {
+      // wavefront 0 finishes the target row's search and wavefront 1 the
+      // draft row's, at once: the row's candidates sorted, largest first
+      // (missing entries are -1 and sort last), by the smallest network that
+      // holds them, then the cut from running sums
+      auto finish = [&](CutRow& row, int cnt, const float* cand, auto per_lane) {
         constexpr int L = decltype(per_lane)::value;
-        float xt[L], xd[L];
+        float x[L];
 #pragma unroll
         for (int j = 0; j < L; ++j) {
           const int q = j * ST_WAVE + lane;
-          xt[j] = q < ct ? c.cand[0][q] : -1.f;
-          xd[j] = q < cd ? c.cand[1][q] : -1.f;
+          x[j] = q < cnt ? cand[q] : -1.f;
         }
-        bitonic_desc<L>(xt, xd, lane);
-        sorted_cut<L>(xt, lane, rt);
-        sorted_cut<L>(xd, lane, rd);
+        bitonic_desc<L, 2, false>(x, x, lane);
+        sorted_cut<L>(x, lane, row);
       };
-      if (max(ct, cd) <= 2 * ST_WAVE) finish(std::integral_constant<int, 2>{});
-      else finish(std::integral_constant<int, kCutLane>{});
-      if (tid == 0) {
-        c.cut[0] = rt.lo;
-        c.cut[1] = rd.lo;
-        c.kept[0] = rt.m_lo;
-        c.kept[1] = rd.m_lo;
-      }
+      auto one = [&](CutRow& row, bool open, int slot) {
+        if (open) {  // wave-uniform
+          const int cnt = row.between();
+          if (cnt <= 2 * ST_WAVE) finish(row, cnt, c.cand[slot], std::integral_constant<int, 2>{});
+          else finish(row, cnt, c.cand[slot], std::integral_constant<int, kCutLane>{});
+        }
+        if (lane == 0) {
+          c.cut[slot] = row.lo;
+          c.kept[slot] = row.m_lo;
+        }
+      };
+      if (__builtin_amdgcn_readfirstlane(tid / ST_WAVE) == 0) one(rt, ot, 0);
+      else one(rd, od, 1);
     }
     __syncthreads();
     rt.lo = (uint32_t)__builtin_amdgcn_readfirstlane(c.cut[0]);
