@@ -673,24 +673,25 @@ __device__ inline void nucleus_cut(float (&P)[NPT], float (&Q)[NPT], bool both, 
     for (int i = tid; i < 2 * kBins; i += kNodeBlock) (&c.hm[0][0])[i] = 0ull;
     if (tid < 2) c.hb[tid].found = 0;
     __syncthreads();
-    const float flt = __uint_as_float(ft), fld = __uint_as_float(fd);
     // (a row without mass, as an all-zero probability row, bins nothing;
     // both factors are block-uniform, kept in scalar registers)
     const float it = __uint_as_float(__builtin_amdgcn_readfirstlane(
         __float_as_uint(zt > 0.0 ? (float)(1.0 / zt) : 0.f)));
     const float id = __uint_as_float(__builtin_amdgcn_readfirstlane(
         __float_as_uint(both && zd > 0.0 ? (float)(1.0 / zd) : 0.f)));
+    // an entry is binned iff it is positive and at or above its row's floor:
+    // max(floor, 1) <= bits <= bits(+inf) as one unsigned compare, the set
+    // the value compares x > 0 and x >= floor select
+    auto bin_row = [&](const float (&X)[NPT], uint32_t fl, float inv, unsigned long long* h) {
+      const uint32_t l1 = fl > 1u ? fl : 1u, span = 0x7F800000u - l1;
 #pragma unroll
-    for (int e = 0; e < NPT; ++e) {
-      if (P[e] > 0.f && P[e] >= flt) {
-        const int b = (int)(__float_as_uint(P[e]) >> kBinShift);
-        atomicAdd(&c.hm[0][b], fix36(P[e] * it) + kCountOne);
+      for (int e = 0; e < NPT; ++e) {
+        const uint32_t u = __float_as_uint(X[e]);
+        if (u - l1 <= span) atomicAdd(&h[u >> kBinShift], fix36(X[e] * inv) + kCountOne);
       }
-      if (both && Q[e] > 0.f && Q[e] >= fld) {
-        const int b = (int)(__float_as_uint(Q[e]) >> kBinShift);
-        atomicAdd(&c.hm[1][b], fix36(Q[e] * id) + kCountOne);
-      }
-    }
+    };
+    bin_row(P, ft, it, c.hm[0]);
+    if (both) bin_row(Q, fd, id, c.hm[1]);
     __syncthreads();
     // suffix sums, largest bin first: thread t holds bins kBins-1-2t and
     // kBins-2-2t; integers below 2^53, so every double sum is exact
