@@ -194,7 +194,9 @@ size_t st_verify_stochastic_workspace(const st_tree* tree, int V);
  * of word 0, u_smp = top 24 bits of word 1, times 2^-24.
  *   target_logits, draft_logits [T][V] fp32; temperature > 0
  *   V <= 32768 (ST_E_UNSUPPORTED above: one workgroup holds a node's two
- *   rows in registers while it tests the node's children); the draft row of
+ *   rows in registers while it tests the node's children), and
+ *   B * max_nodes < 2^22 (ST_E_UNSUPPORTED beyond: one 1024-thread workgroup
+ *   per request and local node index); the draft row of
  *   a node without children takes no part in the result and is not read, so
  *   a non-finite entry there is not flagged;
  *   outputs as for st_verify_greedy;

@@ -315,6 +315,37 @@ def test_stochastic_request_over_max_nodes_beside_a_valid_one(order):
                for o in one[0]), (got, one[0])
 
 
+def test_stochastic_rejects_too_many_node_workgroups():
+    """One 1024-thread workgroup per (request, local node index): B * max_nodes
+    of 2^22 or more is ST_E_UNSUPPORTED before anything is launched, one less
+    in max_nodes is accepted by the size check (16384 one-node requests)."""
+    from token_tree_verification_st_amd.binding import (st_verify_stochastic,
+                                                        st_verify_stochastic_workspace)
+    B, V = 16384, 8
+    node_off = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    parent = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    tokens = torch.zeros(B, dtype=torch.int32, device="cuda")
+    logits = torch.zeros(B, V, dtype=torch.float32, device="cuda")
+    for max_nodes, ok in ((256, False), (255, True)):  # 16384 * 256 = 2^22
+        tree = Tree(node_off, parent, max_nodes, 0)
+        ws = torch.empty(st_verify_stochastic_workspace(tree, V), dtype=torch.uint8, device="cuda")
+        al = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        an = torch.full((B, 1), -7, dtype=torch.int32, device="cuda")
+        ot = torch.full((B, 2), -7, dtype=torch.int32, device="cuda")
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        call = lambda: st_verify_stochastic(tree, tokens, logits, logits, 1.0, 0, 0, al, an, ot, ws,
+                                            status=st)
+        if ok:
+            call()
+            torch.cuda.synchronize()
+            assert al.cpu().tolist() == [0] * B and int(st.item()) == 0
+        else:
+            with pytest.raises(RuntimeError, match=r"\(-2\)"):
+                call()
+            torch.cuda.synchronize()
+            assert (al.cpu() == -7).all()  # nothing ran
+
+
 # ---------------------------------------------------------------- compaction and whole step
 
 
