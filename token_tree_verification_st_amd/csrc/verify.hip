@@ -230,19 +230,46 @@ using st::kMaxPath;
 using st::kArgmaxBlock;
 using st::kArgmaxSlice;
 
-// Workgroup (t, slice) reduces logits[t][slice*8192 .. +8192) to its maximum
-// and lowest index; all of a thread's loads are issued before any is used.
+// Workgroup u reduces unit u (row u / nslices, slice u % nslices: 8192
+// logits) to its maximum and lowest index.  Every load is issued
+// unconditionally, before any is used (an entry past the row end reads the
+// row's first logit; the reduction skips it): with no branch around a load the
+// wait for each one is exact.  (Workgroups that reduce several units in turn,
+// the next unit's loads in flight during each reduction, measured slower on a
+// 61 MB batch than one unit each: the dispatcher's fresh workgroups overlap
+// better than one workgroup's prefetch.)
+template <bool VEC>
+__device__ inline void argmax_unit_load(const float* logits, int V, int nslices, int u,
+                                        st::ArgmaxRegs& r) {
+  const float* row = logits + (size_t)(u / nslices) * V;
+  const int base = (u % nslices) * kArgmaxSlice, tid = threadIdx.x;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int k = 0; k < st::kArgmaxPerThread / 4; ++k) {
+      const int v = base + 4 * (tid + k * kArgmaxBlock);
+      r.x[k] = __builtin_nontemporal_load((const st::am_f32x4*)(row + (v < V ? v : 0)));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < st::kArgmaxPerThread; ++k) {
+      const int v = base + tid + k * kArgmaxBlock;
+      r.x[k / 4][k % 4] = row[v < V ? v : 0];
+    }
+  }
+}
 __global__ void __launch_bounds__(kArgmaxBlock)
-row_argmax_kernel(const float* __restrict__ logits, int V, ArgmaxPart* __restrict__ part,
-                  int32_t* status) {
+row_argmax_kernel(const float* __restrict__ logits, int V, int nslices,
+                  ArgmaxPart* __restrict__ part, int32_t* status) {
   __shared__ int scratch[2 * (kArgmaxBlock / ST_WAVE) + 1];
+  const int u = blockIdx.x;
   st::ArgmaxRegs r;
   if ((V & 3) == 0) {
-    st::argmax_slice_load<true>(logits, V, blockIdx.x, blockIdx.y, r);
-    st::argmax_slice_finish<true>(r, V, blockIdx.x, blockIdx.y, gridDim.y, part, status, scratch);
+    argmax_unit_load<true>(logits, V, nslices, u, r);
+    st::argmax_slice_finish<true>(r, V, u / nslices, u % nslices, nslices, part, status, scratch);
   } else {
-    st::argmax_slice_load<false>(logits, V, blockIdx.x, blockIdx.y, r);
-    st::argmax_slice_finish<false>(r, V, blockIdx.x, blockIdx.y, gridDim.y, part, status, scratch);
+    argmax_unit_load<false>(logits, V, nslices, u, r);
+    st::argmax_slice_finish<false>(r, V, u / nslices, u % nslices, nslices, part, status,
+                                   scratch);
   }
 }
 
@@ -1348,8 +1375,8 @@ int st::greedy_prepare(const st_tree* tree, int V, const int32_t* tokens, const 
 }
 
 int st::greedy_argmax_launch(const st::GreedyWalkArgs& g, const float* logits, void* stream) {
-  hipLaunchKernelGGL(row_argmax_kernel, dim3(g.T, g.nslices), dim3(kArgmaxBlock), 0,
-                     (hipStream_t)stream, logits, g.V, (ArgmaxPart*)g.part, g.status);
+  hipLaunchKernelGGL(row_argmax_kernel, dim3(g.T * g.nslices), dim3(kArgmaxBlock), 0,
+                     (hipStream_t)stream, logits, g.V, g.nslices, (ArgmaxPart*)g.part, g.status);
   return st::check_launch();
 }
 
